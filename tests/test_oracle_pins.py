@@ -1,0 +1,415 @@
+"""Pins for the CPU oracle: facts fixed by the pages and by mathematics, not by the oracle itself.
+
+Each test names the passage or the mathematical fact it checks.  Pages:
+  [Lab5]  "Lab 5: Gemma4 端到端推理优化"
+  [Orin]  "Jetson Orin AGX INT4 推理优化实践：super 分支从 9 tok/s 到 24 tok/s"
+  [Infra] "【infra之路】12-投机解码、量化与推理引擎对比"
+Kinds of pin: printed values (tests/golden), closed forms (on-grid weights whose codes and scales
+are known exactly), invariants, brute force over all candidate codes, and library reductions.
+"""
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+SYM, ASYM = oracle.SYM, oracle.ASYM
+
+
+def _golden(golden_dir, name):
+    with open(os.path.join(golden_dir, name)) as f:
+        return json.load(f)
+
+
+def _f32(v):
+    return np.float32(v)
+
+
+def _bf16_value(bits):
+    """Decode bf16 bits with plain integer arithmetic (independent of the oracle's helper)."""
+    b = int(bits)
+    sign = -1.0 if b & 0x8000 else 1.0
+    e = (b >> 7) & 0xFF
+    m = b & 0x7F
+    if e == 0:
+        return sign * m * 2.0 ** (-133)
+    return sign * (1.0 + m / 128.0) * 2.0 ** (e - 127)
+
+
+# ------------------------------------------------------------------------------------------
+# Nibble layout [Lab5 INT4 线性量化, 融合INT4反量化与矩阵乘], [Orin DP4A 做了什么]
+# ------------------------------------------------------------------------------------------
+def test_uint32_nibble_order_printed(golden_dir):
+    g = _golden(golden_dir, "nibble_layout.json")
+    word = int(g["uint32_hex"], 16)
+    assert word == g["uint32_le"]
+    row = np.frombuffer(np.uint32(word).tobytes(), dtype=np.uint8).reshape(1, 4)
+    codes = oracle.unpack(row)
+    assert codes.ravel().tolist() == g["codes_in_k_order"]
+
+
+def test_all_byte_values_round_trip():
+    row = np.arange(256, dtype=np.uint8).reshape(1, 256)
+    codes = oracle.unpack(row)
+    # invariant: recombining the two codes of each byte gives the byte back
+    re = (codes[0, 0::2].astype(np.int64) | (codes[0, 1::2].astype(np.int64) << 4))
+    assert re.tolist() == list(range(256))
+    assert codes.max() <= 15
+
+
+def test_packed_row_bytes_printed(golden_dir):
+    g = _golden(golden_dir, "packed_row_bytes.json")
+    H = g["H"]
+    w = workloads.weight(1, 0, 2, H)
+    qw, sc, _ = oracle.pack(w, 128, SYM)
+    assert qw.shape[1] == g["bytes_per_row"]["int4"]
+    assert 2 * H == g["bytes_per_row"]["fp16"] and H == g["bytes_per_row"]["int8"]
+
+
+def test_unpack_aliasing_regression():
+    """[Lab5 量化正确性修正]: writing the low codes in place into the byte view before reading the
+    high codes corrupts them; the oracle computes both nibbles from untouched bytes."""
+    rng = np.random.default_rng(7)
+    packed = rng.integers(0, 256, size=(3, 64), dtype=np.uint8)
+    good = oracle.unpack(packed)
+    # emulate the faulty in-place interleave on one shared uint8 buffer
+    buf = np.zeros((3, 128), dtype=np.uint8)
+    buf[:, :64] = packed
+    view = buf[:, :64]  # the "packed" view aliases the output storage
+    buf[:, 0::2] = view & 0x0F
+    buf[:, 1::2] = view >> 4
+    assert not np.array_equal(buf, good)
+    # the corrected form: independent low/high, then stack and flatten
+    low, high = packed & 0x0F, packed >> 4
+    fixed = np.stack((low, high), axis=-1).reshape(3, 128)
+    assert np.array_equal(fixed, good)
+
+
+# ------------------------------------------------------------------------------------------
+# Closed forms: on-grid weights.  [Lab5 INT4 线性量化]
+# ------------------------------------------------------------------------------------------
+def _on_grid_group(codes, s, z):
+    return np.array([(c - z) * s for c in codes], dtype=np.float32)
+
+
+def test_asym_on_grid_codes_scales_zeros_exact():
+    """Values r = s (c - z) with power-of-two s and every code 0..15 present round-trip exactly:
+    s = (max - min)/15, z = round(-min/s), code = c, and each byte is c_even | c_odd << 4."""
+    rng = np.random.default_rng(11)
+    rows = []
+    want_codes = []
+    for j in range(6):
+        s = 2.0 ** (-4 - j)
+        z = [0, 3, 5, 8, 12, 15][j]
+        c = np.concatenate([np.arange(16), rng.integers(0, 16, size=16)])
+        rng.shuffle(c)
+        rows.append(_on_grid_group(c, s, z))
+        want_codes.append(c)
+    w = np.stack(rows)
+    qw, sc, zr = oracle.pack(w, 32, ASYM)
+    for j in range(6):
+        assert _bf16_value(sc[j, 0]) == 2.0 ** (-4 - j)
+        assert _bf16_value(zr[j, 0]) == [0, 3, 5, 8, 12, 15][j]
+        c = want_codes[j]
+        assert qw[j].tolist() == [int(c[2 * i]) | (int(c[2 * i + 1]) << 4) for i in range(16)]
+    wh = oracle.dequant(qw, sc, zr, 32, 32)
+    assert np.array_equal(wh, w.astype(np.float64))
+
+
+def test_sym_on_grid_divides_by_seven():
+    """Symmetric: s = max|r| / 7 (not / 8), codes offset by 8; a group whose extreme is 7 s0 gets
+    s = s0 exactly and codes c + 8 for r = c s0."""
+    s0 = 2.0 ** -6
+    c = np.array(list(range(-7, 8)) * 2 + [7, -7], dtype=np.int64)
+    w = (c * s0).astype(np.float32).reshape(1, 32)
+    qw, sc, _ = oracle.pack(w, 32, SYM)
+    assert _bf16_value(sc[0, 0]) == s0
+    codes = oracle.unpack(qw)[0]
+    assert codes.tolist() == (c + 8).tolist()
+    # the "max/8" rule would have given 7/8 s0 and moved every code
+    assert 0 not in codes.tolist()
+
+
+def test_zero_group_and_per_row_scale():
+    w = np.zeros((2, 64), dtype=np.float32)
+    w[1, 5] = 0.7
+    qw, sc, _ = oracle.pack(w, 0, SYM)
+    assert sc[0, 0] == 0 and oracle.unpack(qw)[0].tolist() == [8] * 64
+    # per-row scale (group_size 0) for W4A8 [Orin 从 FP 线性层到 INT4 DP4A 的数学推导]
+    assert abs(_bf16_value(sc[1, 0]) - 0.1) <= 0.1 * 2 ** -8
+    qa, sa, za = oracle.pack(w, 0, ASYM)
+    assert sa[0, 0] == 0 and za[0, 0] == 0 and oracle.unpack(qa)[0].tolist() == [0] * 64
+
+
+# ------------------------------------------------------------------------------------------
+# Scales against exact rationals; codes against brute force over all 16 candidates.
+# ------------------------------------------------------------------------------------------
+def _check_groups(w, qw, sc, zr, g, mode):
+    d_out, d_in = w.shape
+    kp = oracle.k_pad(d_in, g)
+    ng = oracle.n_groups(d_in, g)
+    gs = kp // ng
+    codes = oracle.unpack(qw)
+    wp = np.zeros((d_out, kp), dtype=np.float64)
+    wp[:, :d_in] = w
+    for j in range(d_out):
+        for G in range(ng):
+            seg = wp[j, G * gs:(G + 1) * gs]
+            s = _bf16_value(sc[j, G])
+            if mode == SYM:
+                exact = Fraction(float(np.max(np.abs(seg)))) / 7
+                z = 8.0
+            else:
+                exact = (Fraction(float(seg.max())) - Fraction(float(seg.min()))) / 15
+                z = _bf16_value(zr[j, G])
+            # bf16 rounding of an fp32 quotient: within half a bf16 ulp plus an fp32 ulp
+            assert abs(Fraction(s) - exact) <= exact * Fraction(1, 256) * Fraction(1025, 1024)
+            if mode == ASYM and s != 0:
+                ratio = -Fraction(float(seg.min())) / Fraction(s)
+                lo = int(np.floor(float(ratio)))
+                assert z in (lo, lo + 1)
+                frac = float(ratio - lo)
+                if abs(frac - 0.5) > 1e-5:
+                    assert z == (lo if frac < 0.5 else lo + 1)
+            c = codes[j, G * gs:(G + 1) * gs].astype(np.float64)
+            if s == 0:
+                assert np.all(c == z)
+                continue
+            cand = s * (np.arange(16)[None, :] - z)  # every representable value of the group
+            err = np.abs(seg[:, None] - cand)
+            best = err.min(axis=1)
+            mine = np.abs(seg - s * (c - z))
+            # RTN: the chosen code is a nearest grid point (up to fp32 rounding of r/s + z)
+            assert np.all(mine <= best + 4e-7 * s * (1 + np.abs(seg / s) + abs(z))), (j, G)
+    return codes
+
+
+@pytest.mark.parametrize("g", [32, 64, 128, 256, 0])
+@pytest.mark.parametrize("mode", [SYM, ASYM])
+def test_scales_and_codes_brute_force(g, mode):
+    w = workloads.weight(5, g + mode, 12, 300)
+    workloads.add_weight_outliers(w, 5, 99, 0.01, 0.5)
+    qw, sc, zr = oracle.pack(w, g, mode)
+    codes = _check_groups(w, qw, sc, zr, g, mode)
+    if mode == SYM:
+        # RTN with s = max|r|/7 never reaches code 0 (= -8)
+        assert codes.min() >= 1
+
+
+def test_extreme_entries_map_to_edge_codes():
+    w = workloads.weight(6, 0, 64, 128)
+    qs, ss, _ = oracle.pack(w, 128, SYM)
+    cs = oracle.unpack(qs)
+    qa, sa, za = oracle.pack(w, 128, ASYM)
+    ca = oracle.unpack(qa)
+    for j in range(64):
+        i = int(np.argmax(np.abs(w[j])))
+        assert cs[j, i] == (15 if w[j, i] > 0 else 1)
+        assert ca[j, int(np.argmin(w[j]))] == 0
+        assert ca[j, int(np.argmax(w[j]))] in (14, 15)
+
+
+def test_unclipped_error_at_most_half_scale():
+    """[Infra 2.2 量化的基本概念]: each value is off by at most scale/2 after round-to-nearest."""
+    w = workloads.weight(8, 0, 32, 512)
+    for mode in (SYM, ASYM):
+        qw, sc, zr = oracle.pack(w, 64, mode)
+        wh = oracle.dequant(qw, sc, zr, 512, 64)
+        s = np.repeat(oracle.bf16_to_f32(sc).astype(np.float64), 64, axis=1)
+        codes = oracle.unpack(qw)
+        interior = (codes > 0) & (codes < 15)
+        assert np.all(np.abs(wh - w)[interior] <= 0.5 * s[interior] * (1 + 1e-6))
+
+
+# ------------------------------------------------------------------------------------------
+# Padding [Lab5 INT4 线性量化]: padded columns decode to exactly zero.
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("mode", [SYM, ASYM])
+@pytest.mark.parametrize("d_in,g", [(3600, 128), (100, 32), (70, 0), (200, 64)])
+def test_padding_decodes_to_zero(mode, d_in, g):
+    w = workloads.weight(9, d_in, 16, d_in)
+    w += 0.05  # mostly positive groups: the pads are what pulls min to 0
+    qw, sc, zr = oracle.pack(w, g, mode)
+    kp = oracle.k_pad(d_in, g)
+    assert kp > d_in
+    codes = oracle.unpack(qw)
+    wh = oracle.dequant(qw, sc, zr, d_in, g)
+    assert np.all(wh[:, d_in:] == 0.0)
+    ng = oracle.n_groups(d_in, g)
+    gs = kp // ng
+    last = (d_in - 1) // gs
+    for j in range(16):
+        z = 8 if mode == SYM else _bf16_value(zr[j, last])
+        assert np.all(codes[j, d_in:] == z)
+        if mode == ASYM:
+            assert 0 <= z <= 15
+
+
+# ------------------------------------------------------------------------------------------
+# W4A16 contraction
+# ------------------------------------------------------------------------------------------
+def test_w4a16_basis_probes_exact():
+    """x = e_k gives y[j] = r_hat[j][k] exactly (one exact product)."""
+    w = workloads.weight(10, 0, 24, 96)
+    for mode, g in ((SYM, 32), (ASYM, 32), (ASYM, 0)):
+        qw, sc, zr = oracle.pack(w, g, mode)
+        wh = oracle.dequant(qw, sc, zr, 96, g)
+        for k in (0, 1, 31, 32, 33, 95):
+            x = np.zeros((1, 96), dtype=np.uint16)
+            x[0, k] = 0x3F80  # bf16 1.0
+            y = oracle.w4a16(x, qw, sc, zr, None, 96, g)
+            assert np.array_equal(y[0], wh[:, k])
+
+
+def test_w4a16_library_reduction_tiny():
+    """On small shapes the loop equals numpy's fp64 matmul of x and the decoded weight."""
+    w = workloads.weight(12, 0, 40, 200)
+    x = workloads.activations(12, 0, 5, 200)
+    b = workloads.bias(12, 0, 40)
+    xf = oracle.bf16_to_f32(x).astype(np.float64)
+    bf = oracle.bf16_to_f32(b).astype(np.float64)
+    for mode, g in ((SYM, 32), (ASYM, 64), (SYM, 0)):
+        qw, sc, zr = oracle.pack(w, g, mode)
+        wh = oracle.dequant(qw, sc, zr, 200, g)[:, :200]
+        y = oracle.w4a16(x, qw, sc, zr, b, 200, g)
+        assert np.allclose(y, xf @ wh.T + bf, rtol=0, atol=1e-12)
+        pts = oracle.w4a16_points(x, qw, sc, zr, b, 200, g, [0, 4, 2], [0, 39, 17])
+        assert np.array_equal(pts, y[[0, 4, 2], [0, 39, 17]])
+
+
+def test_w4a16_constant_codes():
+    """All codes equal to z give y = b exactly; x = 1 with codes z + 1 gives the sum of the
+    scales over the real columns of each group."""
+    d_out, d_in, g = 8, 100, 32
+    kp, ng = oracle.k_pad(d_in, g), oracle.n_groups(d_in, g)
+    sc = oracle.f32_to_bf16(np.linspace(0.01, 0.08, d_out * ng).reshape(d_out, ng))
+    zr = oracle.f32_to_bf16(np.tile(np.arange(ng, dtype=np.float32) + 3, (d_out, 1)))
+    x = workloads.activations(13, 0, 2, d_in)
+    b = workloads.bias(13, 0, d_out)
+    codes = np.repeat(oracle.bf16_to_f32(zr).astype(np.uint8), g, axis=1)
+    qw = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    y = oracle.w4a16(x, qw, sc, zr, b, d_in, g)
+    assert np.array_equal(y, np.tile(oracle.bf16_to_f32(b).astype(np.float64), (2, 1)))
+    codes1 = codes + 1
+    qw1 = (codes1[:, 0::2] | (codes1[:, 1::2] << 4)).astype(np.uint8)
+    ones = np.full((1, d_in), 0x3F80, dtype=np.uint16)
+    y1 = oracle.w4a16(ones, qw1, sc, zr, None, d_in, g)
+    counts = np.array([min(g, d_in - G * g) for G in range(ng)], dtype=np.float64)
+    want = (oracle.bf16_to_f32(sc).astype(np.float64) * counts).sum(axis=1)
+    assert np.allclose(y1[0], want, rtol=1e-15, atol=0)
+
+
+# ------------------------------------------------------------------------------------------
+# Activation quantization [Orin 从 FP 线性层到 INT4 DP4A 的数学推导], [Infra 2.2, 2.4]
+# ------------------------------------------------------------------------------------------
+def test_act_quant_outlier_example_printed(golden_dir):
+    g = _golden(golden_dir, "int8_activation_examples.json")["outlier_example"]
+    x = workloads.to_bf16_bits(np.array([[g["max"], g["value"], -0.02, 0.0]], np.float32))
+    q, s, qs = oracle.act_quant(x)
+    assert abs(s[0] - g["scale_approx"]) < 5e-4
+    assert q[0, 1] == g["code"] and q[0, 0] == 127
+    deq = float(s[0]) * int(q[0, 1])
+    assert abs(deq - g["dequant_approx"]) < 5e-4
+    rel = abs(deq - g["value"]) / g["value"]
+    assert abs(rel - g["relative_error_approx"]) < 0.01
+    assert qs[0] == int(q[0].astype(np.int64).sum())
+
+
+def test_act_quant_symmetric_example_printed(golden_dir):
+    g = _golden(golden_dir, "int8_activation_examples.json")["symmetric_example"]
+    x = workloads.activations(14, 0, 1, 4096)
+    xf = oracle.bf16_to_f32(x)
+    xf = xf / np.abs(xf).max() * np.float32(g["max"])
+    x = workloads.to_bf16_bits(xf)
+    xf = oracle.bf16_to_f32(x).astype(np.float64)
+    q, s, _ = oracle.act_quant(x)
+    assert abs(s[0] - g["scale_approx"]) < 1e-4
+    err = np.abs(xf[0] - float(s[0]) * q[0])
+    assert err.max() <= g["max_error_approx"] + 1e-4
+    assert err.max() <= float(s[0]) / 2 * (1 + 1e-6)
+
+
+def test_act_quant_brute_force_and_edges():
+    x = workloads.activations(15, 0, 6, 333, outlier_frac=0.01, outlier_scale=20.0)
+    x[3] = 0  # an all-zero token
+    q, s, qs = oracle.act_quant(x)
+    xf = oracle.bf16_to_f32(x).astype(np.float64)
+    cand = np.arange(-127, 128, dtype=np.float64)
+    for m in range(6):
+        if m == 3:
+            assert s[m] == 0 and not q[m].any() and qs[m] == 0
+            continue
+        a = np.abs(xf[m]).max()
+        assert abs(Fraction(float(s[m])) - Fraction(a) / 127) <= Fraction(a) / 127 * 2 ** -23
+        i = int(np.argmax(np.abs(xf[m])))
+        assert abs(int(q[m, i])) == 127
+        err = np.abs(xf[m][:, None] - float(s[m]) * cand[None, :])
+        mine = np.abs(xf[m] - float(s[m]) * q[m])
+        assert np.all(mine <= err.min(axis=1) + 1e-6 * float(s[m]))
+        assert qs[m] == int(q[m].astype(np.int64).sum())
+
+
+# ------------------------------------------------------------------------------------------
+# W4A8 [Orin INT32 accumulator 是否安全]
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("H", [3584, 18944])
+def test_w4a8_worst_case_accumulator_printed(golden_dir, H):
+    g = _golden(golden_dir, "int32_accumulator.json")
+    assert g["max_abs_weight_code"] * g["max_abs_activation_code"] == g["max_abs_product"]
+    qw = np.zeros((2, H // 2), dtype=np.uint8)  # all codes 0, i.e. weight -8
+    sw = oracle.f32_to_bf16(np.array([1.0, 0.5], np.float32))
+    q = np.full((1, H), -127, dtype=np.int8)
+    s_x = np.array([1.0], np.float32)
+    acc, y, nov = oracle.w4a8(q, s_x, qw, sw, None, H)
+    want = H * g["max_abs_product"]
+    if H == g["H"]:
+        assert want == g["worst_case_accumulator"]
+    assert nov == 0 and acc[0].tolist() == [want, want]
+    assert want < g["int32_max"]
+    assert y[0].tolist() == [float(want), 0.5 * want]
+
+
+def test_w4a8_brute_force_python_ints():
+    rng = np.random.default_rng(16)
+    d_out, d_in = 7, 90
+    kp = oracle.k_pad(d_in, 0)
+    codes = rng.integers(0, 16, size=(d_out, kp))
+    codes[:, d_in:] = 8
+    qw = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    q = rng.integers(-127, 128, size=(3, d_in)).astype(np.int8)
+    sw = workloads.to_bf16_bits(rng.uniform(0.001, 0.01, d_out))
+    b = workloads.bias(16, 0, d_out)
+    s_x = np.array([0.01, 0.5, 2.0], np.float32)
+    acc, y, _ = oracle.w4a8(q, s_x, qw, sw, b, d_in)
+    for m in range(3):
+        for j in range(d_out):
+            a = sum((int(codes[j, k]) - 8) * int(q[m, k]) for k in range(d_in))
+            assert acc[m, j] == a
+            want = _bf16_value(sw[j]) * float(s_x[m]) * a + _bf16_value(b[j])
+            assert abs(y[m, j] - want) <= 1e-12 * (1 + abs(want))
+
+
+def test_w4a8_end_to_end_within_quantization_bound():
+    """y approximates x W^T: the gap is bounded by the two quantization errors, each at most
+    half a step [Infra 2.2]."""
+    cfg = workloads.C5
+    lin = cfg.linears[0]
+    w = workloads.weight(17, 0, 64, lin.d_in)
+    x = workloads.activations(17, 0, 1, lin.d_in, 0.01, 20.0)
+    qw, sc, _ = oracle.pack(w, 0, SYM)
+    q, s_x, _ = oracle.act_quant(x)
+    acc, y, nov = oracle.w4a8(q, s_x, qw, sc[:, 0], None, lin.d_in)
+    assert nov == 0
+    xf = oracle.bf16_to_f32(x).astype(np.float64)[0]
+    ref = w.astype(np.float64) @ xf
+    sw = oracle.bf16_to_f32(sc[:, 0]).astype(np.float64)
+    wh = oracle.dequant(qw, sc, None, lin.d_in, 0)[:, :lin.d_in]
+    xq = float(s_x[0]) * q[0].astype(np.float64)
+    bound = (np.abs(w - wh) * np.abs(xf)).sum(axis=1) + (np.abs(wh) * np.abs(xf - xq)).sum(axis=1)
+    assert np.all(np.abs(y[0] - ref) <= bound * (1 + 1e-9) + 1e-9)
+    assert np.all(np.abs(xf - xq) <= float(s_x[0]) / 2 * (1 + 1e-6))
+    assert np.all(sw > 0)
