@@ -1,0 +1,401 @@
+"""Benchmark of the INT4 weight-only linear hot path on one MI355X.
+
+Headline workload (one "step"): the 7B-class MLP decode at M = 1 -- the fused gate/up GEMV
+(37888 x 3584) followed by the down GEMV (3584 x 18944), symmetric INT4 with group 128 and 0.1%
+weight outliers, bf16 activations and outputs.  `value` is the step's algorithmic bytes (packed
+weights + scales + activations + outputs) divided by its time, in GB/s.  Weights are rotated over
+distinct copies totalling more than twice the 256 MB Infinity Cache, so they stream from HBM.
+
+Also reported (in "secondary"): the prefill GEMM at M = 2048 (TFLOP/s and MFMA-peak fraction),
+the W4A8 decode path, and the 28-layer asymmetric decoder-step linear set at M = 1, 8, 16.
+
+Prints ONE JSON line.  Only --gpus 1 is supported (this build targets one GPU).
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
+INFINITY_CACHE_BYTES = 256 << 20
+
+METRIC = "W4A16 decode GEMV GB/s & % HBM peak (M=1); prefill GEMM TFLOP/s"
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def linear_bytes(M, d_out, d_in, g, asym, out_bytes=2, bias=False, x_bytes=2):
+    """Algorithmic bytes of one call: what the method must move."""
+    q = 32 if g == 0 else g
+    k_pad = (d_in + q - 1) // q * q
+    n_groups = 1 if g == 0 else k_pad // g
+    b = d_out * k_pad // 2 + d_out * n_groups * 2 * (2 if asym else 1)
+    b += M * d_in * x_bytes + M * d_out * out_bytes
+    if bias:
+        b += d_out * 2
+    return b
+
+
+def source_hash(*files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel_key, src_hash):
+    """HBM traffic per launch from the committed PMC summary, if it was measured on the current
+    kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    entry = data.get(kernel_key)
+    if not entry or entry.get("source_hash") != src_hash:
+        return None
+    return entry.get("bytes_per_launch")
+
+
+class Timer:
+    """HIP events on torch's current stream, which is the stream the library launches on."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = {}
+
+    def start(self, key):
+        ev = self.torch.cuda.Event(enable_timing=True)
+        ev.record()
+        self.pairs.setdefault(key, []).append([ev, None])
+
+    def stop(self, key):
+        ev = self.torch.cuda.Event(enable_timing=True)
+        ev.record()
+        self.pairs[key][-1][1] = ev
+
+    def mean_ms(self, key):
+        v = [a.elapsed_time(b) for a, b in self.pairs.get(key, [])]
+        return float(np.mean(v)) if v else float("nan")
+
+
+def bench_c2(torch, w4, workloads, steps, warmup, rotate_bytes):
+    cfg = workloads.C2
+    gu, dn = cfg.linears
+    dev = torch.device("cuda", 0)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg.seed)
+
+    def packed(lin, li):
+        w = torch.from_numpy(workloads.linear_weight(cfg, li)).to(dev)
+        return w4.w4_pack(w, lin.group_size, lin.mode)
+
+    base = [packed(gu, 0), packed(dn, 1)]
+    per_copy = sum(t.numel() * t.element_size() for p in base for t in p if t is not None)
+    n_copies = max(2, int(np.ceil(rotate_bytes / per_copy)))
+    copies = [base]
+    for _ in range(n_copies - 1):
+        copies.append([tuple(None if t is None else t.clone() for t in p) for p in base])
+    x_gu = torch.from_numpy(workloads.linear_x(cfg, 0, 1).view(np.int16)).view(
+        torch.bfloat16).to(dev)
+    x_dn = torch.from_numpy(workloads.linear_x(cfg, 1, 1).view(np.int16)).view(
+        torch.bfloat16).to(dev)
+    y_gu = torch.empty((1, gu.d_out), dtype=torch.bfloat16, device=dev)
+    y_dn = torch.empty((1, dn.d_out), dtype=torch.bfloat16, device=dev)
+
+    def step(i, timer=None):
+        c = copies[i % n_copies]
+        if timer:
+            timer.start("gate_up")
+        w4.w4_gemv(x_gu, *c[0], None, gu.d_in, gu.group_size, out=y_gu)
+        if timer:
+            timer.stop("gate_up")
+            timer.start("down")
+        w4.w4_gemv(x_dn, *c[1], None, dn.d_in, dn.group_size, out=y_dn)
+        if timer:
+            timer.stop("down")
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # whole-step time: no events between the launches
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for i in range(steps):
+        step(i)
+    t1.record()
+    torch.cuda.synchronize()
+    step_ms = t0.elapsed_time(t1) / steps
+    # per-kernel durations, events around each launch
+    timer = Timer(torch)
+    for i in range(steps):
+        step(i, timer)
+    torch.cuda.synchronize()
+    b_gu = linear_bytes(1, gu.d_out, gu.d_in, gu.group_size, False)
+    b_dn = linear_bytes(1, dn.d_out, dn.d_in, dn.group_size, False)
+    return dict(step_ms=step_ms, bytes_step=b_gu + b_dn, gu_ms=timer.mean_ms("gate_up"),
+                dn_ms=timer.mean_ms("down"), b_gu=b_gu, b_dn=b_dn, n_copies=n_copies,
+                rotate_mb=n_copies * per_copy / 1e6)
+
+
+def bench_c4(torch, w4, workloads, iters):
+    cfg = workloads.C4
+    dev = torch.device("cuda", 0)
+    M = cfg.tokens[0]
+    out = {}
+    total_flop, total_ms = 0.0, 0.0
+    for li, lin in enumerate(cfg.linears):
+        w = torch.from_numpy(workloads.linear_weight(cfg, li)).to(dev)
+        qw, sc, zr = w4.w4_pack(w, lin.group_size, lin.mode)
+        del w
+        x = torch.from_numpy(workloads.linear_x(cfg, li, M).view(np.int16)).view(
+            torch.bfloat16).to(dev)
+        y = torch.empty((M, lin.d_out), dtype=torch.bfloat16, device=dev)
+        for _ in range(2):
+            w4.w4_gemm(x, qw, sc, zr, None, lin.d_in, lin.group_size, out=y)
+        torch.cuda.synchronize()
+        timer = Timer(torch)
+        for _ in range(iters):
+            timer.start(lin.name)
+            w4.w4_gemm(x, qw, sc, zr, None, lin.d_in, lin.group_size, out=y)
+            timer.stop(lin.name)
+        torch.cuda.synchronize()
+        ms = timer.mean_ms(lin.name)
+        flop = 2.0 * M * lin.d_out * lin.d_in
+        total_flop += flop
+        total_ms += ms
+        out[lin.name] = dict(ms=round(ms, 4), tflops=round(flop / ms / 1e9, 1),
+                             mfma_frac=round(flop / ms / 1e9 / BF16_MFMA_PEAK_TFLOPS, 4))
+        del qw, sc, zr, x, y
+    out["total"] = dict(gflop=round(total_flop / 1e9, 2), ms=round(total_ms, 4),
+                        tflops=round(total_flop / total_ms / 1e9, 1),
+                        mfma_frac=round(total_flop / total_ms / 1e9 / BF16_MFMA_PEAK_TFLOPS, 4))
+    return out
+
+
+def bench_c5(torch, w4, workloads, iters):
+    cfg = workloads.C5
+    dev = torch.device("cuda", 0)
+    out = {}
+    for li, lin in enumerate(cfg.linears):
+        w = torch.from_numpy(workloads.linear_weight(cfg, li)).to(dev)
+        base = w4.w4_pack(w, 0, w4.W4_SYM)
+        del w
+        per_copy = base[0].numel() + base[1].numel() * 2
+        n_copies = max(2, int(np.ceil(2 * INFINITY_CACHE_BYTES / per_copy)))
+        copies = [base] + [tuple(None if t is None else t.clone() for t in base)
+                           for _ in range(n_copies - 1)]
+        x = torch.from_numpy(workloads.linear_x(cfg, li, 1).view(np.int16)).view(
+            torch.bfloat16).to(dev)
+        b = torch.from_numpy(workloads.linear_bias(cfg, li).view(np.int16)).view(
+            torch.bfloat16).to(dev)
+        y = torch.empty((1, lin.d_out), dtype=torch.bfloat16, device=dev)
+        q, s_x, _ = w4.act_quant_int8(x, lin.d_in, with_sum=False)
+        for i in range(4):
+            c = copies[i % n_copies]
+            w4.w4a8_gemv(q, s_x, c[0], c[1], b, lin.d_in, out=y)
+        torch.cuda.synchronize()
+        timer = Timer(torch)
+        for i in range(iters):
+            c = copies[i % n_copies]
+            timer.start("aq")
+            w4.act_quant_int8(x, lin.d_in, with_sum=False)
+            timer.stop("aq")
+            timer.start("gemv")
+            w4.w4a8_gemv(q, s_x, c[0], c[1], b, lin.d_in, out=y)
+            timer.stop("gemv")
+        torch.cuda.synchronize()
+        gemv_ms = timer.mean_ms("gemv")
+        aq_ms = timer.mean_ms("aq")
+        gb = linear_bytes(1, lin.d_out, lin.d_in, 0, False, bias=True, x_bytes=1) + 4
+        aq_bytes = 2 * lin.d_in + lin.d_in + 4
+        out[f"{lin.d_out}x{lin.d_in}"] = dict(
+            gemv_us=round(gemv_ms * 1e3, 2), gemv_gbs=round(gb / gemv_ms / 1e6, 1),
+            gemv_hbm_frac=round(gb / gemv_ms / 1e6 / HBM_PEAK_GBS, 4),
+            act_quant_us=round(aq_ms * 1e3, 2),
+            path_gbs=round((gb + aq_bytes) / (gemv_ms + aq_ms) / 1e6, 1))
+        del copies, base
+    return out
+
+
+def bench_c3(torch, w4, workloads, iters):
+    """28 layers x {qkv, o, gate/up, down}, asymmetric g128, weights generated on the GPU with a
+    seeded torch generator (timing only; parity of these shapes is in the GPU tests)."""
+    cfg = workloads.C3
+    dev = torch.device("cuda", 0)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg.seed)
+    layers = []
+    for _ in range(cfg.repeat_layers):
+        packs = []
+        for lin in cfg.linears:
+            w = torch.randn((lin.d_out, lin.d_in), generator=gen, device=dev) * workloads.W_SIGMA
+            packs.append(w4.w4_pack(w, lin.group_size, lin.mode))
+            del w
+        layers.append(packs)
+    out = {}
+    for M in cfg.tokens:
+        xs = [torch.randn((M, lin.d_in), generator=gen, device=dev).to(torch.bfloat16)
+              for lin in cfg.linears]
+        ys = [torch.empty((M, lin.d_out), dtype=torch.bfloat16, device=dev)
+              for lin in cfg.linears]
+
+        def step():
+            for packs in layers:
+                for lin, p, x, y in zip(cfg.linears, packs, xs, ys):
+                    w4.w4_gemv(x, *p, None, lin.d_in, lin.group_size, out=y)
+
+        step()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(iters):
+            step()
+        t1.record()
+        torch.cuda.synchronize()
+        ms = t0.elapsed_time(t1) / iters
+        nbytes = cfg.repeat_layers * sum(linear_bytes(M, l.d_out, l.d_in, l.group_size, True)
+                                         for l in cfg.linears)
+        out[f"M={M}"] = dict(step_us=round(ms * 1e3, 1), gbs=round(nbytes / ms / 1e6, 1),
+                             hbm_frac=round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4))
+    del layers
+    return out
+
+
+def cpu_baseline(workloads, budget_s):
+    """The oracle, as it stands, on the host's cores, over the same C2 step (M = 1)."""
+    import oracle
+    cfg = workloads.C2
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    packs, xs = [], []
+    for li, lin in enumerate(cfg.linears):
+        w = workloads.linear_weight(cfg, li)
+        packs.append(oracle.pack(w, lin.group_size, lin.mode))
+        xs.append(workloads.linear_x(cfg, li, 1))
+        del w
+    nbytes = sum(linear_bytes(1, l.d_out, l.d_in, l.group_size, False) for l in cfg.linears)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        for (qw, sc, zr), x, lin in zip(packs, xs, cfg.linears):
+            oracle.w4a16(x, qw, sc, zr, None, lin.d_in, lin.group_size)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= 2000:
+            break
+    return dict(value=round(nbytes * n / el / 1e9, 3), unit="GB/s", cores=threads,
+                kind="oracle",
+                sample=f"{n} full C2 decode steps (gate/up 37888x3584 + down 3584x18944, M=1) "
+                       f"in {el:.1f} s, fp64 oracle with OpenMP over output rows")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-secondary", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=12.0)
+    ap.add_argument("--only", choices=["c2", "c3", "c4", "c5"], default=None,
+                    help="time one workload only (for profiling runs)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(this build has no multi-GPU path).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import int4_weight_only_amd as w4
+    import workloads
+
+    torch.cuda.set_device(0)
+    log("device", torch.cuda.get_device_name(0), "lib", w4.library_path())
+    rotate = 2 * INFINITY_CACHE_BYTES + (64 << 20)
+
+    secondary = {}
+    if args.only in (None, "c2"):
+        log("C2 decode step")
+        r = bench_c2(torch, w4, workloads, args.steps, args.warmup, rotate)
+    if args.only is not None:
+        if args.only == "c3":
+            secondary["C3_decoder_step"] = bench_c3(torch, w4, workloads, 5)
+        elif args.only == "c4":
+            secondary["C4_prefill_gemm"] = bench_c4(torch, w4, workloads, 10)
+        elif args.only == "c5":
+            secondary["C5_w4a8"] = bench_c5(torch, w4, workloads, 100)
+        if args.only != "c2":
+            print(json.dumps(secondary), flush=True)
+            return
+    if not args.no_secondary:
+        log("C4 prefill GEMM")
+        secondary["C4_prefill_gemm"] = bench_c4(torch, w4, workloads, 10)
+        log("C5 W4A8")
+        secondary["C5_w4a8"] = bench_c5(torch, w4, workloads, 100)
+        log("C3 decoder step")
+        secondary["C3_decoder_step"] = bench_c3(torch, w4, workloads, 5)
+
+    value = r["bytes_step"] / r["step_ms"] / 1e6
+    gu_gbs = r["b_gu"] / r["gu_ms"] / 1e6
+    src = source_hash("int4_weight_only_amd/csrc/decode.hip")
+    roofline = {
+        "bound": "hbm",
+        "kernel": "gemv_w4a16_kernel (C2 gate/up 37888x3584, M=1)",
+        "achieved": round(gu_gbs, 1),
+        "peak": HBM_PEAK_GBS,
+        "unit": "GB/s",
+        "frac": round(gu_gbs / HBM_PEAK_GBS, 4),
+        "traffic": load_traffic("gemv_c2_gate_up", src),
+        "algorithmic_bytes": r["b_gu"],
+        "avg_launch_us": round(r["gu_ms"] * 1e3, 3),
+        "down_avg_launch_us": round(r["dn_ms"] * 1e3, 3),
+        "down_gbs": round(r["b_dn"] / r["dn_ms"] / 1e6, 1),
+    }
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["step_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "w4a16 (int4 weights, bf16 activations, fp32 accumulate)",
+        "data": "synthetic",
+        "config": {
+            "workload": "C2 MLP decode step at M=1: gate/up GEMV 37888x3584 + down GEMV "
+                        "3584x18944, symmetric INT4 g128, 0.1% weight outliers, bf16 out",
+            "tokens": 1,
+            "bytes_per_step": r["bytes_step"],
+            "weight_copies_rotated": r["n_copies"],
+            "rotated_mb": round(r["rotate_mb"], 1),
+            "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        },
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log("CPU oracle baseline")
+        line["cpu_baseline"] = cpu_baseline(workloads, args.cpu_budget_s)
+    if secondary:
+        line["secondary"] = secondary
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,161 @@
+/*
+ * w4.h -- C ABI of libw4.so: the group-wise INT4 weight-only quantized linear layer on MI355X
+ * (gfx950).
+ *
+ *   y = x . W_hat^T (+ b),   W_hat[j][k] = s[j][G] * (code[j][k] - z[j][G]),  G = k / group_size
+ *
+ * Pages cited (title, then section):
+ *   [Lab5]  "Lab 5: Gemma4 端到端推理优化"
+ *   [Orin]  "Jetson Orin AGX INT4 推理优化实践：super 分支从 9 tok/s 到 24 tok/s"
+ *   [Infra] "【infra之路】12-投机解码、量化与推理引擎对比"
+ *
+ * Conventions shared by every entry point
+ *   - Array arguments are DEVICE pointers owned by the caller.  The library never allocates,
+ *     frees or retains device memory and keeps no state between calls (thread-safe; calls on one
+ *     stream are ordered by that stream).
+ *   - bf16 values travel as uint16_t bit patterns.  `stream` is a hipStream_t passed as void*
+ *     (NULL = the default stream).  Calls enqueue kernels and return without synchronizing.
+ *   - Arguments are validated on the host before anything is enqueued.  A failed check returns
+ *     a nonzero w4_status and enqueues nothing; a failed launch returns W4_ERR_HIP and the HIP
+ *     error text is kept in w4_last_hip_error() (per host thread).
+ *   - Outputs are overwritten, never accumulated into.  Inputs and outputs must not overlap.
+ *   - Identical inputs give bitwise-identical outputs (no floating-point atomics).
+ *   - Inputs must be finite; NaN/Inf inputs are not checked and give unspecified results.
+ *
+ * Packed weight format [Lab5 INT4 线性量化], [Lab5 融合INT4反量化与矩阵乘]
+ *   k_pad    = ceil(d_in / group_size) * group_size   (group_size in {32, 64, 128, 256})
+ *            = ceil(d_in / 32) * 32 with one group per row   (group_size == 0)
+ *   n_groups = k_pad / group_size   (1 when group_size == 0)
+ *   qweight  uint8 [d_out][k_pad/2]: two 4-bit codes per byte, column 2i in the low nibble and
+ *            column 2i+1 in the high nibble.  Rows are output channels.
+ *   scales   bf16 [d_out][n_groups]
+ *   zeros    bf16 [d_out][n_groups] for W4_ASYM; absent (NULL) for W4_SYM, whose zero point is
+ *            the constant 8 (signed levels -8..7 stored as codes 0..15).
+ *   Padded columns k >= d_in carry the zero code and decode to exactly 0.
+ */
+#ifndef W4_H
+#define W4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    W4_OK = 0,
+    W4_ERR_NULL = 1,        /* a required pointer is NULL, or zeros given/missing for the mode */
+    W4_ERR_SHAPE = 2,       /* a size is < 1, or a leading dimension is smaller than its row  */
+    W4_ERR_GROUP = 3,       /* group_size not in {0, 32, 64, 128, 256}                        */
+    W4_ERR_ALIGN = 4,       /* a pointer or leading dimension breaks the alignment rules       */
+    W4_ERR_RANGE = 5,       /* a size beyond the limits stated for the entry point             */
+    W4_ERR_UNSUPPORTED = 6, /* valid arguments this entry point does not serve (e.g. M > 64)   */
+    W4_ERR_HIP = 7          /* a HIP launch or query failed; see w4_last_hip_error()           */
+} w4_status;
+
+enum { W4_SYM = 0, W4_ASYM = 1 };         /* quantization mode                      */
+enum { W4_OUT_BF16 = 0, W4_OUT_F32 = 1 }; /* element type of y                      */
+
+/* Upper bounds checked by every entry point (W4_ERR_RANGE beyond them). */
+#define W4_MAX_DIM ((int64_t)1 << 24)  /* d_out, d_in, M, K                      */
+#define W4_MAX_W4A8_D_IN ((int64_t)1 << 20) /* keeps sum(code * q) within int32: 2^20*15*127 < 2^31 */
+#define W4_GEMV_MAX_M 64
+
+/*
+ * w4_packed_layout -- host-only size query (no GPU work).
+ * [Lab5 INT4 线性量化]: the input dimension is padded to a whole number of groups.
+ * Writes k_pad, n_groups and the byte size of qweight (d_out * k_pad / 2) for the given shape.
+ * Any output pointer may be NULL.  Errors: W4_ERR_SHAPE, W4_ERR_GROUP, W4_ERR_RANGE.
+ */
+int w4_packed_layout(int64_t d_out, int64_t d_in, int group_size, int64_t *k_pad,
+                     int64_t *n_groups, size_t *qweight_bytes);
+
+/*
+ * w4_pack -- round-to-nearest (RTN) quantization of an fp32 weight into the packed format.
+ * [Lab5 INT4 线性量化]: per (output row, group):
+ *   W4_SYM : s = bf16(max|r| / 7), z = 8
+ *   W4_ASYM: s = bf16((max r - min r) / 15), z = bf16(round(-min r / s))
+ *   code = clip(round(r / s + z), 0, 15), with the stored bf16 s and z; round = ties-to-even.
+ * Statistics run over the padded group (pads are 0), so pads encode to z and decode to 0.
+ * A group whose bf16 scale is 0 is stored as s = +0, z = +0 (ASYM) and all codes equal to z.
+ * The fp32 steps are single IEEE operations in this order:  a/7 (or (mx-mn)/15), bf16 rounding,
+ * (-mn)/s, rint, bf16 rounding, then per element  r/s, +z, rint, clamp.
+ *   w        fp32 [d_out][ldw], ldw >= d_in, 4-byte aligned
+ *   qweight  uint8 [d_out][k_pad/2], 16-byte aligned
+ *   scales   bf16 [d_out][n_groups];  zeros bf16 [d_out][n_groups] iff mode == W4_ASYM, else NULL
+ */
+int w4_pack(const float *w, int64_t d_out, int64_t d_in, int64_t ldw, int group_size, int mode,
+            uint8_t *qweight, uint16_t *scales, uint16_t *zeros, void *stream);
+
+/*
+ * w4_gemv -- W4A16 decode linear for 1 <= M <= 64 token rows, weights read once per call.
+ * [Lab5 Prefill和Decode分流] (the small-M decode path), [Lab5 融合INT4反量化与矩阵乘]
+ * (dequantize in registers inside the product, never a dense weight in memory),
+ * [Orin 模型尺寸和 decode 的真实瓶颈] (y_j = sum_i W_ji x_i + b_j).
+ *   x        bf16 [M][ldx], ldx >= d_in, ldx % 8 == 0, 16-byte aligned; only k < d_in is used
+ *   qweight, scales, zeros, group_size: the packed format above (zeros NULL iff symmetric)
+ *   bias     bf16 [d_out] or NULL
+ *   y        [M][ldy], ldy >= d_out, element type out_dtype (W4_OUT_BF16 / W4_OUT_F32),
+ *            naturally aligned.  Accumulation is fp32; the bf16 output is the round-to-nearest-
+ *            even image of the fp32 result of the same call.
+ * M > 64 returns W4_ERR_UNSUPPORTED (use w4_gemm).
+ */
+int w4_gemv(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
+            const uint16_t *scales, const uint16_t *zeros, const uint16_t *bias, int64_t d_out,
+            int64_t d_in, int group_size, void *y, int64_t ldy, int out_dtype, void *stream);
+
+/*
+ * w4_gemm -- W4A16 prefill linear for any M >= 1 (same arguments and result as w4_gemv).
+ * [Lab5 Prefill和Decode分流] (large M: dequantize once per tile and run a dense matrix product).
+ * Weight tiles are dequantized on chip to the exact integers (code - z) in bf16, multiplied on
+ * the bf16 matrix cores with fp32 accumulation, and each group's partial product is scaled by
+ * s[j][G] in fp32.  No dense weight is written to memory.
+ */
+int w4_gemm(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
+            const uint16_t *scales, const uint16_t *zeros, const uint16_t *bias, int64_t d_out,
+            int64_t d_in, int group_size, void *y, int64_t ldy, int out_dtype, void *stream);
+
+/*
+ * act_quant_int8 -- per-token dynamic symmetric int8 quantization of activations.
+ * [Orin 从 FP 线性层到 INT4 DP4A 的数学推导], [Infra 2.2 量化的基本概念]:
+ *   s_x[m] = max_k |x[m][k]| / 127 (fp32),  q[m][k] = clip(round(x[m][k] / s_x[m]), -127, 127)
+ * round = ties-to-even, the division is one correctly rounded fp32 division.  A token whose
+ * values are all zero gets s_x = 0 and q = 0.
+ *   x      bf16 [M][ldx], ldx >= K, ldx % 8 == 0, 16-byte aligned
+ *   q      int8 [M][ldq], ldq >= K, ldq % 16 == 0, 16-byte aligned; q[m][k] for k < K only
+ *   s_x    fp32 [M]
+ *   q_sum  int32 [M] = sum_k q[m][k], or NULL
+ */
+int act_quant_int8(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int8_t *q, int64_t ldq,
+                   float *s_x, int32_t *q_sum, void *stream);
+
+/*
+ * w4a8_gemv -- W4A8 decode linear: int4 weights x int8 activations into an int32 accumulator.
+ * [Orin 从 FP 线性层到 INT4 DP4A 的数学推导], [Orin INT32 accumulator 是否安全]:
+ *   acc[m][j] = sum_{k < d_in} (code[j][k] - 8) * q[m][k]          (exact, int32)
+ *   y[m][j]   = s_w[j] * s_x[m] * acc[m][j] + b[j]                  (fp32)
+ * Weights are a per-row symmetric pack (w4_pack with group_size = 0, W4_SYM); s_w is that pack's
+ * scales array.  1 <= M <= 64 and d_in <= W4_MAX_W4A8_D_IN, so every partial sum fits in int32.
+ *   q        int8 [M][ldq], ldq >= d_in, ldq % 16 == 0, 16-byte aligned (from act_quant_int8)
+ *   s_x      fp32 [M]
+ *   qweight  uint8 [d_out][k_pad/2], k_pad = ceil(d_in/32)*32, 16-byte aligned
+ *   s_w      bf16 [d_out];  bias bf16 [d_out] or NULL
+ *   y        [M][ldy], ldy >= d_out, out_dtype as for w4_gemv
+ *   acc      int32 [M][d_out] (dense), or NULL: the exact accumulators, for bit-exact checks
+ */
+int w4a8_gemv(const int8_t *q, const float *s_x, int64_t M, int64_t ldq, const uint8_t *qweight,
+              const uint16_t *s_w, const uint16_t *bias, int64_t d_out, int64_t d_in, void *y,
+              int64_t ldy, int out_dtype, int32_t *acc, void *stream);
+
+/* Text for a w4_status value (static storage). */
+const char *w4_status_string(int status);
+
+/* Text of the last HIP error seen by this host thread ("" if none). */
+const char *w4_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4_H */

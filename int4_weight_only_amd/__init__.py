@@ -1,0 +1,218 @@
+"""int4_weight_only_amd -- Python binding of libw4.so, the MI355X (gfx950) group-wise INT4
+weight-only linear layer.
+
+The binding only marshals arguments: it checks tensor dtypes/devices/shapes, allocates outputs
+with torch (device memory is torch's), passes raw pointers and the current HIP stream to the C
+ABI declared in include/w4.h, and turns a nonzero status into an exception.  Every step of the
+computation runs in the library's HIP kernels; there is no CPU or PyTorch fallback: if libw4.so is
+missing or cannot be loaded, importing this package raises.
+
+bf16 tensors are passed as torch.bfloat16 (their bits are the uint16 patterns of the ABI).
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "W4_SYM", "W4_ASYM", "W4_OUT_BF16", "W4_OUT_F32", "W4Error", "packed_layout", "w4_pack",
+    "w4_gemv", "w4_gemm", "act_quant_int8", "w4a8_gemv", "w4_linear", "library_path",
+]
+
+W4_SYM, W4_ASYM = 0, 1
+W4_OUT_BF16, W4_OUT_F32 = 0, 1
+GEMV_MAX_M = 64
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libw4.so")
+
+
+class W4Error(RuntimeError):
+    def __init__(self, fn, status, text):
+        super().__init__(f"{fn} failed with status {status}: {text}")
+        self.status = status
+
+
+def _load():
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(f"libw4.so not found at {_LIB_PATH}; build it with "
+                          "`python -c 'import __graft_entry__ as g; g.build()'` or "
+                          "`python int4_weight_only_amd/build.py`")
+    lib = ctypes.CDLL(_LIB_PATH)
+    i64, p, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    lib.w4_packed_layout.argtypes = [i64, i64, i32, ctypes.POINTER(i64), ctypes.POINTER(i64),
+                                     ctypes.POINTER(ctypes.c_size_t)]
+    lib.w4_pack.argtypes = [p, i64, i64, i64, i32, i32, p, p, p, p]
+    lin = [p, i64, i64, p, p, p, p, i64, i64, i32, p, i64, i32, p]
+    lib.w4_gemv.argtypes = lin
+    lib.w4_gemm.argtypes = lin
+    lib.act_quant_int8.argtypes = [p, i64, i64, i64, p, i64, p, p, p]
+    lib.w4a8_gemv.argtypes = [p, p, i64, i64, p, p, p, i64, i64, p, i64, i32, p, p]
+    for f in ("w4_packed_layout", "w4_pack", "w4_gemv", "w4_gemm", "act_quant_int8",
+              "w4a8_gemv"):
+        getattr(lib, f).restype = i32
+    lib.w4_status_string.argtypes = [i32]
+    lib.w4_status_string.restype = ctypes.c_char_p
+    lib.w4_last_hip_error.argtypes = []
+    lib.w4_last_hip_error.restype = ctypes.c_char_p
+    return lib
+
+
+_lib = _load()
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def _check(fn, status):
+    if status != 0:
+        text = _lib.w4_status_string(status).decode()
+        if status == 7:
+            text += ": " + _lib.w4_last_hip_error().decode()
+        raise W4Error(fn, status, text)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype, device=None, dim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if dim is not None and t.dim() != dim:
+        raise ValueError(f"{name} must have {dim} dims, got {t.dim()}")
+    if t.dim() > 0 and t.stride(-1) != 1:
+        raise ValueError(f"{name} must be contiguous along its last dim")
+
+
+def packed_layout(d_out, d_in, group_size):
+    """(k_pad, n_groups, qweight_bytes) of the packed format (host-only query)."""
+    kp, ng, nb = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_size_t()
+    _check("w4_packed_layout", _lib.w4_packed_layout(d_out, d_in, group_size, ctypes.byref(kp),
+                                                     ctypes.byref(ng), ctypes.byref(nb)))
+    return kp.value, ng.value, nb.value
+
+
+def w4_pack(w, group_size, mode, d_in=None):
+    """RTN-pack an fp32 weight [d_out][ldw] (first d_in columns) on the GPU.
+    Returns (qweight uint8 [d_out][k_pad/2], scales bf16 [d_out][G], zeros bf16 or None)."""
+    _need(w, "w", torch.float32, dim=2)
+    d_out, ldw = w.shape
+    d_in = ldw if d_in is None else d_in
+    k_pad, n_groups, _ = packed_layout(d_out, d_in, group_size)
+    dev = w.device
+    qweight = torch.empty((d_out, k_pad // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((d_out, n_groups), dtype=torch.bfloat16, device=dev)
+    zeros = torch.empty_like(scales) if mode == W4_ASYM else None
+    _check("w4_pack", _lib.w4_pack(_ptr(w), d_out, d_in, w.stride(0), group_size, mode,
+                                   _ptr(qweight), _ptr(scales), _ptr(zeros), _stream(dev)))
+    return qweight, scales, zeros
+
+
+def _linear(fn_name, x, qweight, scales, zeros, bias, d_in, group_size, out_dtype, out):
+    _need(x, "x", torch.bfloat16, dim=2)
+    dev = x.device
+    _need(qweight, "qweight", torch.uint8, dev, 2)
+    _need(scales, "scales", torch.bfloat16, dev, 2)
+    if zeros is not None:
+        _need(zeros, "zeros", torch.bfloat16, dev, 2)
+    if bias is not None:
+        _need(bias, "bias", torch.bfloat16, dev, 1)
+    M = x.shape[0]
+    d_out = qweight.shape[0]
+    k_pad, n_groups, _ = packed_layout(d_out, d_in, group_size)
+    if tuple(qweight.shape) != (d_out, k_pad // 2) or not qweight.is_contiguous():
+        raise ValueError(f"qweight must be contiguous [{d_out}][{k_pad // 2}]")
+    for name, t in (("scales", scales), ("zeros", zeros)):
+        if t is not None and (tuple(t.shape) != (d_out, n_groups) or not t.is_contiguous()):
+            raise ValueError(f"{name} must be contiguous [{d_out}][{n_groups}]")
+    if bias is not None and bias.shape[0] != d_out:
+        raise ValueError(f"bias must have {d_out} elements")
+    if x.shape[1] < d_in:
+        raise ValueError(f"x has {x.shape[1]} columns, fewer than d_in={d_in}")
+    tdtype = torch.float32 if out_dtype == W4_OUT_F32 else torch.bfloat16
+    if out is None:
+        out = torch.empty((M, d_out), dtype=tdtype, device=dev)
+    else:
+        _need(out, "out", tdtype, dev, 2)
+    fn = getattr(_lib, fn_name)
+    _check(fn_name, fn(_ptr(x), M, x.stride(0), _ptr(qweight), _ptr(scales), _ptr(zeros),
+                       _ptr(bias), d_out, d_in, group_size, _ptr(out), out.stride(0), out_dtype,
+                       _stream(dev)))
+    return out
+
+
+def w4_gemv(x, qweight, scales, zeros, bias, d_in, group_size, out_dtype=W4_OUT_BF16, out=None):
+    """Decode W4A16 linear, 1 <= M <= 64: y[M][d_out] = x . W_hat^T (+ b)."""
+    return _linear("w4_gemv", x, qweight, scales, zeros, bias, d_in, group_size, out_dtype, out)
+
+
+def w4_gemm(x, qweight, scales, zeros, bias, d_in, group_size, out_dtype=W4_OUT_BF16, out=None):
+    """Prefill W4A16 linear, any M >= 1 (bf16 matrix cores)."""
+    return _linear("w4_gemm", x, qweight, scales, zeros, bias, d_in, group_size, out_dtype, out)
+
+
+def w4_linear(x, qweight, scales, zeros, bias, d_in, group_size, out_dtype=W4_OUT_BF16,
+              out=None):
+    """Dispatch by token count: the decode kernel for M <= 64, the matrix-core GEMM above."""
+    fn = w4_gemv if x.shape[0] <= GEMV_MAX_M else w4_gemm
+    return fn(x, qweight, scales, zeros, bias, d_in, group_size, out_dtype, out)
+
+
+def act_quant_int8(x, K=None, with_sum=True):
+    """Per-token int8 quantization.  Returns (q int8 [M][ldq], s_x fp32 [M], q_sum int32 [M] or
+    None); ldq is K rounded up to 16 (columns >= K are left unset)."""
+    _need(x, "x", torch.bfloat16, dim=2)
+    M = x.shape[0]
+    K = x.shape[1] if K is None else K
+    dev = x.device
+    ldq = (K + 15) // 16 * 16
+    q = torch.empty((M, ldq), dtype=torch.int8, device=dev)
+    s_x = torch.empty((M,), dtype=torch.float32, device=dev)
+    q_sum = torch.empty((M,), dtype=torch.int32, device=dev) if with_sum else None
+    _check("act_quant_int8", _lib.act_quant_int8(_ptr(x), M, K, x.stride(0), _ptr(q), ldq,
+                                                 _ptr(s_x), _ptr(q_sum), _stream(dev)))
+    return q, s_x, q_sum
+
+
+def w4a8_gemv(q, s_x, qweight, s_w, bias, d_in, out_dtype=W4_OUT_BF16, want_acc=False,
+              out=None):
+    """W4A8 decode linear.  Returns y, or (y, acc int32 [M][d_out]) when want_acc."""
+    _need(q, "q", torch.int8, dim=2)
+    dev = q.device
+    _need(s_x, "s_x", torch.float32, dev, 1)
+    _need(qweight, "qweight", torch.uint8, dev, 2)
+    s_w = s_w.reshape(-1)
+    _need(s_w, "s_w", torch.bfloat16, dev, 1)
+    if bias is not None:
+        _need(bias, "bias", torch.bfloat16, dev, 1)
+    M = q.shape[0]
+    d_out = qweight.shape[0]
+    k_pad, _, _ = packed_layout(d_out, d_in, 0)
+    if tuple(qweight.shape) != (d_out, k_pad // 2) or not qweight.is_contiguous():
+        raise ValueError(f"qweight must be contiguous [{d_out}][{k_pad // 2}]")
+    if s_w.shape[0] != d_out or (bias is not None and bias.shape[0] != d_out):
+        raise ValueError(f"s_w and bias must have {d_out} elements")
+    if s_x.shape[0] != M or q.shape[1] < d_in:
+        raise ValueError("q must be [M][>= d_in] and s_x [M]")
+    tdtype = torch.float32 if out_dtype == W4_OUT_F32 else torch.bfloat16
+    if out is None:
+        out = torch.empty((M, d_out), dtype=tdtype, device=dev)
+    else:
+        _need(out, "out", tdtype, dev, 2)
+    acc = torch.empty((M, d_out), dtype=torch.int32, device=dev) if want_acc else None
+    _check("w4a8_gemv", _lib.w4a8_gemv(_ptr(q), _ptr(s_x), M, q.stride(0), _ptr(qweight),
+                                       _ptr(s_w), _ptr(bias), d_out, d_in, _ptr(out),
+                                       out.stride(0), out_dtype, _ptr(acc), _stream(dev)))
+    return (out, acc) if want_acc else out

@@ -1,0 +1,36 @@
+// w4_launch.h -- host-side launchers of the gfx950 kernels (called by the C ABI after the
+// arguments have been validated).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4 {
+
+hipError_t launch_pack(const float *w, int64_t d_out, int64_t d_in, int64_t ldw, int64_t span,
+                       int64_t n_groups, int64_t k_pad, int mode, uint8_t *qweight,
+                       uint16_t *scales, uint16_t *zeros, hipStream_t stream);
+
+hipError_t launch_act_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int8_t *q,
+                            int64_t ldq, float *s_x, int32_t *q_sum, hipStream_t stream);
+
+// Decode W4A16 for 1 <= M <= 64 (the launcher tiles tokens in groups of at most 4).
+hipError_t launch_gemv(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
+                       const uint16_t *scales, const uint16_t *zeros, const uint16_t *bias,
+                       int64_t d_out, int64_t d_in, int64_t k_pad, int64_t span,
+                       int64_t n_groups, void *y, int64_t ldy, bool out_f32, hipStream_t stream);
+
+hipError_t launch_w4a8(const int8_t *q, const float *s_x, int64_t M, int64_t ldq,
+                       const uint8_t *qweight, const uint16_t *s_w, const uint16_t *bias,
+                       int64_t d_out, int64_t d_in, int64_t k_pad, void *y, int64_t ldy,
+                       bool out_f32, int32_t *acc, hipStream_t stream);
+
+hipError_t launch_gemm(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
+                       const uint16_t *scales, const uint16_t *zeros, const uint16_t *bias,
+                       int64_t d_out, int64_t d_in, int64_t k_pad, int64_t span,
+                       int64_t n_groups, void *y, int64_t ldy, bool out_f32, hipStream_t stream);
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+}  // namespace w4

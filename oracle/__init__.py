@@ -64,6 +64,10 @@ def _declare(lib):
     lib.oracle_bf16_to_f32.restype = ctypes.c_float
     lib.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
     lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
+    lib.oracle_bf16_to_f32_array.argtypes = [_p, _i64, _p]
+    lib.oracle_bf16_to_f32_array.restype = None
+    lib.oracle_f32_to_bf16_array.argtypes = [_p, _i64, _p]
+    lib.oracle_f32_to_bf16_array.restype = None
     lib.oracle_k_pad.argtypes = [_i64, ctypes.c_int]
     lib.oracle_k_pad.restype = _i64
     lib.oracle_n_groups.argtypes = [_i64, ctypes.c_int]
@@ -97,17 +101,19 @@ def _c(a, dtype):
 def bf16_to_f32(bits):
     """bf16 bit patterns -> fp32 values (exact)."""
     lib = _load()
-    b = np.asarray(bits, dtype=np.uint16)
-    return np.array([lib.oracle_bf16_to_f32(int(v)) for v in b.ravel()],
-                    dtype=np.float32).reshape(b.shape)
+    b = np.ascontiguousarray(bits, dtype=np.uint16)
+    out = np.empty(b.shape, dtype=np.float32)
+    lib.oracle_bf16_to_f32_array(_ptr(b), b.size, _ptr(out))
+    return out
 
 
 def f32_to_bf16(vals):
     """fp32 values -> bf16 bit patterns, round to nearest even."""
     lib = _load()
-    v = np.asarray(vals, dtype=np.float32)
-    return np.array([lib.oracle_f32_to_bf16(float(t)) for t in v.ravel()],
-                    dtype=np.uint16).reshape(v.shape)
+    v = np.ascontiguousarray(vals, dtype=np.float32)
+    out = np.empty(v.shape, dtype=np.uint16)
+    lib.oracle_f32_to_bf16_array(_ptr(v), v.size, _ptr(out))
+    return out
 
 
 def k_pad(d_in, group_size):

@@ -48,6 +48,15 @@ uint16_t oracle_f32_to_bf16(float f) {
     return (uint16_t)upper;
 }
 
+/* element-wise over arrays (the same two conversions) */
+void oracle_bf16_to_f32_array(const uint16_t *h, int64_t n, float *out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_bf16_to_f32(h[i]);
+}
+
+void oracle_f32_to_bf16_array(const float *f, int64_t n, uint16_t *out) {
+    for (int64_t i = 0; i < n; ++i) out[i] = oracle_f32_to_bf16(f[i]);
+}
+
 /* ------------------------------------------------------------------------------------------ */
 /* Packed layout.  [Lab5 INT4 线性量化]: parameters are shared per output channel and per       */
 /* group_size input columns; the input dimension is padded up to a multiple of the group size.  */

@@ -1,0 +1,176 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every function declared in
+include/w4.h, reports the packed layout, and rejects invalid arguments before touching the GPU.
+Pointer arguments here are fake addresses that the library must never dereference: every call
+below fails validation first."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4.h")
+LIB = os.path.join(ROOT, "int4_weight_only_amd", "libw4.so")
+
+W4_OK, W4_ERR_NULL, W4_ERR_SHAPE, W4_ERR_GROUP, W4_ERR_ALIGN, W4_ERR_RANGE = 0, 1, 2, 3, 4, 5
+W4_ERR_UNSUPPORTED = 6
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^(?:int|const char \*)\s*(\w+)\s*\(", text, flags=re.M)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libw4.so is not built; run __graft_entry__.build() first")
+    L = ctypes.CDLL(LIB)
+    i64, p, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
+    L.w4_packed_layout.argtypes = [i64, i64, i32, ctypes.POINTER(i64), ctypes.POINTER(i64),
+                                   ctypes.POINTER(ctypes.c_size_t)]
+    L.w4_pack.argtypes = [p, i64, i64, i64, i32, i32, p, p, p, p]
+    lin = [p, i64, i64, p, p, p, p, i64, i64, i32, p, i64, i32, p]
+    L.w4_gemv.argtypes = lin
+    L.w4_gemm.argtypes = lin
+    L.act_quant_int8.argtypes = [p, i64, i64, i64, p, i64, p, p, p]
+    L.w4a8_gemv.argtypes = [p, p, i64, i64, p, p, p, i64, i64, p, i64, i32, p, p]
+    L.w4_status_string.restype = ctypes.c_char_p
+    L.w4_last_hip_error.restype = ctypes.c_char_p
+    return L
+
+
+def test_header_declares_the_five_entry_points():
+    names = declared_functions()
+    for n in ("w4_pack", "w4_gemv", "w4_gemm", "act_quant_int8", "w4a8_gemv",
+              "w4_packed_layout", "w4_status_string", "w4_last_hip_error"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    for s in range(8):
+        assert lib.w4_status_string(s)
+    assert lib.w4_last_hip_error() == b""
+
+
+def test_packed_layout(lib):
+    kp, ng, nb = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_size_t()
+    cases = [
+        # (d_out, d_in, g) -> (k_pad, n_groups)
+        ((3584, 3600, 128), (3712, 29)),
+        ((37888, 3584, 128), (3584, 28)),
+        ((3584, 18944, 32), (18944, 592)),
+        ((18944, 3584, 0), (3584, 1)),
+        ((7, 70, 0), (96, 1)),
+        ((1, 1, 256), (256, 1)),
+    ]
+    for (d_out, d_in, g), (k_pad, n_groups) in cases:
+        assert lib.w4_packed_layout(d_out, d_in, g, ctypes.byref(kp), ctypes.byref(ng),
+                                    ctypes.byref(nb)) == W4_OK
+        assert (kp.value, ng.value, nb.value) == (k_pad, n_groups, d_out * k_pad // 2)
+    # one packed row of hidden size 3584 is 1792 bytes (the Orin page's per-row table)
+    lib.w4_packed_layout(1, 3584, 128, ctypes.byref(kp), ctypes.byref(ng), ctypes.byref(nb))
+    assert nb.value == 1792
+    assert lib.w4_packed_layout(1, 64, 48, None, None, None) == W4_ERR_GROUP
+    assert lib.w4_packed_layout(0, 64, 32, None, None, None) == W4_ERR_SHAPE
+    assert lib.w4_packed_layout(1, (1 << 24) + 1, 32, None, None, None) == W4_ERR_RANGE
+
+
+A = 0x10000  # fake, 16-byte aligned "device" addresses (never dereferenced)
+B, C, D, E = 0x20000, 0x30000, 0x40000, 0x50000
+
+
+def _lin(fn, **kw):
+    a = dict(x=A, M=1, ldx=256, qw=B, sc=C, zr=None, bias=None, d_out=128, d_in=256, g=32, y=D,
+             ldy=128, out=0)
+    a.update(kw)
+    return fn(a["x"], a["M"], a["ldx"], a["qw"], a["sc"], a["zr"], a["bias"], a["d_out"],
+              a["d_in"], a["g"], a["y"], a["ldy"], a["out"], None)
+
+
+@pytest.mark.parametrize("entry", ["w4_gemv", "w4_gemm"])
+def test_linear_rejects_bad_arguments(lib, entry):
+    fn = getattr(lib, entry)
+    assert _lin(fn, x=None) == W4_ERR_NULL
+    assert _lin(fn, qw=None) == W4_ERR_NULL
+    assert _lin(fn, sc=None) == W4_ERR_NULL
+    assert _lin(fn, y=None) == W4_ERR_NULL
+    assert _lin(fn, M=0) == W4_ERR_SHAPE
+    assert _lin(fn, d_out=0) == W4_ERR_SHAPE
+    assert _lin(fn, d_in=0) == W4_ERR_SHAPE
+    assert _lin(fn, ldx=128) == W4_ERR_SHAPE
+    assert _lin(fn, ldy=64) == W4_ERR_SHAPE
+    assert _lin(fn, g=16) == W4_ERR_GROUP
+    assert _lin(fn, g=96) == W4_ERR_GROUP
+    assert _lin(fn, out=2) == W4_ERR_UNSUPPORTED
+    assert _lin(fn, x=A + 8) == W4_ERR_ALIGN
+    assert _lin(fn, ldx=260) == W4_ERR_ALIGN
+    assert _lin(fn, qw=B + 4) == W4_ERR_ALIGN
+    assert _lin(fn, y=D + 1) == W4_ERR_ALIGN
+    assert _lin(fn, y=D + 2, out=1) == W4_ERR_ALIGN
+    assert _lin(fn, zr=E + 1) == W4_ERR_ALIGN
+    assert _lin(fn, d_in=(1 << 24) + 8, ldx=(1 << 24) + 8) == W4_ERR_RANGE
+
+
+def test_gemv_token_limit(lib):
+    # M > 64 belongs to the prefill path
+    assert _lin(lib.w4_gemv, M=65) == W4_ERR_UNSUPPORTED
+    assert _lin(lib.w4_gemv, d_in=65544, ldx=65544) == W4_ERR_RANGE
+
+
+def test_pack_rejects_bad_arguments(lib):
+    f = lib.w4_pack
+    ok = dict(w=A, d_out=128, d_in=256, ldw=256, g=32, mode=0, qw=B, sc=C, zr=None)
+
+    def call(**kw):
+        a = dict(ok)
+        a.update(kw)
+        return f(a["w"], a["d_out"], a["d_in"], a["ldw"], a["g"], a["mode"], a["qw"], a["sc"],
+                 a["zr"], None)
+
+    assert call(w=None) == W4_ERR_NULL
+    assert call(zr=E) == W4_ERR_NULL  # symmetric packs have no zeros
+    assert call(mode=1) == W4_ERR_NULL  # asymmetric packs need zeros
+    assert call(mode=2) == W4_ERR_UNSUPPORTED
+    assert call(ldw=255) == W4_ERR_SHAPE
+    assert call(g=8) == W4_ERR_GROUP
+    assert call(qw=B + 8) == W4_ERR_ALIGN
+    assert call(w=A + 2) == W4_ERR_ALIGN
+
+
+def test_act_quant_rejects_bad_arguments(lib):
+    f = lib.act_quant_int8
+    assert f(None, 1, 256, 256, B, 256, C, None, None) == W4_ERR_NULL
+    assert f(A, 0, 256, 256, B, 256, C, None, None) == W4_ERR_SHAPE
+    assert f(A, 1, 256, 128, B, 256, C, None, None) == W4_ERR_SHAPE
+    assert f(A, 1, 256, 256, B, 248, C, None, None) == W4_ERR_SHAPE
+    assert f(A, 1, 256, 256, B, 264, C, None, None) == W4_ERR_ALIGN
+    assert f(A, 1, 256, 256, B + 8, 256, C, None, None) == W4_ERR_ALIGN
+    assert f(A + 2, 1, 256, 256, B, 256, C, None, None) == W4_ERR_ALIGN
+
+
+def test_w4a8_rejects_bad_arguments(lib):
+    f = lib.w4a8_gemv
+
+    def call(**kw):
+        a = dict(q=A, sx=B, M=1, ldq=256, qw=C, sw=D, bias=None, d_out=128, d_in=256, y=E,
+                 ldy=128, out=0, acc=None)
+        a.update(kw)
+        return f(a["q"], a["sx"], a["M"], a["ldq"], a["qw"], a["sw"], a["bias"], a["d_out"],
+                 a["d_in"], a["y"], a["ldy"], a["out"], a["acc"], None)
+
+    assert call(q=None) == W4_ERR_NULL
+    assert call(sw=None) == W4_ERR_NULL
+    assert call(M=0) == W4_ERR_SHAPE
+    assert call(M=65) == W4_ERR_UNSUPPORTED
+    assert call(ldq=255) == W4_ERR_SHAPE
+    assert call(ldq=264) == W4_ERR_ALIGN
+    assert call(acc=E + 2) == W4_ERR_ALIGN
+    big = (1 << 20) + 16
+    assert call(d_in=big, ldq=big) == W4_ERR_RANGE

@@ -1,0 +1,377 @@
+"""GPU parity: every entry point of libw4.so, called through the C ABI (the thin Python binding),
+against the CPU oracle on the same seeded inputs.
+
+Bars: packing, codes, int8 activations, their scales and the W4A8 int32 accumulators are
+bit-exact; floating outputs satisfy |y - y_ref| <= 2e-3 (1 + |y_ref|) on the fp32 output, and
+the bf16 output of a call equals the round-to-nearest-even image of its fp32 output.
+"""
+import numpy as np
+import pytest
+import torch
+
+import int4_weight_only_amd as w4
+import oracle
+import workloads
+from tests.gpu_helpers import (assert_bf16_is_rne_of_f32, assert_close, dev, dev_bf16, host,
+                               host_bits)
+
+pytestmark = pytest.mark.gpu
+
+SYM, ASYM = w4.W4_SYM, w4.W4_ASYM
+F32, BF16 = w4.W4_OUT_F32, w4.W4_OUT_BF16
+
+
+def _announce(*what):
+    print("[case]", *what, flush=True)
+
+
+def gpu_pack(w, g, mode):
+    qw, sc, zr = w4.w4_pack(dev(w), g, mode)
+    return qw, sc, zr
+
+
+def check_pack_bit_exact(w, g, mode, what):
+    _announce("pack", what, w.shape, g, mode)
+    qw_o, sc_o, zr_o = oracle.pack(w, g, mode)
+    qw, sc, zr = gpu_pack(w, g, mode)
+    assert np.array_equal(host(qw), qw_o), f"{what}: packed codes differ"
+    assert np.array_equal(host_bits(sc), sc_o), f"{what}: scales differ"
+    if mode == ASYM:
+        assert np.array_equal(host_bits(zr), zr_o), f"{what}: zero points differ"
+    else:
+        assert zr is None
+    return (qw_o, sc_o, zr_o), (qw, sc, zr)
+
+
+def check_linear(entry, x_bits, packed_host, packed_dev, bias_bits, d_in, g, what,
+                 ldx=None, ldy=None):
+    """Run `entry` with fp32 and bf16 outputs; compare with oracle O4."""
+    _announce(entry, what, x_bits.shape, d_in, g)
+    qw_o, sc_o, zr_o = packed_host
+    qw, sc, zr = packed_dev
+    M = x_bits.shape[0]
+    xb = x_bits
+    if ldx is not None and ldx > x_bits.shape[1]:
+        xb = np.zeros((M, ldx), dtype=np.uint16)
+        xb[:, :x_bits.shape[1]] = x_bits
+        xb[:, x_bits.shape[1]:] = 0x7FC0  # NaN beyond the row: must never be read
+    x = dev_bf16(xb)
+    b = dev_bf16(bias_bits) if bias_bits is not None else None
+    fn = getattr(w4, entry)
+    d_out = qw.shape[0]
+    if ldy is not None:
+        out32 = torch.full((M, ldy), float("nan"), dtype=torch.float32, device="cuda")
+        y32 = fn(x, qw, sc, zr, b, d_in, g, F32, out=out32)[:, :d_out]
+    else:
+        y32 = fn(x, qw, sc, zr, b, d_in, g, F32)
+    y16 = fn(x, qw, sc, zr, b, d_in, g, BF16)
+    torch.cuda.synchronize()
+    y_ref = oracle.w4a16(x_bits, qw_o, sc_o, zr_o, bias_bits, d_in, g)
+    y32h = host(y32)
+    assert_close(y32h, y_ref, what)
+    assert_bf16_is_rne_of_f32(y16, y32h, what)
+    return y32h, y_ref
+
+
+# ------------------------------------------------------------------------------------------
+# w4_pack
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("g", [32, 64, 128, 256, 0])
+@pytest.mark.parametrize("mode", [SYM, ASYM])
+def test_pack_ragged_shapes(g, mode):
+    for d_out, d_in in ((1, 1), (3, 33), (17, 100), (64, 3600), (5, 1000)):
+        w = workloads.weight(21, d_in + g + mode, d_out, d_in)
+        workloads.add_weight_outliers(w, 21, 7, 0.02, 0.5)
+        check_pack_bit_exact(w, g, mode, f"ragged {d_out}x{d_in}")
+
+
+def test_pack_edge_values():
+    rng = np.random.default_rng(22)
+    rows = []
+    rows.append(np.zeros(128, np.float32))                        # all-zero group
+    rows.append(np.full(128, 0.25, np.float32))                   # constant group
+    rows.append(np.full(128, -3.0, np.float32))                   # constant negative group
+    rows.append((rng.normal(0, 1e-39, 128)).astype(np.float32))   # denormal weights
+    rows.append((rng.normal(0, 1e30, 128)).astype(np.float32))    # huge weights
+    rows.append(((np.arange(128) % 16 - 7.5) / 16).astype(np.float32))  # exact ties r/s + z
+    rows.append(np.linspace(1.0, 1.01, 128).astype(np.float32))   # far-from-zero group (z < 0)
+    sz = np.zeros(128, np.float32)
+    sz[::2] = -0.0
+    rows.append(sz)                                               # signed zeros
+    w = np.stack(rows)
+    for g in (32, 128, 0):
+        for mode in (SYM, ASYM):
+            check_pack_bit_exact(w, g, mode, "edge values")
+
+
+def test_pack_configs_full_size():
+    cases = [(workloads.C1, 0), (workloads.C2, 0), (workloads.C2, 1), (workloads.C3, 0),
+             (workloads.C3, 3), (workloads.C4, 1), (workloads.C5, 0), (workloads.C5, 1)]
+    for cfg, li in cases:
+        lin = cfg.linears[li]
+        w = workloads.linear_weight(cfg, li)
+        check_pack_bit_exact(w, lin.group_size, lin.mode, f"{cfg.key}/{lin.name}")
+    lin = workloads.C3.extra[0]
+    w = workloads.linear_weight(workloads.C3, 4, lin=lin)
+    check_pack_bit_exact(w, lin.group_size, lin.mode, "C3/pad3600")
+
+
+# ------------------------------------------------------------------------------------------
+# act_quant_int8
+# ------------------------------------------------------------------------------------------
+def check_act_quant(x_bits, what, K=None):
+    _announce("act_quant", what, x_bits.shape)
+    K = x_bits.shape[1] if K is None else K
+    q_o, s_o, qs_o = oracle.act_quant(x_bits, K)
+    q, s, qs = w4.act_quant_int8(dev_bf16(x_bits), K)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(q)[:, :K], q_o), f"{what}: int8 codes differ"
+    assert np.array_equal(host(s).view(np.uint32), s_o.view(np.uint32)), f"{what}: s_x differs"
+    assert np.array_equal(host(qs), qs_o), f"{what}: q_sum differs"
+
+
+def test_act_quant_configs():
+    for li, lin in enumerate(workloads.C5.linears):
+        x = workloads.linear_x(workloads.C5, li, 1)
+        check_act_quant(x, f"C5/{lin.name}")
+    x = workloads.activations(23, 0, 64, 1000, 0.01, 20.0)
+    x[5] = 0
+    check_act_quant(x, "64 tokens, ragged K, one zero token")
+
+
+def test_act_quant_all_bf16_patterns():
+    """Every finite bf16 value, quantized against several fixed maxima."""
+    allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    vals = oracle.bf16_to_f32(allbits)
+    finite = np.isfinite(vals)
+    rows = []
+    for top in (1.0, 5.0, 127.0, 3.0e38, 1e-30, 2.0 ** -126):
+        keep = allbits[finite & (np.abs(vals) <= top)]
+        top_bits = workloads.to_bf16_bits(np.array([top], np.float32))
+        rows.append(np.concatenate([top_bits, keep]))
+    K = (max(len(r) for r in rows) + 7) // 8 * 8
+    x = np.zeros((len(rows), K), dtype=np.uint16)
+    for i, r in enumerate(rows):
+        x[i, :len(r)] = r
+    check_act_quant(x, "all finite bf16 patterns")
+
+
+# ------------------------------------------------------------------------------------------
+# w4_gemv (decode, M <= 64) and w4_gemm (prefill)
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("entry", ["w4_gemv", "w4_gemm"])
+def test_linear_c1_tiny(entry):
+    cfg = workloads.C1
+    lin = cfg.linears[0]
+    w = workloads.linear_weight(cfg, 0)
+    ph, pd = check_pack_bit_exact(w, lin.group_size, lin.mode, "C1")
+    for M in cfg.tokens:
+        x = workloads.linear_x(cfg, 0, M)
+        check_linear(entry, x, ph, pd, None, lin.d_in, lin.group_size, f"C1 M={M}")
+    b = workloads.bias(cfg.seed, 0, lin.d_out)
+    x = workloads.linear_x(cfg, 0, 4)
+    check_linear(entry, x, ph, pd, b, lin.d_in, lin.group_size, "C1 M=4 with bias")
+
+
+@pytest.mark.parametrize("entry", ["w4_gemv", "w4_gemm"])
+@pytest.mark.parametrize("g", [32, 64, 128, 256, 0])
+@pytest.mark.parametrize("mode", [SYM, ASYM])
+def test_linear_ragged(entry, g, mode):
+    """Shapes that span several tiles with ragged tails in every dimension."""
+    shapes = [(1, 1, 1), (3, 130, 100), (17, 257, 1000), (64, 200, 3600)]
+    if entry == "w4_gemm":
+        shapes += [(130, 131, 300), (257, 96, 64)]
+    for M, d_out, d_in in shapes:
+        w = workloads.weight(24, M + d_out + d_in + g, d_out, d_in)
+        ph, pd = check_pack_bit_exact(w, g, mode, "ragged")
+        x = workloads.activations(24, g + mode, M, d_in)
+        b = workloads.bias(24, 1, d_out)
+        ldx = (d_in + 7) // 8 * 8 + 8
+        check_linear(entry, x, ph, pd, b, d_in, g, f"M={M} {d_out}x{d_in}", ldx=ldx,
+                     ldy=d_out + 3)
+
+
+@pytest.mark.parametrize("entry", ["w4_gemv", "w4_gemm"])
+def test_linear_basis_probes_exact(entry):
+    """x = e_k gives y[j] = w_hat[j][k] exactly in the fp32 output: pins nibble order, group
+    index, scale and zero point of every probed column."""
+    d_out, d_in = 96, 300
+    w = workloads.weight(25, 0, d_out, d_in)
+    for g, mode in ((32, SYM), (64, ASYM), (128, ASYM), (0, SYM)):
+        ph, pd = check_pack_bit_exact(w, g, mode, "probe")
+        wh = oracle.dequant(ph[0], ph[1], ph[2], d_in, g)
+        cols = [0, 1, 2, 7, 8, 31, 32, 33, 63, 64, 127, 128, 255, 256, 299]
+        x = np.zeros((len(cols), (d_in + 7) // 8 * 8), dtype=np.uint16)
+        for i, k in enumerate(cols):
+            x[i, k] = 0x3F80
+        for chunk in (slice(0, 4), slice(0, len(cols))):
+            xs = x[chunk]
+            if entry == "w4_gemv" and xs.shape[0] > 64:
+                continue
+            y = getattr(w4, entry)(dev_bf16(xs), *pd, None, d_in, g, F32)
+            got = host(y).astype(np.float64)
+            want = wh[:, [cols[i] for i in range(len(cols))][chunk]].T
+            assert np.array_equal(got, want), f"{entry} basis probe g={g} mode={mode}"
+
+
+@pytest.mark.parametrize("entry", ["w4_gemv", "w4_gemm"])
+def test_linear_padding_with_junk_activations(entry):
+    """The d_in = 3600 layer, run with d_in := k_pad = 3712 on activations whose 112 pad columns
+    hold 1e3: the result must still match the d_in = 3600 oracle, which is only possible if the
+    kernel multiplies the pad columns by exact zeros."""
+    cfg = workloads.C3
+    lin = cfg.extra[0]
+    w = workloads.linear_weight(cfg, 4, lin=lin)
+    ph, pd = check_pack_bit_exact(w, lin.group_size, lin.mode, "C3/pad3600")
+    k_pad = oracle.k_pad(lin.d_in, lin.group_size)
+    for M in cfg.tokens:
+        x = workloads.linear_x(cfg, 4, M, lin=lin)
+        check_linear(entry, x, ph, pd, None, lin.d_in, lin.group_size, f"pad3600 M={M}")
+        xj = np.zeros((M, k_pad), dtype=np.uint16)
+        xj[:, :lin.d_in] = x
+        xj[:, lin.d_in:] = workloads.to_bf16_bits(np.array([1000.0], np.float32))[0]
+        _announce(entry, "junk pads", M)
+        y = getattr(w4, entry)(dev_bf16(xj), *pd, None, k_pad, lin.group_size, F32)
+        y_ref = oracle.w4a16(x, ph[0], ph[1], ph[2], None, lin.d_in, lin.group_size)
+        assert_close(host(y), y_ref, f"junk pads M={M}")
+
+
+def test_gemv_c2_full_size():
+    cfg = workloads.C2
+    for li, lin in enumerate(cfg.linears):
+        w = workloads.linear_weight(cfg, li)
+        ph, pd = check_pack_bit_exact(w, lin.group_size, lin.mode, f"C2/{lin.name}")
+        x = workloads.linear_x(cfg, li, 1)
+        check_linear("w4_gemv", x, ph, pd, None, lin.d_in, lin.group_size, f"C2/{lin.name}")
+
+
+def test_gemv_c3_layers():
+    """Each C3 shape (asymmetric g128) at M = 1, 8, 16, for the first and the last layer."""
+    cfg = workloads.C3
+    for layer in (0, cfg.repeat_layers - 1):
+        for li, lin in enumerate(cfg.linears):
+            w = workloads.linear_weight(cfg, li, layer=layer)
+            ph, pd = check_pack_bit_exact(w, lin.group_size, lin.mode,
+                                          f"C3/L{layer}/{lin.name}")
+            for M in cfg.tokens:
+                x = workloads.linear_x(cfg, li, M, layer=layer)
+                check_linear("w4_gemv", x, ph, pd, None, lin.d_in, lin.group_size,
+                             f"C3/L{layer}/{lin.name} M={M}")
+
+
+def test_gemv_all_token_counts():
+    d_out, d_in, g = 200, 520, 64
+    w = workloads.weight(26, 0, d_out, d_in)
+    ph, pd = check_pack_bit_exact(w, g, ASYM, "M sweep")
+    for M in (1, 2, 3, 4, 5, 7, 8, 9, 16, 31, 33, 63, 64):
+        x = workloads.activations(26, M, M, d_in)
+        check_linear("w4_gemv", x, ph, pd, None, d_in, g, f"M={M}")
+
+
+def test_gemm_c4_sampled_full_size():
+    """C4 at its full size (M = 2048): every output of sampled token rows is compared with the
+    oracle, computed point by point."""
+    cfg = workloads.C4
+    rng = np.random.default_rng(404)
+    for li, lin in enumerate(cfg.linears):
+        w = workloads.linear_weight(cfg, li)
+        ph, pd = check_pack_bit_exact(w, lin.group_size, lin.mode, f"C4/{lin.name}")
+        del w
+        M = cfg.tokens[0]
+        x = workloads.linear_x(cfg, li, M)
+        _announce("w4_gemm", f"C4/{lin.name}", M)
+        xd = dev_bf16(x)
+        y32 = w4.w4_gemm(xd, *pd, None, lin.d_in, lin.group_size, F32)
+        y16 = w4.w4_gemm(xd, *pd, None, lin.d_in, lin.group_size, BF16)
+        torch.cuda.synchronize()
+        y32h = host(y32)
+        assert np.all(np.isfinite(y32h))
+        assert_bf16_is_rne_of_f32(y16, y32h, f"C4/{lin.name}")
+        toks = np.concatenate([[0, M - 1], rng.choice(M, size=6, replace=False)])
+        n_cols = min(lin.d_out, 4096)
+        for t in toks:
+            rows = np.sort(rng.choice(lin.d_out, size=n_cols, replace=False))
+            ref = oracle.w4a16_points(x, ph[0], ph[1], ph[2], None, lin.d_in, lin.group_size,
+                                      np.full(n_cols, t), rows)
+            assert_close(y32h[t, rows], ref, f"C4/{lin.name} token {t}")
+
+
+def test_gemm_matches_gemv_small_m():
+    d_out, d_in, g = 300, 1024, 32
+    w = workloads.weight(27, 0, d_out, d_in)
+    _, pd = check_pack_bit_exact(w, g, SYM, "gemm vs gemv")
+    x = dev_bf16(workloads.activations(27, 0, 8, d_in))
+    a = host(w4.w4_gemv(x, *pd, None, d_in, g, F32))
+    b = host(w4.w4_gemm(x, *pd, None, d_in, g, F32))
+    assert_close(a, b.astype(np.float64), "gemm vs gemv")
+
+
+@pytest.mark.parametrize("entry", ["w4_gemv", "w4_gemm"])
+def test_linear_deterministic(entry):
+    d_out, d_in, g = 1000, 3584, 128
+    w = workloads.weight(28, 0, d_out, d_in)
+    _, pd = check_pack_bit_exact(w, g, ASYM, "determinism")
+    x = dev_bf16(workloads.activations(28, 0, 16, d_in))
+    fn = getattr(w4, entry)
+    first = host(fn(x, *pd, None, d_in, g, F32))
+    for _ in range(3):
+        again = host(fn(x, *pd, None, d_in, g, F32))
+        assert np.array_equal(first.view(np.uint32), again.view(np.uint32))
+
+
+# ------------------------------------------------------------------------------------------
+# w4a8_gemv
+# ------------------------------------------------------------------------------------------
+def check_w4a8(w, x_bits, bias_bits, what):
+    _announce("w4a8", what, w.shape, x_bits.shape)
+    d_out, d_in = w.shape
+    ph, pd = check_pack_bit_exact(w, 0, SYM, what)
+    q_o, s_o, _ = oracle.act_quant(x_bits, d_in)
+    acc_o, y_ref, nov = oracle.w4a8(q_o, s_o, ph[0], ph[1][:, 0], bias_bits, d_in)
+    assert nov == 0
+    xpad = np.zeros((x_bits.shape[0], (d_in + 7) // 8 * 8), dtype=np.uint16)
+    xpad[:, :d_in] = x_bits
+    q, s, _ = w4.act_quant_int8(dev_bf16(xpad), d_in)
+    b = dev_bf16(bias_bits) if bias_bits is not None else None
+    y32, acc = w4.w4a8_gemv(q, s, pd[0], pd[1], b, d_in, F32, want_acc=True)
+    y16 = w4.w4a8_gemv(q, s, pd[0], pd[1], b, d_in, BF16)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(acc), acc_o), f"{what}: int32 accumulators differ"
+    y32h = host(y32)
+    assert_close(y32h, y_ref, what)
+    assert_bf16_is_rne_of_f32(y16, y32h, what)
+
+
+def test_w4a8_c5_full_size():
+    cfg = workloads.C5
+    for li, lin in enumerate(cfg.linears):
+        w = workloads.linear_weight(cfg, li)
+        x = workloads.linear_x(cfg, li, 1)
+        b = workloads.linear_bias(cfg, li)
+        check_w4a8(w, x, b, f"C5/{lin.name}")
+
+
+def test_w4a8_ragged_and_token_counts():
+    for M, d_out, d_in in ((1, 1, 1), (3, 70, 90), (5, 257, 1000), (64, 130, 3600),
+                           (16, 64, 18944)):
+        w = workloads.weight(29, M + d_in, d_out, d_in)
+        x = workloads.activations(29, M, M, d_in, 0.01, 20.0)
+        b = workloads.bias(29, 2, d_out)
+        check_w4a8(w, x, b if M % 2 else None, f"M={M} {d_out}x{d_in}")
+
+
+@pytest.mark.parametrize("H", [3584, 18944])
+def test_w4a8_worst_case_accumulator(H):
+    """All weight codes 0 (level -8) and all activations -127: acc = H * 1016 (3,641,344 for
+    H = 3584, the Orin page's bound), exactly, in int32."""
+    _announce("w4a8 worst case", H)
+    qw = torch.zeros((4, H // 2), dtype=torch.uint8, device="cuda")
+    sw = dev_bf16(workloads.to_bf16_bits(np.ones(4, np.float32)))
+    q = torch.full((1, H), -127, dtype=torch.int8, device="cuda")
+    s = torch.ones(1, dtype=torch.float32, device="cuda")
+    y, acc = w4.w4a8_gemv(q, s, qw, sw, None, H, F32, want_acc=True)
+    torch.cuda.synchronize()
+    assert host(acc).tolist() == [[H * 1016] * 4]
+    if H == 3584:
+        assert H * 1016 == 3641344
+    assert host(y).tolist() == [[float(H * 1016)] * 4]
