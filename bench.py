@@ -90,12 +90,38 @@ class Timer:
         return float(np.mean(v)) if v else float("nan")
 
 
+def graph_ms(torch, body, launches, replays):
+    """Capture `body` (which enqueues `launches` kernel calls through the library) in a HIP graph
+    and time `replays` replays with HIP events on the replaying stream; returns ms per launch.
+    Graph replay keeps the GPU fed: the Python binding's per-call cost does not enter the
+    measured region."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        body()  # warm-up outside the graph
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        body()
+    g.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(replays):
+        g.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / (replays * launches)
+    del g
+    return ms
+
+
 def bench_c2(torch, w4, workloads, steps, warmup, rotate_bytes):
     cfg = workloads.C2
     gu, dn = cfg.linears
     dev = torch.device("cuda", 0)
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(cfg.seed)
 
     def packed(lin, li):
         w = torch.from_numpy(workloads.linear_weight(cfg, li)).to(dev)
@@ -114,40 +140,31 @@ def bench_c2(torch, w4, workloads, steps, warmup, rotate_bytes):
     y_gu = torch.empty((1, gu.d_out), dtype=torch.bfloat16, device=dev)
     y_dn = torch.empty((1, dn.d_out), dtype=torch.bfloat16, device=dev)
 
-    def step(i, timer=None):
-        c = copies[i % n_copies]
-        if timer:
-            timer.start("gate_up")
+    def gate_up(c):
         w4.w4_gemv(x_gu, *c[0], None, gu.d_in, gu.group_size, out=y_gu)
-        if timer:
-            timer.stop("gate_up")
-            timer.start("down")
+
+    def down(c):
         w4.w4_gemv(x_dn, *c[1], None, dn.d_in, dn.group_size, out=y_dn)
-        if timer:
-            timer.stop("down")
+
+    def steps_body():
+        for c in copies:
+            gate_up(c)
+            down(c)
 
     for i in range(warmup):
-        step(i)
+        c = copies[i % n_copies]
+        gate_up(c)
+        down(c)
     torch.cuda.synchronize()
-    # whole-step time: no events between the launches
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for i in range(steps):
-        step(i)
-    t1.record()
-    torch.cuda.synchronize()
-    step_ms = t0.elapsed_time(t1) / steps
-    # per-kernel durations, events around each launch
-    timer = Timer(torch)
-    for i in range(steps):
-        step(i, timer)
-    torch.cuda.synchronize()
+    replays = max(1, steps // n_copies)
+    step_ms = graph_ms(torch, steps_body, n_copies, replays)
+    gu_ms = graph_ms(torch, lambda: [gate_up(c) for c in copies], n_copies, replays)
+    dn_ms = graph_ms(torch, lambda: [down(c) for c in copies], n_copies, replays)
     b_gu = linear_bytes(1, gu.d_out, gu.d_in, gu.group_size, False)
     b_dn = linear_bytes(1, dn.d_out, dn.d_in, dn.group_size, False)
-    return dict(step_ms=step_ms, bytes_step=b_gu + b_dn, gu_ms=timer.mean_ms("gate_up"),
-                dn_ms=timer.mean_ms("down"), b_gu=b_gu, b_dn=b_dn, n_copies=n_copies,
-                rotate_mb=n_copies * per_copy / 1e6)
+    return dict(step_ms=step_ms, bytes_step=b_gu + b_dn, gu_ms=gu_ms, dn_ms=dn_ms, b_gu=b_gu,
+                b_dn=b_dn, n_copies=n_copies, rotate_mb=n_copies * per_copy / 1e6,
+                steps_timed=replays * n_copies)
 
 
 def bench_c4(torch, w4, workloads, iters):
@@ -203,22 +220,19 @@ def bench_c5(torch, w4, workloads, iters):
             torch.bfloat16).to(dev)
         y = torch.empty((1, lin.d_out), dtype=torch.bfloat16, device=dev)
         q, s_x, _ = w4.act_quant_int8(x, lin.d_in, with_sum=False)
-        for i in range(4):
-            c = copies[i % n_copies]
-            w4.w4a8_gemv(q, s_x, c[0], c[1], b, lin.d_in, out=y)
-        torch.cuda.synchronize()
-        timer = Timer(torch)
-        for i in range(iters):
-            c = copies[i % n_copies]
-            timer.start("aq")
-            w4.act_quant_int8(x, lin.d_in, with_sum=False)
-            timer.stop("aq")
-            timer.start("gemv")
-            w4.w4a8_gemv(q, s_x, c[0], c[1], b, lin.d_in, out=y)
-            timer.stop("gemv")
-        torch.cuda.synchronize()
-        gemv_ms = timer.mean_ms("gemv")
-        aq_ms = timer.mean_ms("aq")
+
+        def gemvs():
+            for c in copies:
+                w4.w4a8_gemv(q, s_x, c[0], c[1], b, lin.d_in, out=y)
+
+        def quants():
+            for _ in copies:
+                w4.act_quant_int8(x, lin.d_in, with_sum=False)
+
+        gemv_ms_g = graph_ms(torch, gemvs, n_copies, max(1, iters // n_copies))
+        aq_ms_g = graph_ms(torch, quants, n_copies, max(1, iters // n_copies))
+        gemv_ms = gemv_ms_g
+        aq_ms = aq_ms_g
         gb = linear_bytes(1, lin.d_out, lin.d_in, 0, False, bias=True, x_bytes=1) + 4
         aq_bytes = 2 * lin.d_in + lin.d_in + 4
         out[f"{lin.d_out}x{lin.d_in}"] = dict(
@@ -257,16 +271,7 @@ def bench_c3(torch, w4, workloads, iters):
                 for lin, p, x, y in zip(cfg.linears, packs, xs, ys):
                     w4.w4_gemv(x, *p, None, lin.d_in, lin.group_size, out=y)
 
-        step()
-        torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
-        t0.record()
-        for _ in range(iters):
-            step()
-        t1.record()
-        torch.cuda.synchronize()
-        ms = t0.elapsed_time(t1) / iters
+        ms = graph_ms(torch, step, 1, iters)
         nbytes = cfg.repeat_layers * sum(linear_bytes(M, l.d_out, l.d_in, l.group_size, True)
                                          for l in cfg.linears)
         out[f"M={M}"] = dict(step_us=round(ms * 1e3, 1), gbs=round(nbytes / ms / 1e6, 1),
@@ -341,7 +346,7 @@ def main():
         if args.only != "c2":
             print(json.dumps(secondary), flush=True)
             return
-    if not args.no_secondary:
+    if not args.no_secondary and args.only is None:
         log("C4 prefill GEMM")
         secondary["C4_prefill_gemm"] = bench_c4(torch, w4, workloads, 10)
         log("C5 W4A8")
@@ -384,12 +389,13 @@ def main():
             "tokens": 1,
             "bytes_per_step": r["bytes_step"],
             "weight_copies_rotated": r["n_copies"],
+            "timing": "HIP graph replays of the library launches, HIP events on the stream",
             "rotated_mb": round(r["rotate_mb"], 1),
             "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         },
         "roofline": roofline,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.only is None:
         log("CPU oracle baseline")
         line["cpu_baseline"] = cpu_baseline(workloads, args.cpu_budget_s)
     if secondary:

@@ -16,12 +16,16 @@
 //     [Orin o2-all 和 o4-all 为什么能加速], applied to every row a wave visits);
 //   * lane partials are summed across the wave with cross-lane shuffles and across the S waves
 //     of a stream through LDS; the sums run in a fixed order, so results are deterministic.
+#include <stdlib.h>
+
 #include "w4_device.h"
 #include "w4_launch.h"
 
 namespace w4 {
 
 namespace {
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kChunkCols = 32;  // columns per 16-byte chunk
 constexpr int kBlockThreads = 256;  // launch size of every decode kernel (= its launch bound)
@@ -41,7 +45,7 @@ constexpr int kMaxS = kBlockThreads / kWave;  // waves sharing one row
 // bf16 inputs) are split into such an integer and a residual applied through the chunk's
 // activation sum.
 // ---------------------------------------------------------------------------------------------
-template <int MT, int T, bool ZP>
+template <int MT, int T, int U, bool ZP>
 __global__ void __launch_bounds__(kBlockThreads) gemv_w4a16_kernel(
     const uint16_t *__restrict__ x, int64_t ldx, int M, const uint8_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
@@ -59,6 +63,39 @@ __global__ void __launch_bounds__(kBlockThreads) gemv_w4a16_kernel(
     const int64_t cpr = k_pad / kChunkCols;
     const int64_t row_bytes = k_pad / 2;
 
+    // Rows are visited in batches of U; the loads of the next batch (codes, scales and zero
+    // points) are issued before the current batch is computed, and the first batch is requested
+    // before the activation set-up.  Vector-memory loads retire in order, so every load the
+    // compute needs is part of a batch: nothing issued later can make it wait for the prefetch.
+    struct Batch {
+        u32x4_t w[U][T];
+        uint32_t sz[U][T];  // scale bits | zero-point bits << 16
+    };
+    auto load_batch = [&](int it0, Batch &dst) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t row = stream_id + (int64_t)(it0 + u) * total_streams;
+            const bool row_ok = (it0 + u) < R && row < d_out;
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                // Loads are unconditional (an out-of-range lane reads row 0, chunk 0, and its
+                // data is never used) so the compiler can count outstanding loads exactly.
+                const int64_t c = (int64_t)(s_idx * T + t) * kWave + lane;
+                const bool ok = row_ok && c < cpr;
+                const int64_t rr = ok ? row : 0;
+                const int64_t cc = ok ? c : 0;
+                dst.w[u][t] = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4_t *>(qweight + rr * row_bytes) + cc);
+                const int64_t gi = rr * n_groups + (cc >> chunk_group_shift);
+                uint32_t v = scales[gi];
+                if (ZP) v |= static_cast<uint32_t>(zeros[gi]) << 16;
+                dst.sz[u][t] = v;
+            }
+        }
+    };
+    Batch wa, wb;
+    load_batch(0, wa);
+
     // ---- activations of this lane's chunk columns, in registers for the whole kernel ----
     // Two passes over the (cached) activations keep the set-up's register use low: the first
     // finds the lane's max |x| per token, the second converts and pairs the values.
@@ -67,10 +104,9 @@ __global__ void __launch_bounds__(kBlockThreads) gemv_w4a16_kernel(
     int xexp[MT];
     auto load_piece = [&](int m, int64_t c, int p, float *dst) {
         const int64_t col = c * kChunkCols + 8 * p;
-        uint4 v = make_uint4(0, 0, 0, 0);
-        if (m < M && c < cpr && col < d_in)
-            v = *reinterpret_cast<const uint4 *>(x + (int64_t)m * ldx + col);
-        const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+        const bool ok = m < M && c < cpr && col < d_in;
+        const uint4 v = *reinterpret_cast<const uint4 *>(x + (ok ? (int64_t)m * ldx + col : 0));
+        const uint32_t u[4] = {ok ? v.x : 0u, ok ? v.y : 0u, ok ? v.z : 0u, ok ? v.w : 0u};
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const uint32_t bits = (e & 1) ? (u[e >> 1] >> 16) : (u[e >> 1] & 0xFFFFu);
@@ -116,83 +152,78 @@ __global__ void __launch_bounds__(kBlockThreads) gemv_w4a16_kernel(
         }
     }
 
-    auto load_row = [&](int64_t row, uint4 *dst) {
+    const half2_t one16 = {static_cast<half_t>(0.0625f), static_cast<half_t>(0.0625f)};
+    auto compute_batch = [&](int it0, const Batch &bt) {
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-            const int64_t c = (int64_t)(s_idx * T + t) * kWave + lane;
-            if (row < d_out && c < cpr)
-                dst[t] = *reinterpret_cast<const uint4 *>(qweight + row * row_bytes + 16 * c);
-            else
-                dst[t] = make_uint4(0, 0, 0, 0);
+        for (int u = 0; u < U; ++u) {
+            const int it = it0 + u;
+            if (it >= R) break;  // uniform across the block
+            const int64_t row = stream_id + (int64_t)it * total_streams;
+            float acc[MT];
+#pragma unroll
+            for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
+            if (row < d_out) {
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    const int64_t c = (int64_t)(s_idx * T + t) * kWave + lane;
+                    if (c >= cpr) continue;
+                    const float s = bf16_to_f32(bt.sz[u][t] & 0xFFFFu);
+                    float z = 8.0f;
+                    if (ZP) z = bf16_to_f32(bt.sz[u][t] >> 16);
+                    const bool zint = (z == __builtin_rintf(z)) && fabsf(z) <= 1024.0f;
+                    const float zi = zint ? z : 0.0f;
+                    const float zres = z - zi;
+                    const half_t n0 = static_cast<half_t>(-(1024.0f + zi));
+                    const half_t n1 = static_cast<half_t>(-(64.0f + zi));
+                    const half2_t nz0 = {n0, n0};
+                    const half2_t nz1 = {n1, n1};
+                    const uint32_t wv[4] = {bt.w[u][t][0], bt.w[u][t][1], bt.w[u][t][2],
+                                            bt.w[u][t][3]};
+                    float d0[MT], d1[MT];
+#pragma unroll
+                    for (int m = 0; m < MT; ++m) {
+                        d0[m] = 0.0f;
+                        d1[m] = 0.0f;
+                    }
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t w0 = wv[j];
+                        const uint32_t w8 = w0 >> 8;
+                        const half2_t a0 = as_half2((w0 & 0x000F000Fu) | 0x64006400u) + nz0;
+                        const half2_t a1 = __builtin_elementwise_fma(
+                            as_half2((w0 & 0x00F000F0u) | 0x64006400u), one16, nz1);
+                        const half2_t a2 = as_half2((w8 & 0x000F000Fu) | 0x64006400u) + nz0;
+                        const half2_t a3 = __builtin_elementwise_fma(
+                            as_half2((w8 & 0x00F000F0u) | 0x64006400u), one16, nz1);
+#pragma unroll
+                        for (int m = 0; m < MT; ++m) {
+                            d0[m] = __builtin_amdgcn_fdot2(a0, xf[m][t][4 * j + 0], d0[m], false);
+                            d1[m] = __builtin_amdgcn_fdot2(a1, xf[m][t][4 * j + 1], d1[m], false);
+                            d0[m] = __builtin_amdgcn_fdot2(a2, xf[m][t][4 * j + 2], d0[m], false);
+                            d1[m] = __builtin_amdgcn_fdot2(a3, xf[m][t][4 * j + 3], d1[m], false);
+                        }
+                    }
+#pragma unroll
+                    for (int m = 0; m < MT; ++m) {
+                        const float chunk = (d0[m] + d1[m]) - zres * xsum[m][t];
+                        acc[m] = fmaf(s, chunk, acc[m]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const float v = wave_sum_dpp(ldexpf(acc[m], xexp[m]));
+                if (lane == 0) partial[((stream_blk * R + it) * S + s_idx) * MT + m] = v;
+            }
         }
     };
 
-    const half2_t one16 = {static_cast<half_t>(0.0625f), static_cast<half_t>(0.0625f)};
-    uint4 wcur[T], wnxt[T];
-    int64_t row = stream_id;
-    load_row(row, wcur);
-    for (int it = 0; it < R; ++it) {
-        const int64_t next = row + total_streams;
-        if (it + 1 < R) load_row(next, wnxt);
-        float acc[MT];
-#pragma unroll
-        for (int m = 0; m < MT; ++m) acc[m] = 0.0f;
-        if (row < d_out) {
-#pragma unroll
-            for (int t = 0; t < T; ++t) {
-                const int64_t c = (int64_t)(s_idx * T + t) * kWave + lane;
-                if (c >= cpr) continue;
-                const int64_t G = c >> chunk_group_shift;
-                const float s = bf16_to_f32(scales[row * n_groups + G]);
-                float z = 8.0f;
-                if (ZP) z = bf16_to_f32(zeros[row * n_groups + G]);
-                const bool zint = (z == __builtin_rintf(z)) && fabsf(z) <= 1024.0f;
-                const float zi = zint ? z : 0.0f;
-                const float zres = z - zi;
-                const half_t n0 = static_cast<half_t>(-(1024.0f + zi));
-                const half_t n1 = static_cast<half_t>(-(64.0f + zi));
-                const half2_t nz0 = {n0, n0};
-                const half2_t nz1 = {n1, n1};
-                const uint32_t wv[4] = {wcur[t].x, wcur[t].y, wcur[t].z, wcur[t].w};
-                float d0[MT], d1[MT];
-#pragma unroll
-                for (int m = 0; m < MT; ++m) {
-                    d0[m] = 0.0f;
-                    d1[m] = 0.0f;
-                }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t w0 = wv[j];
-                    const uint32_t w8 = w0 >> 8;
-                    const half2_t a0 = as_half2((w0 & 0x000F000Fu) | 0x64006400u) + nz0;
-                    const half2_t a1 = __builtin_elementwise_fma(
-                        as_half2((w0 & 0x00F000F0u) | 0x64006400u), one16, nz1);
-                    const half2_t a2 = as_half2((w8 & 0x000F000Fu) | 0x64006400u) + nz0;
-                    const half2_t a3 = __builtin_elementwise_fma(
-                        as_half2((w8 & 0x00F000F0u) | 0x64006400u), one16, nz1);
-#pragma unroll
-                    for (int m = 0; m < MT; ++m) {
-                        d0[m] = __builtin_amdgcn_fdot2(a0, xf[m][t][4 * j + 0], d0[m], false);
-                        d1[m] = __builtin_amdgcn_fdot2(a1, xf[m][t][4 * j + 1], d1[m], false);
-                        d0[m] = __builtin_amdgcn_fdot2(a2, xf[m][t][4 * j + 2], d0[m], false);
-                        d1[m] = __builtin_amdgcn_fdot2(a3, xf[m][t][4 * j + 3], d1[m], false);
-                    }
-                }
-#pragma unroll
-                for (int m = 0; m < MT; ++m) {
-                    const float chunk = (d0[m] + d1[m]) - zres * xsum[m][t];
-                    acc[m] = fmaf(s, chunk, acc[m]);
-                }
-            }
-        }
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const float v = wave_sum(ldexpf(acc[m], xexp[m]));
-            if (lane == 0) partial[((stream_blk * R + it) * S + s_idx) * MT + m] = v;
-        }
-        row = next;
-#pragma unroll
-        for (int t = 0; t < T; ++t) wcur[t] = wnxt[t];
+    for (int it0 = 0; it0 < R; it0 += 2 * U) {
+        if (it0 + U < R) load_batch(it0 + U, wb);
+        compute_batch(it0, wa);
+        if (it0 + U >= R) break;
+        if (it0 + 2 * U < R) load_batch(it0 + 2 * U, wa);
+        compute_batch(it0 + U, wb);
     }
     __syncthreads();
     const int n_out = n_streams_blk * R * MT;
@@ -217,7 +248,7 @@ __global__ void __launch_bounds__(kBlockThreads) gemv_w4a16_kernel(
 // way once, and v_dot4_i32_i8 accumulates code * q exactly.  The offset of 8 is removed with the
 // lane's own activation sum: sum (c - 8) q = sum c q - 8 sum q, all in int32.
 // ---------------------------------------------------------------------------------------------
-template <int MT, int T>
+template <int MT, int T, int U>
 __global__ void __launch_bounds__(kBlockThreads) gemv_w4a8_kernel(
     const int8_t *__restrict__ q, int64_t ldq, int M, const float *__restrict__ s_x,
     const uint8_t *__restrict__ qweight, const uint16_t *__restrict__ s_w,
@@ -235,6 +266,25 @@ __global__ void __launch_bounds__(kBlockThreads) gemv_w4a8_kernel(
     const int64_t cpr = k_pad / kChunkCols;
     const int64_t row_bytes = k_pad / 2;
 
+    auto load_batch = [&](int it0, u32x4_t (&dst)[U][T]) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t row = stream_id + (int64_t)(it0 + u) * total_streams;
+            const bool row_ok = (it0 + u) < R && row < d_out;
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
+                // unconditional loads (see the W4A16 kernel); unused lanes read row 0, chunk 0
+                const int64_t c = (int64_t)(s_idx * T + t) * kWave + lane;
+                const bool ok = row_ok && c < cpr;
+                dst[u][t] = __builtin_nontemporal_load(
+                    reinterpret_cast<const u32x4_t *>(qweight + (ok ? row : 0) * row_bytes) +
+                    (ok ? c : 0));
+            }
+        }
+    };
+    u32x4_t wa[U][T], wb[U][T];
+    load_batch(0, wa);
+
     uint32_t xe[MT][T][4], xo[MT][T][4];
     int qsum[MT];
 #pragma unroll
@@ -247,13 +297,13 @@ __global__ void __launch_bounds__(kBlockThreads) gemv_w4a8_kernel(
 #pragma unroll
             for (int p = 0; p < 2; ++p) {
                 const int64_t col = c * kChunkCols + 16 * p;
-                uint4 v = make_uint4(0, 0, 0, 0);
-                if (m < M && c < cpr && col < d_in)
-                    v = *reinterpret_cast<const uint4 *>(q + (int64_t)m * ldq + col);
-                u[4 * p + 0] = v.x;
-                u[4 * p + 1] = v.y;
-                u[4 * p + 2] = v.z;
-                u[4 * p + 3] = v.w;
+                const bool ok = m < M && c < cpr && col < d_in;
+                const uint4 v =
+                    *reinterpret_cast<const uint4 *>(q + (ok ? (int64_t)m * ldq + col : 0));
+                u[4 * p + 0] = ok ? v.x : 0u;
+                u[4 * p + 1] = ok ? v.y : 0u;
+                u[4 * p + 2] = ok ? v.z : 0u;
+                u[4 * p + 3] = ok ? v.w : 0u;
             }
             // zero the columns at or beyond d_in, and add up the rest
 #pragma unroll
@@ -272,54 +322,49 @@ __global__ void __launch_bounds__(kBlockThreads) gemv_w4a8_kernel(
         qsum[m] = sum;
     }
 
-    auto load_row = [&](int64_t row, uint4 *dst) {
+    auto compute_batch = [&](int it0, const u32x4_t (&w)[U][T]) {
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-            const int64_t c = (int64_t)(s_idx * T + t) * kWave + lane;
-            if (row < d_out && c < cpr)
-                dst[t] = *reinterpret_cast<const uint4 *>(qweight + row * row_bytes + 16 * c);
-            else
-                dst[t] = make_uint4(0, 0, 0, 0);
+        for (int u = 0; u < U; ++u) {
+            const int it = it0 + u;
+            if (it >= R) break;  // uniform across the block
+            const int64_t row = stream_id + (int64_t)it * total_streams;
+            int acc[MT];
+#pragma unroll
+            for (int m = 0; m < MT; ++m) acc[m] = 0;
+            if (row < d_out) {
+#pragma unroll
+                for (int t = 0; t < T; ++t) {
+                    const uint32_t wv[4] = {w[u][t][0], w[u][t][1], w[u][t][2], w[u][t][3]};
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int lo = static_cast<int>(wv[j] & 0x0F0F0F0Fu);
+                        const int hi = static_cast<int>((wv[j] >> 4) & 0x0F0F0F0Fu);
+#pragma unroll
+                        for (int m = 0; m < MT; ++m) {
+                            acc[m] = __builtin_amdgcn_sdot4(lo, static_cast<int>(xe[m][t][j]),
+                                                            acc[m], false);
+                            acc[m] = __builtin_amdgcn_sdot4(hi, static_cast<int>(xo[m][t][j]),
+                                                            acc[m], false);
+                        }
+                    }
+                }
+#pragma unroll
+                for (int m = 0; m < MT; ++m) acc[m] -= 8 * qsum[m];
+            }
+#pragma unroll
+            for (int m = 0; m < MT; ++m) {
+                const int v = wave_sum_dpp(acc[m]);
+                if (lane == 0) ipartial[((stream_blk * R + it) * S + s_idx) * MT + m] = v;
+            }
         }
     };
 
-    uint4 wcur[T], wnxt[T];
-    int64_t row = stream_id;
-    load_row(row, wcur);
-    for (int it = 0; it < R; ++it) {
-        const int64_t next = row + total_streams;
-        if (it + 1 < R) load_row(next, wnxt);
-        int acc[MT];
-#pragma unroll
-        for (int m = 0; m < MT; ++m) acc[m] = 0;
-        if (row < d_out) {
-#pragma unroll
-            for (int t = 0; t < T; ++t) {
-                const uint32_t wv[4] = {wcur[t].x, wcur[t].y, wcur[t].z, wcur[t].w};
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int lo = static_cast<int>(wv[j] & 0x0F0F0F0Fu);
-                    const int hi = static_cast<int>((wv[j] >> 4) & 0x0F0F0F0Fu);
-#pragma unroll
-                    for (int m = 0; m < MT; ++m) {
-                        acc[m] = __builtin_amdgcn_sdot4(lo, static_cast<int>(xe[m][t][j]), acc[m],
-                                                        false);
-                        acc[m] = __builtin_amdgcn_sdot4(hi, static_cast<int>(xo[m][t][j]), acc[m],
-                                                        false);
-                    }
-                }
-            }
-#pragma unroll
-            for (int m = 0; m < MT; ++m) acc[m] -= 8 * qsum[m];
-        }
-#pragma unroll
-        for (int m = 0; m < MT; ++m) {
-            const int v = wave_sum(acc[m]);
-            if (lane == 0) ipartial[((stream_blk * R + it) * S + s_idx) * MT + m] = v;
-        }
-        row = next;
-#pragma unroll
-        for (int t = 0; t < T; ++t) wcur[t] = wnxt[t];
+    for (int it0 = 0; it0 < R; it0 += 2 * U) {
+        if (it0 + U < R) load_batch(it0 + U, wb);
+        compute_batch(it0, wa);
+        if (it0 + U >= R) break;
+        if (it0 + 2 * U < R) load_batch(it0 + 2 * U, wa);
+        compute_batch(it0 + U, wb);
     }
     __syncthreads();
     const int n_out = n_streams_blk * R * MT;
@@ -340,9 +385,16 @@ __global__ void __launch_bounds__(kBlockThreads) gemv_w4a8_kernel(
     }
 }
 
+// Rows per batch: the double-buffered weights of 2 * U * T chunks stay within 64 registers.
+constexpr int batch_rows(int T) { return T >= 5 ? 1 : (8 / T > 4 ? 4 : 8 / T); }
+
 struct DecodePlan {
     int T, S, waves, grid, R;
 };
+
+// Workgroups per compute unit of the persistent decode grid.
+constexpr int kDecodeBlocksPerCu = 2;
+int decode_blocks_per_cu() { return kDecodeBlocksPerCu; }
 
 // Waves (at most kMaxS, all in one 256-thread workgroup) x T steps needed to cover a row of
 // `cpr` chunks; returns T, or a value above t_max if even kMaxS waves are not enough.
@@ -360,14 +412,19 @@ DecodePlan plan_decode(int64_t d_out, int64_t cpr, int t_max) {
     p.T = steps_needed(cpr, S);
     p.waves = kBlockThreads / kWave;
     const int n_streams_blk = p.waves / S;
+    // A persistent grid of a few blocks per CU; every stream walks R rows.
     const int64_t want_blocks = (d_out + n_streams_blk - 1) / n_streams_blk;
-    int64_t max_blocks = (int64_t)device_cu_count() * 8;
-    // keep at most 64 rows per stream (bounds the per-row LDS partials)
-    const int64_t min_blocks = (d_out + (int64_t)n_streams_blk * 64 - 1) / ((int64_t)n_streams_blk * 64);
-    if (max_blocks < min_blocks) max_blocks = min_blocks;
-    p.grid = static_cast<int>(want_blocks < max_blocks ? want_blocks : max_blocks);
-    const int64_t streams = (int64_t)p.grid * n_streams_blk;
+    int64_t blocks = (int64_t)device_cu_count() * decode_blocks_per_cu();
+    // at most 64 rows per stream (bounds the per-row LDS partials)
+    const int64_t min_blocks =
+        (d_out + (int64_t)n_streams_blk * 64 - 1) / ((int64_t)n_streams_blk * 64);
+    if (blocks < min_blocks) blocks = min_blocks;
+    if (blocks > want_blocks) blocks = want_blocks;
+    const int64_t streams = blocks * n_streams_blk;
     p.R = static_cast<int>((d_out + streams - 1) / streams);
+    // with R fixed, use no more blocks than the rows need
+    p.grid = static_cast<int>((d_out + (int64_t)p.R * n_streams_blk - 1) /
+                              ((int64_t)p.R * n_streams_blk));
     return p;
 }
 
@@ -378,14 +435,17 @@ hipError_t launch_w4a16_t(const DecodePlan &p, bool zp, const uint16_t *x, int64
                           int shift, int64_t n_groups, void *y, int64_t ldy, bool out_f32,
                           hipStream_t stream) {
     const size_t lds = sizeof(float) * (size_t)(p.waves / p.S) * p.R * p.S * MT;
+    constexpr int U = batch_rows(T);
     if (zp)
-        hipLaunchKernelGGL((gemv_w4a16_kernel<MT, T, true>), dim3(p.grid), dim3(p.waves * kWave),
-                           lds, stream, x, ldx, M, qweight, scales, zeros, bias, d_out, d_in,
-                           k_pad, shift, n_groups, y, ldy, out_f32 ? 1 : 0, p.S, p.R);
+        hipLaunchKernelGGL((gemv_w4a16_kernel<MT, T, U, true>), dim3(p.grid),
+                           dim3(p.waves * kWave), lds, stream, x, ldx, M, qweight, scales, zeros,
+                           bias, d_out, d_in, k_pad, shift, n_groups, y, ldy, out_f32 ? 1 : 0,
+                           p.S, p.R);
     else
-        hipLaunchKernelGGL((gemv_w4a16_kernel<MT, T, false>), dim3(p.grid), dim3(p.waves * kWave),
-                           lds, stream, x, ldx, M, qweight, scales, zeros, bias, d_out, d_in,
-                           k_pad, shift, n_groups, y, ldy, out_f32 ? 1 : 0, p.S, p.R);
+        hipLaunchKernelGGL((gemv_w4a16_kernel<MT, T, U, false>), dim3(p.grid),
+                           dim3(p.waves * kWave), lds, stream, x, ldx, M, qweight, scales, zeros,
+                           bias, d_out, d_in, k_pad, shift, n_groups, y, ldy, out_f32 ? 1 : 0,
+                           p.S, p.R);
     return hipGetLastError();
 }
 
@@ -425,7 +485,8 @@ hipError_t launch_w4a8_t(const DecodePlan &p, const int8_t *q, int64_t ldq, int 
                          const uint16_t *bias, int64_t d_out, int64_t d_in, int64_t k_pad,
                          void *y, int64_t ldy, bool out_f32, int32_t *acc, hipStream_t stream) {
     const size_t lds = sizeof(int) * (size_t)(p.waves / p.S) * p.R * p.S * MT;
-    hipLaunchKernelGGL((gemv_w4a8_kernel<MT, T>), dim3(p.grid), dim3(p.waves * kWave), lds, stream,
+    constexpr int U = batch_rows(T);
+    hipLaunchKernelGGL((gemv_w4a8_kernel<MT, T, U>), dim3(p.grid), dim3(p.waves * kWave), lds, stream,
                        q, ldq, M, s_x, qweight, s_w, bias, d_out, d_in, k_pad, y, ldy,
                        out_f32 ? 1 : 0, acc, p.S, p.R);
     return hipGetLastError();
@@ -470,6 +531,11 @@ hipError_t launch_gemv(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t 
     const int64_t cpr = k_pad / kChunkCols;
     // chunks per group is a power of two (group sizes 32..256); one group per row -> shift 62
     const int shift = n_groups == 1 ? 62 : log2_exact(span / kChunkCols);
+    // the streaming kernel serves rows up to its LDS budget; longer rows (and tokens in tiles of
+    // up to 4) fall back to the per-row kernels below
+    if (gemv_stream_supported(M, k_pad))
+        return launch_gemv_stream(x, M, ldx, qweight, scales, zeros, bias, d_out, d_in, k_pad,
+                                  shift, n_groups, y, ldy, out_f32, stream);
     const bool zp = zeros != nullptr;
     const size_t out_elem = out_f32 ? sizeof(float) : sizeof(uint16_t);
     int mt_max = 4;
@@ -509,6 +575,9 @@ hipError_t launch_w4a8(const int8_t *q, const float *s_x, int64_t M, int64_t ldq
                        const uint8_t *qweight, const uint16_t *s_w, const uint16_t *bias,
                        int64_t d_out, int64_t d_in, int64_t k_pad, void *y, int64_t ldy,
                        bool out_f32, int32_t *acc, hipStream_t stream) {
+    if (w4a8_stream_supported(M, k_pad))  // see launch_gemv
+        return launch_w4a8_stream(q, s_x, M, ldq, qweight, s_w, bias, d_out, d_in, k_pad, y, ldy,
+                                  out_f32, acc, stream);
     const int64_t cpr = k_pad / kChunkCols;
     const size_t out_elem = out_f32 ? sizeof(float) : sizeof(uint16_t);
     int mt_max = 4;

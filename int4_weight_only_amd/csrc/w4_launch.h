@@ -30,6 +30,19 @@ hipError_t launch_gemm(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t 
                        int64_t d_out, int64_t d_in, int64_t k_pad, int64_t span,
                        int64_t n_groups, void *y, int64_t ldy, bool out_f32, hipStream_t stream);
 
+// Persistent streaming decode GEMVs (decode_stream.hip).
+bool gemv_stream_supported(int64_t M, int64_t k_pad);
+bool w4a8_stream_supported(int64_t M, int64_t k_pad);
+hipError_t launch_gemv_stream(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
+                              const uint16_t *scales, const uint16_t *zeros, const uint16_t *bias,
+                              int64_t d_out, int64_t d_in, int64_t k_pad, int chunk_group_shift,
+                              int64_t n_groups, void *y, int64_t ldy, bool out_f32,
+                              hipStream_t stream);
+hipError_t launch_w4a8_stream(const int8_t *q, const float *s_x, int64_t M, int64_t ldq,
+                              const uint8_t *qweight, const uint16_t *s_w, const uint16_t *bias,
+                              int64_t d_out, int64_t d_in, int64_t k_pad, void *y, int64_t ldy,
+                              bool out_f32, int32_t *acc, hipStream_t stream);
+
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 
