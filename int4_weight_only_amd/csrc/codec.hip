@@ -91,48 +91,115 @@ __global__ void __launch_bounds__(256) pack_kernel(const float *__restrict__ w, 
     }
 }
 
-// One workgroup of 256 threads per token row.  [Orin 从 FP 线性层到 INT4 DP4A 的数学推导],
+// One workgroup of kAqThreads threads per token row.  [Orin 从 FP 线性层到 INT4 DP4A 的数学推导],
 // [Infra 2.2 量化的基本概念]:  s = max|x|/127,  q = clamp(rint(x/s), -127, 127).
-__global__ void __launch_bounds__(256) act_quant_kernel(const uint16_t *__restrict__ x,
-                                                        int64_t K, int64_t ldx,
-                                                        int8_t *__restrict__ q, int64_t ldq,
-                                                        float *__restrict__ s_x,
-                                                        int32_t *__restrict__ q_sum) {
+// A thread owns the 8-column chunks tid, tid + kAqThreads, ...; the first kAqCache of them stay in
+// registers between the max pass and the quantization pass, so a row of up to
+// kAqThreads * kAqCache * 8 columns is read from memory once.  Loads are 16 bytes (ldx % 8 == 0
+// keeps every chunk that starts before K inside the row); columns >= K are masked.
+constexpr int kAqThreads = 1024;
+constexpr int kAqCache = 4;
+
+__device__ __forceinline__ float chunk_absmax(const uint4 &v, int64_t col, int64_t K) {
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+    float a = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t bits = (e & 1) ? (u[e >> 1] >> 16) : (u[e >> 1] & 0xFFFFu);
+        const float f = col + e < K ? fabsf(bf16_to_f32(bits)) : 0.0f;
+        a = fmaxf(a, f);
+    }
+    return a;
+}
+
+// Quantizes the chunk at `col` and stores the codes of its columns < K; returns their sum.
+__device__ __forceinline__ int chunk_quantize(const uint4 &v, int64_t col, int64_t K, float a,
+                                              float s, int8_t *__restrict__ qr) {
 #pragma clang fp contract(off)
-    __shared__ float red_f[256 / kWave];
-    __shared__ int red_i[256 / kWave];
+    const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+    int qi[8];
+    int sum = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const uint32_t bits = (e & 1) ? (u[e >> 1] >> 16) : (u[e >> 1] & 0xFFFFu);
+        float t = bf16_to_f32(bits) / s;  // one correctly rounded fp32 division
+        t = __builtin_rintf(t);
+        t = fmaxf(t, -127.0f);
+        t = fminf(t, 127.0f);
+        qi[e] = (a != 0.0f && col + e < K) ? static_cast<int>(t) : 0;
+        sum += qi[e];
+    }
+    if (col + 8 <= K) {
+        uint2 packed;
+        packed.x = (qi[0] & 0xFF) | ((qi[1] & 0xFF) << 8) | ((qi[2] & 0xFF) << 16) |
+                   (static_cast<uint32_t>(qi[3] & 0xFF) << 24);
+        packed.y = (qi[4] & 0xFF) | ((qi[5] & 0xFF) << 8) | ((qi[6] & 0xFF) << 16) |
+                   (static_cast<uint32_t>(qi[7] & 0xFF) << 24);
+        *reinterpret_cast<uint2 *>(qr + col) = packed;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if (col + e < K) qr[col + e] = static_cast<int8_t>(qi[e]);
+    }
+    return sum;
+}
+
+__global__ void __launch_bounds__(kAqThreads) act_quant_kernel(const uint16_t *__restrict__ x,
+                                                               int64_t K, int64_t ldx,
+                                                               int8_t *__restrict__ q, int64_t ldq,
+                                                               float *__restrict__ s_x,
+                                                               int32_t *__restrict__ q_sum) {
+#pragma clang fp contract(off)
+    constexpr int kWaves = kAqThreads / kWave;
+    __shared__ float red_f[kWaves];
+    __shared__ int red_i[kWaves];
     const int64_t m = blockIdx.x;
     const uint16_t *xr = x + m * ldx;
+    int8_t *qr = q + m * ldq;
     const int tid = threadIdx.x, wid = tid / kWave, lane = tid & (kWave - 1);
+    const int64_t n_chunks = (K + 7) / 8;
 
+    uint4 cache[kAqCache];
     float a = 0.0f;
-    for (int64_t k = tid; k < K; k += 256) a = fmaxf(a, fabsf(bf16_to_f32(xr[k])));
+#pragma unroll
+    for (int i = 0; i < kAqCache; ++i) {
+        const int64_t c = tid + static_cast<int64_t>(i) * kAqThreads;
+        cache[i] = c < n_chunks ? *reinterpret_cast<const uint4 *>(xr + 8 * c)
+                                : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < kAqCache; ++i) {
+        const int64_t c = tid + static_cast<int64_t>(i) * kAqThreads;
+        if (c < n_chunks) a = fmaxf(a, chunk_absmax(cache[i], 8 * c, K));
+    }
+    for (int64_t c = tid + static_cast<int64_t>(kAqCache) * kAqThreads; c < n_chunks;
+         c += kAqThreads)
+        a = fmaxf(a, chunk_absmax(*reinterpret_cast<const uint4 *>(xr + 8 * c), 8 * c, K));
     a = wave_max(a);
     if (lane == 0) red_f[wid] = a;
     __syncthreads();
-    a = fmaxf(fmaxf(red_f[0], red_f[1]), fmaxf(red_f[2], red_f[3]));
+    a = red_f[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) a = fmaxf(a, red_f[w]);
 
     const float s = a / 127.0f;
     int sum = 0;
-    int8_t *qr = q + m * ldq;
-    for (int64_t k = tid; k < K; k += 256) {
-        int qi = 0;
-        if (a != 0.0f) {
-            float v = bf16_to_f32(xr[k]) / s;
-            v = __builtin_rintf(v);
-            v = fmaxf(v, -127.0f);
-            v = fminf(v, 127.0f);
-            qi = static_cast<int>(v);
-        }
-        qr[k] = static_cast<int8_t>(qi);
-        sum += qi;
+#pragma unroll
+    for (int i = 0; i < kAqCache; ++i) {
+        const int64_t c = tid + static_cast<int64_t>(i) * kAqThreads;
+        if (c < n_chunks) sum += chunk_quantize(cache[i], 8 * c, K, a, s, qr);
     }
+    for (int64_t c = tid + static_cast<int64_t>(kAqCache) * kAqThreads; c < n_chunks;
+         c += kAqThreads)
+        sum += chunk_quantize(*reinterpret_cast<const uint4 *>(xr + 8 * c), 8 * c, K, a, s, qr);
     sum = wave_sum(sum);
     if (lane == 0) red_i[wid] = sum;
     __syncthreads();
     if (tid == 0) {
+        int total = 0;
+        for (int w = 0; w < kWaves; ++w) total += red_i[w];
         s_x[m] = s;
-        if (q_sum) q_sum[m] = red_i[0] + red_i[1] + red_i[2] + red_i[3];
+        if (q_sum) q_sum[m] = total;
     }
 }
 
@@ -153,8 +220,8 @@ hipError_t launch_pack(const float *w, int64_t d_out, int64_t d_in, int64_t ldw,
 
 hipError_t launch_act_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int8_t *q,
                             int64_t ldq, float *s_x, int32_t *q_sum, hipStream_t stream) {
-    hipLaunchKernelGGL(act_quant_kernel, dim3(static_cast<unsigned>(M)), dim3(256), 0, stream, x,
-                       K, ldx, q, ldq, s_x, q_sum);
+    hipLaunchKernelGGL(act_quant_kernel, dim3(static_cast<unsigned>(M)), dim3(kAqThreads), 0,
+                       stream, x, K, ldx, q, ldq, s_x, q_sum);
     return hipGetLastError();
 }
 
