@@ -260,11 +260,14 @@ __global__ void __launch_bounds__(kMaxWaves * kWave) gemv_mfma_kernel(
             load(p, ring[p]);
         }
         phase_fence();
+        // Slots past the wave's last chunk were loaded out of range (zeros): computing them adds
+        // exactly 0, and leaving the computation unconditional keeps the loop free of branches
+        // (after a skipped slot, the compiler would wait for its loads before reusing registers).
         int b = 0;
         do {
 #pragma unroll
             for (int p = 0; p < P; ++p) {
-                if (b + p < L) compute(ring[p]);
+                compute(ring[p]);
                 phase_fence();
                 load(b + p + P, ring[p]);
                 phase_fence();
