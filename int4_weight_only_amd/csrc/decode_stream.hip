@@ -152,22 +152,29 @@ __global__ void __launch_bounds__(kThreads) gemv_w4a16_stream_kernel(
     };
 
     // ---- activations: SI chunk loads per thread, issued before the weight batches so that
-    // waiting for them does not wait for the weights ----
+    // waiting for them does not wait for the weight loads. x rows are ldx apart with ldx % 8 == 0,
+    // so an 8-column piece that starts before d_in lies inside its row; a piece at or past d_in,
+    // and every piece of a thread past the last chunk, gets an out-of-range offset and reads as
+    // zeros. (The host keeps the tile's offsets below 2^31.) ----
     constexpr int SI = (MT * T + 3) / 4;  // >= ceil(MT * cpr / kThreads)
-    const int64_t n_chunks = (int64_t)MT * cpr;
+    const int n_chunks = MT * static_cast<int>(cpr);
+    const int cpr_i = static_cast<int>(cpr);
+    const int din = static_cast<int>(d_in);  // decode rows have d_in <= 65536
+    const rsrc_t rx = make_rsrc(x, 0x7FFFFFFFu);
     uint4 xraw[SI][4];
 #pragma unroll
     for (int si = 0; si < SI; ++si) {
-        int64_t idx = threadIdx.x + (int64_t)si * kThreads;
-        idx = idx < n_chunks ? idx : n_chunks - 1;
-        const int m = static_cast<int>(idx / cpr);
-        const int64_t c = idx - (int64_t)m * cpr;
+        const int idx = static_cast<int>(threadIdx.x) + si * kThreads;
+        const int m = MT == 1 ? 0 : idx / cpr_i;
+        const int c = idx - m * cpr_i;
         const int mx = m < M ? m : M - 1;  // tokens of the tile past M repeat token M - 1
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            const int64_t col = c * kChunkCols + 8 * p;
-            const bool ok = col < d_in;
-            xraw[si][p] = *reinterpret_cast<const uint4 *>(x + (ok ? (int64_t)mx * ldx + col : 0));
+            const int col = c * kChunkCols + 8 * p;
+            const uint32_t off = idx < n_chunks && col < din
+                                     ? static_cast<uint32_t>(((int64_t)mx * ldx + col) * 2)
+                                     : kOutOfRange;
+            xraw[si][p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
         }
     }
     Batch buf[NB];
@@ -181,30 +188,41 @@ __global__ void __launch_bounds__(kThreads) gemv_w4a16_stream_kernel(
     // ---- convert: each 32-column chunk is scaled by 2^-e with max|x 2^-e| in [2^14, 2^15):
     // bf16 values convert to fp16 exactly (8 of fp16's 11 significand bits) unless they are
     // below max * 2^-31 of their chunk ----
-    // (decode rows have d_in <= 65536, so column arithmetic fits 32 bits; selects, not branches:
-    // a branch here would make the waits for the activation loads cover the weight batches)
-    const int din = static_cast<int>(d_in);
+    // (a wave whose chunks all lie past the end skips the work: a wave-uniform branch that holds
+    // no load, so the waits for the activation loads still leave the weight loads in flight)
+    const bool ragged = (din & 7) != 0;  // the piece holding column d_in - 1 has columns past it
+    typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+    const half2_t ones = {static_cast<half_t>(1.0f), static_cast<half_t>(1.0f)};
 #pragma unroll
     for (int si = 0; si < SI; ++si) {
-        // clamped like the loads: threads past the end rewrite the last record with equal bits
-        int64_t idx = threadIdx.x + (int64_t)si * kThreads;
-        idx = idx < n_chunks ? idx : n_chunks - 1;
-        const int m = static_cast<int>(idx / cpr);
-        const int c = static_cast<int>(idx - (int64_t)m * cpr);
-        float v[32];
-        float amax = 0.0f;
+        if (si * kThreads + wid * kWave >= n_chunks) break;
+        const int idx = static_cast<int>(threadIdx.x) + si * kThreads;
+        const int m = MT == 1 ? 0 : idx / cpr_i;
+        const int c = idx - m * cpr_i;
+        uint32_t u[16];  // piece p, dword k: columns 8p + 2k (low half) and 8p + 2k + 1 (high)
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-            const int col = c * kChunkCols + 8 * p;
-            const uint32_t u[4] = {xraw[si][p].x, xraw[si][p].y, xraw[si][p].z, xraw[si][p].w};
+            u[4 * p + 0] = xraw[si][p].x;
+            u[4 * p + 1] = xraw[si][p].y;
+            u[4 * p + 2] = xraw[si][p].z;
+            u[4 * p + 3] = xraw[si][p].w;
+        }
+        if (__builtin_expect(ragged, 0)) {  // zero the columns at or past d_in
+            // (kept a real branch: if-converted, the masks would cost every shape 64 VALU ops)
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t bits = (e & 1) ? (u[e >> 1] & 0xFFFF0000u) : (u[e >> 1] << 16);
-                v[8 * p + e] = col + e < din ? __uint_as_float(bits) : 0.0f;  // zero past d_in
+            for (int k = 0; k < 16; ++k) {
+                const int col = c * kChunkCols + 2 * k;
+                u[k] &= col + 1 < din ? 0xFFFFFFFFu : (col < din ? 0x0000FFFFu : 0u);
             }
         }
+        // the largest magnitude, compared on the bf16 bit patterns (monotone in |x|)
+        u16x2_t am = {0, 0};
 #pragma unroll
-        for (int i = 0; i < 32; i += 2) amax = fmaxf(amax, fmaxf(fabsf(v[i]), fabsf(v[i + 1])));
+        for (int k = 0; k < 16; ++k)
+            am = __builtin_elementwise_max(am, __builtin_bit_cast(u16x2_t, u[k] & 0x7FFF7FFFu));
+        const uint32_t amax_bits = am.x > am.y ? am.x : am.y;
+        const float amax = __uint_as_float(amax_bits << 16);
         const int e = amax > 0.0f ? ilogbf(amax) - 14 : 0;
         XChunk16 rec;
         float sum = 0.0f;
@@ -212,17 +230,20 @@ __global__ void __launch_bounds__(kThreads) gemv_w4a16_stream_kernel(
         for (int j = 0; j < 4; ++j) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
+                const uint32_t a = u[4 * j + (i >> 1)], b = u[4 * j + 2 + (i >> 1)];
+                const float xa = __uint_as_float((i & 1) ? (a & 0xFFFF0000u) : (a << 16));
+                const float xb = __uint_as_float((i & 1) ? (b & 0xFFFF0000u) : (b << 16));
                 half2_t h;
-                h.x = static_cast<half_t>(ldexpf(v[8 * j + i], -e));  // exact (v_ldexp)
-                h.y = static_cast<half_t>(ldexpf(v[8 * j + i + 4], -e));
+                h.x = static_cast<half_t>(ldexpf(xa, -e));  // column 8j + i, exact (v_ldexp)
+                h.y = static_cast<half_t>(ldexpf(xb, -e));  // column 8j + i + 4
                 rec.h[4 * j + i] = as_u32(h);
-                if (ZP) sum += static_cast<float>(h.x) + static_cast<float>(h.y);
+                if (ZP) sum = __builtin_amdgcn_fdot2(h, ones, sum, false);
             }
         }
         rec.e = e;
         rec.sum = sum;
         rec.pad[0] = rec.pad[1] = 0;
-        xsh[(int64_t)m * (cpr + 1) + c] = rec;
+        if (idx < n_chunks) xsh[m * (cpr_i + 1) + c] = rec;
     }
     if (threadIdx.x < MT) {
         XChunk16 zero;
@@ -763,7 +784,9 @@ hipError_t launch_gemv_stream(const uint16_t *x, int64_t M, int64_t ldx, const u
                               int64_t n_groups, void *y, int64_t ldy, bool out_f32,
                               hipStream_t stream) {
     const int T = pick_steps(k_pad / kChunkCols);
-    const int tile = stream_token_tile(M, T);
+    int tile = stream_token_tile(M, T);
+    // the kernel addresses a tile's activations with 31-bit byte offsets; one token always fits
+    if (((int64_t)(tile - 1) * ldx + k_pad) * 2 >= (int64_t)kOutOfRange) tile = 1;
     const size_t out_elem = out_f32 ? sizeof(float) : sizeof(uint16_t);
     const bool zp = zeros != nullptr;
     for (int64_t m0 = 0; m0 < M; m0 += tile) {
