@@ -535,6 +535,11 @@ hipError_t launch_gemv(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t 
                        int64_t d_out, int64_t d_in, int64_t k_pad, int64_t span,
                        int64_t n_groups, void *y, int64_t ldy, bool out_f32, void *workspace,
                        hipStream_t stream) {
+    // Group-aligned shapes: the int8 matrix cores, with the codes as an operand as they are.
+    if (gemv_i8_preferred(M, d_out, k_pad) &&
+        gemv_i8_supported(M, d_out, d_in, k_pad, span, n_groups, ldx))
+        return launch_gemv_i8(x, M, ldx, qweight, scales, zeros, bias, d_out, d_in, k_pad, span,
+                              n_groups, y, ldy, out_f32, stream);
     // Two or more tokens: the matrix-core path reads the weights once for all of them.
     if (gemv_mfma_supported(M, d_out, k_pad, span, n_groups))
         return launch_gemv_mfma(x, M, ldx, qweight, scales, zeros, bias, d_out, d_in, k_pad, span,

@@ -57,6 +57,17 @@ hipError_t launch_gemv_mfma(const uint16_t *x, int64_t M, int64_t ldx, const uin
                             int64_t n_groups, void *y, int64_t ldy, bool out_f32, void *workspace,
                             hipStream_t stream);
 
+// One to four tokens on the int8 matrix cores (decode_i8.hip): activations as exact integer
+// digits prepared inside each block, raw codes as the other operand; no workspace.
+bool gemv_i8_supported(int64_t M, int64_t d_out, int64_t d_in, int64_t k_pad, int64_t span,
+                       int64_t n_groups, int64_t ldx);
+bool gemv_i8_preferred(int64_t M, int64_t d_out, int64_t k_pad);
+hipError_t launch_gemv_i8(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
+                          const uint16_t *scales, const uint16_t *zeros, const uint16_t *bias,
+                          int64_t d_out, int64_t d_in, int64_t k_pad, int64_t span,
+                          int64_t n_groups, void *y, int64_t ldy, bool out_f32,
+                          hipStream_t stream);
+
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 

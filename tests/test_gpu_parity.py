@@ -320,6 +320,51 @@ def test_linear_deterministic(entry):
 
 
 # ------------------------------------------------------------------------------------------
+# the int8 matrix-core decode kernel, forced onto every shape it supports (by default it serves
+# one token on wide matrices only)
+# ------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("g", [128, 256, 0])
+@pytest.mark.parametrize("mode", [SYM, ASYM])
+def test_gemv_int8_kernel_ragged(monkeypatch, g, mode):
+    """One to four tokens, ragged d_out and d_in (NaN past d_in in x), bias, strided x and y."""
+    monkeypatch.setenv("W4_GEMV_PATH", "i8")
+    shapes = [(1, 1, 100), (3, 130, 100), (4, 257, 1000), (2, 200, 3600), (1, 700, 4100),
+              (1, 33, 18944)]
+    for M, d_out, d_in in shapes:
+        w = workloads.weight(29, M + d_out + d_in + g, d_out, d_in)
+        ph, pd = check_pack_bit_exact(w, g, mode, "int8 kernel")
+        x = workloads.activations(29, g + mode, M, d_in)
+        b = workloads.bias(29, 1, d_out)
+        ldx = (d_in + 7) // 8 * 8 + 16
+        check_linear("w4_gemv", x, ph, pd, b, d_in, g, f"int8 kernel M={M} {d_out}x{d_in}",
+                     ldx=ldx, ldy=d_out + 5)
+
+
+def test_gemv_int8_kernel_junk_pads_and_determinism(monkeypatch):
+    """Pad columns of the d_in = 3600 layer run as real columns holding 1e3 must add exact
+    zeros; repeated calls are bit-identical."""
+    monkeypatch.setenv("W4_GEMV_PATH", "i8")
+    cfg = workloads.C3
+    lin = cfg.extra[0]
+    w = workloads.linear_weight(cfg, 4, lin=lin)
+    ph, pd = check_pack_bit_exact(w, lin.group_size, lin.mode, "int8 kernel pad3600")
+    k_pad = oracle.k_pad(lin.d_in, lin.group_size)
+    for M in (1, 4):
+        x = workloads.linear_x(cfg, 4, M, lin=lin)
+        xj = np.zeros((M, k_pad), dtype=np.uint16)
+        xj[:, :lin.d_in] = x
+        xj[:, lin.d_in:] = workloads.to_bf16_bits(np.array([1000.0], np.float32))[0]
+        _announce("int8 kernel junk pads", M)
+        xd = dev_bf16(xj)
+        y = host(w4.w4_gemv(xd, *pd, None, k_pad, lin.group_size, F32))
+        y_ref = oracle.w4a16(x, ph[0], ph[1], ph[2], None, lin.d_in, lin.group_size)
+        assert_close(y, y_ref, f"int8 kernel junk pads M={M}")
+        for _ in range(2):
+            again = host(w4.w4_gemv(xd, *pd, None, k_pad, lin.group_size, F32))
+            assert np.array_equal(y.view(np.uint32), again.view(np.uint32))
+
+
+# ------------------------------------------------------------------------------------------
 # w4a8_gemv
 # ------------------------------------------------------------------------------------------
 def check_w4a8(w, x_bits, bias_bits, what):
