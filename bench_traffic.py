@@ -25,9 +25,7 @@ sys.path.insert(0, ROOT)
 
 COPY_BYTES = 256 << 20
 CALIB_COPIES = 4
-GEMV_KERNEL = "gemv_w4a16_stream_kernel"
-KERNEL_SOURCES = ("int4_weight_only_amd/csrc/decode_stream.hip",
-                  "int4_weight_only_amd/csrc/w4_device.h")
+GEMV_KERNEL = "gemv_i8_kernel"
 
 
 def run():
@@ -80,7 +78,7 @@ def per_kernel_mean(path, counter):
 
 
 def summarize(fetch_csv, write_csv):
-    from bench import linear_bytes, source_hash
+    from bench import TRAFFIC_SOURCES, linear_bytes, source_hash
     import workloads
 
     f = per_kernel_mean(fetch_csv, "FETCH_SIZE")
@@ -97,7 +95,7 @@ def summarize(fetch_csv, write_csv):
     algo = linear_bytes(1, gu.d_out, gu.d_in, gu.group_size, False)
     entry = {
         "kernel": f"{GEMV_KERNEL} (C2 gate/up 37888x3584, M=1, bf16 out)",
-        "source_hash": source_hash(*KERNEL_SOURCES),
+        "source_hash": source_hash(*TRAFFIC_SOURCES),
         "bytes_per_launch": round(read_b + write_b),
         "read_bytes_per_launch": round(read_b),
         "write_bytes_per_launch": round(write_b),
