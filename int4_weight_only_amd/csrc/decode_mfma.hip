@@ -25,7 +25,9 @@
 //
 // Weight loads are raw buffer loads through a descriptor covering exactly the block's rows, so a
 // row past the block or a chunk past the row reads zeros without touching memory; every load is
-// unconditional and sits in a ring of P chunks in flight per wave.
+// unconditional and sits in a ring of P chunks in flight per wave. They use the default cache
+// policy: a load covers one 64-byte half of 16 rows' lines and the same wave reads the other
+// half next, which the streaming (non-temporal) hint made about 10% slower.
 #include "w4_device.h"
 #include "w4_launch.h"
 
@@ -203,7 +205,7 @@ __global__ void __launch_bounds__(kMaxWaves * kWave) gemv_mfma_kernel(
                 const uint32_t row = 16u * i + n;
                 const uint4 v = __builtin_bit_cast(
                     uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                               rq, kok ? row * row_bytes + kb : kOutOfRange, 0, kNonTemporal));
+                               rq, kok ? row * row_bytes + kb : kOutOfRange, 0, 0));
                 S.w[i][0] = v.x; S.w[i][1] = v.y; S.w[i][2] = v.z; S.w[i][3] = v.w;
                 const uint32_t go = ok ? (row * n_groups + G) * 2u : kOutOfRange;
                 S.s[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, go, 0, 0);
