@@ -89,7 +89,11 @@ struct Rows {
 // W4A16
 // ---------------------------------------------------------------------------------------------
 
-template <int MT, int T, int RW, int NB, bool ZP>
+// Long rows are cut into SEG segments of T steps: batch b of a wave is segment b % SEG of its
+// row group b / SEG (NB is a multiple of SEG, so ring slot i always holds segment i % SEG), and
+// the row's sums are carried from one segment to the next. A segment's loads take fewer
+// registers than a whole row's, so more waves fit on a CU.
+template <int MT, int T, int RW, int NB, bool ZP, int SEG>
 __global__ void __launch_bounds__(kThreads) gemv_w4a16_stream_kernel(
     const uint16_t *__restrict__ x, int64_t ldx, int M, const uint8_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
@@ -106,15 +110,19 @@ __global__ void __launch_bounds__(kThreads) gemv_w4a16_stream_kernel(
     // lane's chunk of step t: byte offsets of its codes in a row and of its group's scale (out of
     // range past the row end), and its activation record (the token's zero record cpr past the
     // row end, so a chunk of zero codes adds nothing)
-    uint32_t wofs[T], gofs[T];
-    int xofs[T];
+    static_assert(NB % SEG == 0, "ring slots hold fixed segments");
+    uint32_t wofs[SEG][T], gofs[SEG][T];
+    int xofs[SEG][T];
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-        const int64_t c = (int64_t)t * kWave + lane;
-        wofs[t] = c < cpr ? static_cast<uint32_t>(c * 16) : kOutOfRange;
-        gofs[t] = c < cpr ? static_cast<uint32_t>((c >> chunk_group_shift) * 2) : kOutOfRange;
-        xofs[t] = static_cast<int>(c < cpr ? c : cpr);
-    }
+    for (int sg = 0; sg < SEG; ++sg)
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const int64_t c = (int64_t)(sg * T + t) * kWave + lane;
+            wofs[sg][t] = c < cpr ? static_cast<uint32_t>(c * 16) : kOutOfRange;
+            gofs[sg][t] =
+                c < cpr ? static_cast<uint32_t>((c >> chunk_group_shift) * 2) : kOutOfRange;
+            xofs[sg][t] = static_cast<int>(c < cpr ? c : cpr);
+        }
 
     // Everything a batch needs, including the per-row bias of the epilogue (16-bit values have
     // no scalar load, and a load issued later would wait behind the prefetch). The loaded values
@@ -128,7 +136,7 @@ __global__ void __launch_bounds__(kThreads) gemv_w4a16_stream_kernel(
     };
     const uint32_t rb = static_cast<uint32_t>(row_bytes);
     const uint32_t gb = static_cast<uint32_t>(n_groups * 2);
-    auto load_batch = [&](int b, Batch &dst) {
+    auto load_batch = [&](int b, int sg, Batch &dst) {  // row group b, segment sg
         const int row0 = R.row0(b);
         const int valid = R.valid(row0);
         const int64_t r0 = valid > 0 ? row0 : 0;
@@ -141,12 +149,13 @@ __global__ void __launch_bounds__(kThreads) gemv_w4a16_stream_kernel(
             dst.bs[r] = __builtin_amdgcn_raw_buffer_load_b16(rbias, 2 * r, 0, 0);
 #pragma unroll
             for (int t = 0; t < T; ++t) {
-                dst.w[r][t] =
-                    __builtin_amdgcn_raw_buffer_load_b128(rw, wofs[t] + r * rb, 0, kNonTemporal);
-                dst.sc[r][t] = __builtin_amdgcn_raw_buffer_load_b16(rs, gofs[t] + r * gb, 0, 0);
+                dst.w[r][t] = __builtin_amdgcn_raw_buffer_load_b128(rw, wofs[sg][t] + r * rb, 0,
+                                                                    kNonTemporal);
+                dst.sc[r][t] =
+                    __builtin_amdgcn_raw_buffer_load_b16(rs, gofs[sg][t] + r * gb, 0, 0);
                 if (ZP)
                     dst.zr[ZP ? r : 0][ZP ? t : 0] =
-                        __builtin_amdgcn_raw_buffer_load_b16(rz, gofs[t] + r * gb, 0, 0);
+                        __builtin_amdgcn_raw_buffer_load_b16(rz, gofs[sg][t] + r * gb, 0, 0);
             }
         }
     };
@@ -156,7 +165,7 @@ __global__ void __launch_bounds__(kThreads) gemv_w4a16_stream_kernel(
     // so an 8-column piece that starts before d_in lies inside its row; a piece at or past d_in,
     // and every piece of a thread past the last chunk, gets an out-of-range offset and reads as
     // zeros. (The host keeps the tile's offsets below 2^31.) ----
-    constexpr int SI = (MT * T + 3) / 4;  // >= ceil(MT * cpr / kThreads)
+    constexpr int SI = (MT * T * SEG + 3) / 4;  // >= ceil(MT * cpr / kThreads)
     const int n_chunks = MT * static_cast<int>(cpr);
     const int cpr_i = static_cast<int>(cpr);
     const int din = static_cast<int>(d_in);  // decode rows have d_in <= 65536
@@ -181,7 +190,7 @@ __global__ void __launch_bounds__(kThreads) gemv_w4a16_stream_kernel(
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
         phase_fence();
-        load_batch(i, buf[i]);
+        load_batch(i / SEG, i % SEG, buf[i]);
     }
     phase_fence();
 
@@ -267,12 +276,13 @@ __global__ void __launch_bounds__(kThreads) gemv_w4a16_stream_kernel(
     struct Out {
         float v[RW][MT];
     };
-    auto compute_batch = [&](const Batch &bt, Out &out) {
+    float carry[RW][MT];  // a row's sums from its earlier segments
+    auto compute_batch = [&](const Batch &bt, Out &out, int sg) {
         float acc[RW][MT];
 #pragma unroll
         for (int r = 0; r < RW; ++r)
 #pragma unroll
-            for (int m = 0; m < MT; ++m) acc[r][m] = 0.0f;
+            for (int m = 0; m < MT; ++m) acc[r][m] = sg == 0 ? 0.0f : carry[r][m];
 #pragma unroll
         for (int t = 0; t < T; ++t) {
             half2_t xf[MT][16];
@@ -280,7 +290,7 @@ __global__ void __launch_bounds__(kThreads) gemv_w4a16_stream_kernel(
             float xs[MT];
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
-                const XChunk16 &rec = xsh[(int64_t)m * (cpr + 1) + xofs[t]];
+                const XChunk16 &rec = xsh[(int64_t)m * (cpr + 1) + xofs[sg][t]];
 #pragma unroll
                 for (int i = 0; i < 16; ++i) xf[m][i] = as_half2(rec.h[i]);
                 xe[m] = rec.e;
@@ -336,6 +346,13 @@ __global__ void __launch_bounds__(kThreads) gemv_w4a16_stream_kernel(
                 }
             }
         }
+        if (sg < SEG - 1) {
+#pragma unroll
+            for (int r = 0; r < RW; ++r)
+#pragma unroll
+                for (int m = 0; m < MT; ++m) carry[r][m] = acc[r][m];
+            return;
+        }
 #pragma unroll
         for (int r = 0; r < RW; ++r) {
 #pragma unroll
@@ -377,16 +394,18 @@ __global__ void __launch_bounds__(kThreads) gemv_w4a16_stream_kernel(
     // has no exit between a prefetch and its use (a prefetch that is dead on some path would be
     // sunk past the fences). Batches past the wave's last row group are loaded (zeros, no
     // memory traffic) but not computed.
+    // (b counts segments; the row group of batch b is b / SEG)
     Out out;
+    const int b_last = (R.b_last + 1) * SEG - 1;
     int b = 0;
     do {
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
-            if (b + i <= R.b_last) compute_batch(buf[i], out);
+            if (b + i <= b_last) compute_batch(buf[i], out, i % SEG);
             phase_fence();
-            load_batch(b + i + NB, buf[i]);
+            load_batch((b + i + NB) / SEG, i % SEG, buf[i]);
             phase_fence();
-            if (b + i <= R.b_last) store_batch(b + i, out);
+            if (i % SEG == SEG - 1 && b + i <= b_last) store_batch((b + i) / SEG, out);
         }
         b += NB;
     } while (b < n_batches);
@@ -640,7 +659,7 @@ int pick_steps(int64_t cpr) {
 
 // Workgroups per CU of the persistent grid (measured defaults; W4_STREAM_BLOCKS_PER_CU, read once,
 // overrides them for tuning on other parts).
-int stream_blocks_per_cu(int T) {
+int stream_blocks_per_cu(int T, int seg) {
     static const int forced = [] {
         const char *e = getenv("W4_STREAM_BLOCKS_PER_CU");
         return e ? atoi(e) : 0;
@@ -654,14 +673,16 @@ struct StreamPlan {
     int n_batches;
 };
 
-StreamPlan plan_stream(int64_t d_out, int T, int RW, int NB) {
+// T: steps per row; SEG: segments per row (n_batches counts segments)
+StreamPlan plan_stream(int64_t d_out, int T, int RW, int NB, int SEG = 1) {
     StreamPlan p{};
     const int64_t rows_per_round_per_block = (int64_t)kWaves * RW;
-    int64_t blocks = (int64_t)device_cu_count() * stream_blocks_per_cu(T);
+    int64_t blocks = (int64_t)device_cu_count() * stream_blocks_per_cu(T, SEG);
     const int64_t need = (d_out + rows_per_round_per_block - 1) / rows_per_round_per_block;
     if (blocks > need) blocks = need;
     p.grid = static_cast<int>(blocks);
     int64_t nb = (d_out + blocks * rows_per_round_per_block - 1) / (blocks * rows_per_round_per_block);
+    nb *= SEG;
     nb = (nb + NB - 1) / NB * NB;  // the kernels' ring takes batches NB at a time
     p.n_batches = static_cast<int>(nb);
     return p;
@@ -674,18 +695,21 @@ hipError_t launch_w4a16_stream_t(bool zp, const uint16_t *x, int64_t ldx, int M,
                                  int64_t d_in, int64_t k_pad, int shift, int64_t n_groups,
                                  void *y, int64_t ldy, bool out_f32, hipStream_t stream) {
     constexpr Shape S = stream_shape(T);
-    const StreamPlan p = plan_stream(d_out, T, S.rw, S.nb);
+    // one token on rows of 8 or more steps: two segments per row (see the kernel)
+    constexpr int SEG = MT == 1 && T >= 8 ? 2 : 1;
+    static_assert(T % SEG == 0 && S.nb % SEG == 0, "segments");
+    const StreamPlan p = plan_stream(d_out, T, S.rw, S.nb, SEG);
     const size_t lds = sizeof(XChunk16) * (size_t)MT * (size_t)(k_pad / kChunkCols + 1);
     if (zp)
-        hipLaunchKernelGGL((gemv_w4a16_stream_kernel<MT, T, S.rw, S.nb, true>), dim3(p.grid),
-                           dim3(kThreads), lds, stream, x, ldx, M, qweight, scales, zeros, bias,
-                           d_out, d_in, k_pad, shift, n_groups, y, ldy, out_f32 ? 1 : 0,
-                           p.n_batches);
+        hipLaunchKernelGGL((gemv_w4a16_stream_kernel<MT, T / SEG, S.rw, S.nb, true, SEG>),
+                           dim3(p.grid), dim3(kThreads), lds, stream, x, ldx, M, qweight, scales,
+                           zeros, bias, d_out, d_in, k_pad, shift, n_groups, y, ldy,
+                           out_f32 ? 1 : 0, p.n_batches);
     else
-        hipLaunchKernelGGL((gemv_w4a16_stream_kernel<MT, T, S.rw, S.nb, false>), dim3(p.grid),
-                           dim3(kThreads), lds, stream, x, ldx, M, qweight, scales, zeros, bias,
-                           d_out, d_in, k_pad, shift, n_groups, y, ldy, out_f32 ? 1 : 0,
-                           p.n_batches);
+        hipLaunchKernelGGL((gemv_w4a16_stream_kernel<MT, T / SEG, S.rw, S.nb, false, SEG>),
+                           dim3(p.grid), dim3(kThreads), lds, stream, x, ldx, M, qweight, scales,
+                           zeros, bias, d_out, d_in, k_pad, shift, n_groups, y, ldy,
+                           out_f32 ? 1 : 0, p.n_batches);
     return hipGetLastError();
 }
 
