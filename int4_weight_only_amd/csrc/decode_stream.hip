@@ -71,9 +71,9 @@ constexpr Shape stream_shape(int /*T*/) { return Shape{1, 2}; }
 template <int RW>
 struct Rows {
     int wave_id, total_waves, rows, b_last;
-    __device__ __forceinline__ Rows(int wid, int64_t d_out) {
-        wave_id = static_cast<int>(blockIdx.x) * kWaves + wid;
-        total_waves = static_cast<int>(gridDim.x) * kWaves;
+    __device__ __forceinline__ Rows(int wid, int64_t d_out, int waves_per_block) {
+        wave_id = static_cast<int>(blockIdx.x) * waves_per_block + wid;
+        total_waves = static_cast<int>(gridDim.x) * waves_per_block;
         rows = static_cast<int>(d_out);
         const int groups = (rows + RW - 1) / RW;
         b_last = wave_id < groups ? (groups - 1 - wave_id) / total_waves : -1;
@@ -92,9 +92,9 @@ struct Rows {
 // Long rows are cut into SEG segments of T steps: batch b of a wave is segment b % SEG of its
 // row group b / SEG (NB is a multiple of SEG, so ring slot i always holds segment i % SEG), and
 // the row's sums are carried from one segment to the next. A segment's loads take fewer
-// registers than a whole row's, so more waves fit on a CU.
-template <int MT, int T, int RW, int NB, bool ZP, int SEG>
-__global__ void __launch_bounds__(kThreads) gemv_w4a16_stream_kernel(
+// registers than a whole row's, so more waves fit on a CU. BT threads per workgroup.
+template <int MT, int T, int RW, int NB, bool ZP, int SEG, int BT>
+__global__ void __launch_bounds__(BT) gemv_w4a16_stream_kernel(
     const uint16_t *__restrict__ x, int64_t ldx, int M, const uint8_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
     const uint16_t *__restrict__ bias, int64_t d_out, int64_t d_in, int64_t k_pad,
@@ -105,7 +105,7 @@ __global__ void __launch_bounds__(kThreads) gemv_w4a16_stream_kernel(
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t cpr = k_pad / kChunkCols;
     const int64_t row_bytes = k_pad / 2;
-    const Rows<RW> R(wid, d_out);
+    const Rows<RW> R(wid, d_out, BT / kWave);
 
     // lane's chunk of step t: byte offsets of its codes in a row and of its group's scale (out of
     // range past the row end), and its activation record (the token's zero record cpr past the
@@ -165,7 +165,7 @@ __global__ void __launch_bounds__(kThreads) gemv_w4a16_stream_kernel(
     // so an 8-column piece that starts before d_in lies inside its row; a piece at or past d_in,
     // and every piece of a thread past the last chunk, gets an out-of-range offset and reads as
     // zeros. (The host keeps the tile's offsets below 2^31.) ----
-    constexpr int SI = (MT * T * SEG + 3) / 4;  // >= ceil(MT * cpr / kThreads)
+    constexpr int SI = (MT * T * SEG * kWave + BT - 1) / BT;  // >= ceil(MT * cpr / BT)
     const int n_chunks = MT * static_cast<int>(cpr);
     const int cpr_i = static_cast<int>(cpr);
     const int din = static_cast<int>(d_in);  // decode rows have d_in <= 65536
@@ -173,7 +173,7 @@ __global__ void __launch_bounds__(kThreads) gemv_w4a16_stream_kernel(
     uint4 xraw[SI][4];
 #pragma unroll
     for (int si = 0; si < SI; ++si) {
-        const int idx = static_cast<int>(threadIdx.x) + si * kThreads;
+        const int idx = static_cast<int>(threadIdx.x) + si * BT;
         const int m = MT == 1 ? 0 : idx / cpr_i;
         const int c = idx - m * cpr_i;
         const int mx = m < M ? m : M - 1;  // tokens of the tile past M repeat token M - 1
@@ -204,8 +204,8 @@ __global__ void __launch_bounds__(kThreads) gemv_w4a16_stream_kernel(
     const half2_t ones = {static_cast<half_t>(1.0f), static_cast<half_t>(1.0f)};
 #pragma unroll
     for (int si = 0; si < SI; ++si) {
-        if (si * kThreads + wid * kWave >= n_chunks) break;
-        const int idx = static_cast<int>(threadIdx.x) + si * kThreads;
+        if (si * BT + wid * kWave >= n_chunks) break;
+        const int idx = static_cast<int>(threadIdx.x) + si * BT;
         const int m = MT == 1 ? 0 : idx / cpr_i;
         const int c = idx - m * cpr_i;
         uint32_t u[16];  // piece p, dword k: columns 8p + 2k (low half) and 8p + 2k + 1 (high)
@@ -427,7 +427,7 @@ __global__ void __launch_bounds__(kThreads) gemv_w4a8_stream_kernel(
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t cpr = k_pad / kChunkCols;
     const int64_t row_bytes = k_pad / 2;
-    const Rows<RW> R(wid, d_out);
+    const Rows<RW> R(wid, d_out, kWaves);
 
     uint32_t wofs[T];  // see the W4A16 kernel
     int xofs[T];
@@ -665,7 +665,7 @@ int stream_blocks_per_cu(int T, int seg) {
         return e ? atoi(e) : 0;
     }();
     if (forced > 0) return forced;
-    return T <= 2 ? 4 : 2;
+    return T <= 2 ? 4 : seg > 1 ? 1 : 2;
 }
 
 struct StreamPlan {
@@ -674,9 +674,9 @@ struct StreamPlan {
 };
 
 // T: steps per row; SEG: segments per row (n_batches counts segments)
-StreamPlan plan_stream(int64_t d_out, int T, int RW, int NB, int SEG = 1) {
+StreamPlan plan_stream(int64_t d_out, int T, int RW, int NB, int SEG = 1, int waves = kWaves) {
     StreamPlan p{};
-    const int64_t rows_per_round_per_block = (int64_t)kWaves * RW;
+    const int64_t rows_per_round_per_block = (int64_t)waves * RW;
     int64_t blocks = (int64_t)device_cu_count() * stream_blocks_per_cu(T, SEG);
     const int64_t need = (d_out + rows_per_round_per_block - 1) / rows_per_round_per_block;
     if (blocks > need) blocks = need;
@@ -698,16 +698,19 @@ hipError_t launch_w4a16_stream_t(bool zp, const uint16_t *x, int64_t ldx, int M,
     // one token on rows of 8 or more steps: two segments per row (see the kernel)
     constexpr int SEG = MT == 1 && T >= 8 ? 2 : 1;
     static_assert(T % SEG == 0 && S.nb % SEG == 0, "segments");
-    const StreamPlan p = plan_stream(d_out, T, S.rw, S.nb, SEG);
+    // segmented long rows: 8-wave workgroups, so that the activations are converted once per
+    // 8 waves instead of once per 4
+    constexpr int BT = SEG > 1 ? 2 * kThreads : kThreads;
+    const StreamPlan p = plan_stream(d_out, T, S.rw, S.nb, SEG, BT / kWave);
     const size_t lds = sizeof(XChunk16) * (size_t)MT * (size_t)(k_pad / kChunkCols + 1);
     if (zp)
-        hipLaunchKernelGGL((gemv_w4a16_stream_kernel<MT, T / SEG, S.rw, S.nb, true, SEG>),
-                           dim3(p.grid), dim3(kThreads), lds, stream, x, ldx, M, qweight, scales,
+        hipLaunchKernelGGL((gemv_w4a16_stream_kernel<MT, T / SEG, S.rw, S.nb, true, SEG, BT>),
+                           dim3(p.grid), dim3(BT), lds, stream, x, ldx, M, qweight, scales,
                            zeros, bias, d_out, d_in, k_pad, shift, n_groups, y, ldy,
                            out_f32 ? 1 : 0, p.n_batches);
     else
-        hipLaunchKernelGGL((gemv_w4a16_stream_kernel<MT, T / SEG, S.rw, S.nb, false, SEG>),
-                           dim3(p.grid), dim3(kThreads), lds, stream, x, ldx, M, qweight, scales,
+        hipLaunchKernelGGL((gemv_w4a16_stream_kernel<MT, T / SEG, S.rw, S.nb, false, SEG, BT>),
+                           dim3(p.grid), dim3(BT), lds, stream, x, ldx, M, qweight, scales,
                            zeros, bias, d_out, d_in, k_pad, shift, n_groups, y, ldy,
                            out_f32 ? 1 : 0, p.n_batches);
     return hipGetLastError();
