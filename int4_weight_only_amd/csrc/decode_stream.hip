@@ -659,13 +659,15 @@ int pick_steps(int64_t cpr) {
 
 // Workgroups per CU of the persistent grid (measured defaults; W4_STREAM_BLOCKS_PER_CU, read once,
 // overrides them for tuning on other parts).
-int stream_blocks_per_cu(int T, int seg) {
+int stream_blocks_per_cu(int T, int seg, int64_t d_out) {
     static const int forced = [] {
         const char *e = getenv("W4_STREAM_BLOCKS_PER_CU");
         return e ? atoi(e) : 0;
     }();
     if (forced > 0) return forced;
-    return T <= 2 ? 4 : seg > 1 ? 1 : 2;
+    if (seg > 1) return 1;
+    if (T > 2) return 2;
+    return d_out >= 32 * (int64_t)device_cu_count() ? 4 : 3;  // fewer rows: fewer workgroups
 }
 
 struct StreamPlan {
@@ -677,7 +679,7 @@ struct StreamPlan {
 StreamPlan plan_stream(int64_t d_out, int T, int RW, int NB, int SEG = 1, int waves = kWaves) {
     StreamPlan p{};
     const int64_t rows_per_round_per_block = (int64_t)waves * RW;
-    int64_t blocks = (int64_t)device_cu_count() * stream_blocks_per_cu(T, SEG);
+    int64_t blocks = (int64_t)device_cu_count() * stream_blocks_per_cu(T, SEG, d_out);
     const int64_t need = (d_out + rows_per_round_per_block - 1) / rows_per_round_per_block;
     if (blocks > need) blocks = need;
     p.grid = static_cast<int>(blocks);
