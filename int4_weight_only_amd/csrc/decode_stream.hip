@@ -415,8 +415,9 @@ __global__ void __launch_bounds__(BT) gemv_w4a16_stream_kernel(
 // W4A8
 // ---------------------------------------------------------------------------------------------
 
-template <int MT, int T, int RW, int NB>
-__global__ void __launch_bounds__(kThreads) gemv_w4a8_stream_kernel(
+// (segments of long rows and BT threads per workgroup: see the W4A16 kernel)
+template <int MT, int T, int RW, int NB, int SEG, int BT>
+__global__ void __launch_bounds__(BT) gemv_w4a8_stream_kernel(
     const int8_t *__restrict__ q, int64_t ldq, int M, const float *__restrict__ s_x,
     const uint8_t *__restrict__ qweight, const uint16_t *__restrict__ s_w,
     const uint16_t *__restrict__ bias, int64_t d_out, int64_t d_in, int64_t k_pad,
@@ -427,16 +428,19 @@ __global__ void __launch_bounds__(kThreads) gemv_w4a8_stream_kernel(
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t cpr = k_pad / kChunkCols;
     const int64_t row_bytes = k_pad / 2;
-    const Rows<RW> R(wid, d_out, kWaves);
+    const Rows<RW> R(wid, d_out, BT / kWave);
 
-    uint32_t wofs[T];  // see the W4A16 kernel
-    int xofs[T];
+    static_assert(NB % SEG == 0, "ring slots hold fixed segments");
+    uint32_t wofs[SEG][T];  // see the W4A16 kernel
+    int xofs[SEG][T];
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-        const int64_t c = (int64_t)t * kWave + lane;
-        wofs[t] = c < cpr ? static_cast<uint32_t>(c * 16) : kOutOfRange;
-        xofs[t] = static_cast<int>(c < cpr ? c : cpr);
-    }
+    for (int sg = 0; sg < SEG; ++sg)
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const int64_t c = (int64_t)(sg * T + t) * kWave + lane;
+            wofs[sg][t] = c < cpr ? static_cast<uint32_t>(c * 16) : kOutOfRange;
+            xofs[sg][t] = static_cast<int>(c < cpr ? c : cpr);
+        }
     // per-row s_w and bias travel with the batch (see the W4A16 kernel)
     struct Batch {
         u32x4_t w[RW][T];
@@ -444,7 +448,7 @@ __global__ void __launch_bounds__(kThreads) gemv_w4a8_stream_kernel(
         uint32_t bs[RW];
     };
     const uint32_t rb = static_cast<uint32_t>(row_bytes);
-    auto load_batch = [&](int b, Batch &dst) {
+    auto load_batch = [&](int b, int sg, Batch &dst) {  // row group b, segment sg
         const int row0 = R.row0(b);
         const int valid = R.valid(row0);
         const int64_t r0 = valid > 0 ? row0 : 0;
@@ -457,58 +461,68 @@ __global__ void __launch_bounds__(kThreads) gemv_w4a8_stream_kernel(
             dst.bs[r] = __builtin_amdgcn_raw_buffer_load_b16(rbias, 2 * r, 0, 0);
 #pragma unroll
             for (int t = 0; t < T; ++t)
-                dst.w[r][t] =
-                    __builtin_amdgcn_raw_buffer_load_b128(rw, wofs[t] + r * rb, 0, kNonTemporal);
+                dst.w[r][t] = __builtin_amdgcn_raw_buffer_load_b128(rw, wofs[sg][t] + r * rb, 0,
+                                                                    kNonTemporal);
         }
     };
     // activations and their scales first (see the W4A16 kernel), then the ring of batches
     float sx[MT];
 #pragma unroll
     for (int m = 0; m < MT; ++m) sx[m] = s_x[m < M ? m : M - 1];
-    constexpr int SI = (MT * T + 3) / 4;
-    const int64_t n_chunks = (int64_t)MT * cpr;
+    // (q rows are ldq apart with ldq % 16 == 0: a 16-byte piece that starts before d_in lies
+    // inside its row; pieces past d_in and threads past the last chunk read zeros)
+    constexpr int SI = (MT * T * SEG * kWave + BT - 1) / BT;  // >= ceil(MT * cpr / BT)
+    const int n_chunks = MT * static_cast<int>(cpr);
+    const int cpr_i = static_cast<int>(cpr);
+    const int din = static_cast<int>(d_in);
+    const rsrc_t rx = make_rsrc(q, 0x7FFFFFFFu);  // the host keeps the offsets below 2^31
     uint4 qraw[SI][2];
 #pragma unroll
     for (int si = 0; si < SI; ++si) {
-        int64_t idx = threadIdx.x + (int64_t)si * kThreads;
-        idx = idx < n_chunks ? idx : n_chunks - 1;
-        const int m = static_cast<int>(idx / cpr);
-        const int64_t c = idx - (int64_t)m * cpr;
+        const int idx = static_cast<int>(threadIdx.x) + si * BT;
+        const int m = MT == 1 ? 0 : idx / cpr_i;
+        const int c = idx - m * cpr_i;
         const int mx = m < M ? m : M - 1;  // tokens of the tile past M repeat token M - 1
 #pragma unroll
         for (int p = 0; p < 2; ++p) {
-            const int64_t col = c * kChunkCols + 16 * p;
-            const bool ok = col < d_in;
-            qraw[si][p] = *reinterpret_cast<const uint4 *>(q + (ok ? (int64_t)mx * ldq + col : 0));
+            const int col = c * kChunkCols + 16 * p;
+            const uint32_t off = idx < n_chunks && col < din
+                                     ? static_cast<uint32_t>((int64_t)mx * ldq + col)
+                                     : kOutOfRange;
+            qraw[si][p] =
+                __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
         }
     }
     Batch buf[NB];
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
         phase_fence();
-        load_batch(i, buf[i]);
+        load_batch(i / SEG, i % SEG, buf[i]);
     }
     phase_fence();
 
-    // permute to the nibble order ([Orin DP4A 做了什么]) and stage in LDS
-    // (selects, not branches: see the W4A16 kernel)
-    const int din = static_cast<int>(d_in);
+    // permute to the nibble order ([Orin DP4A 做了什么]) and stage in LDS (a wave whose chunks
+    // all lie past the end skips the work; see the W4A16 kernel)
+    const bool ragged = (din & 15) != 0;  // the piece holding column d_in - 1 has bytes past it
 #pragma unroll
     for (int si = 0; si < SI; ++si) {
-        // clamped like the loads: threads past the end rewrite the last record with equal bits
-        int64_t idx = threadIdx.x + (int64_t)si * kThreads;
-        idx = idx < n_chunks ? idx : n_chunks - 1;
-        const int m = static_cast<int>(idx / cpr);
-        const int c = static_cast<int>(idx - (int64_t)m * cpr);
+        if (si * BT + wid * kWave >= n_chunks) break;
+        const int idx = static_cast<int>(threadIdx.x) + si * BT;
+        const int m = MT == 1 ? 0 : idx / cpr_i;
+        const int c = idx - m * cpr_i;
         uint32_t u[8];
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const uint4 &raw = qraw[si][i >> 2];
-            const uint32_t w = (i & 3) == 0 ? raw.x : (i & 3) == 1 ? raw.y : (i & 3) == 2 ? raw.z : raw.w;
-            // bytes of this u32 that lie before d_in: 0..4
-            const int left = din - (c * kChunkCols + 4 * i);
-            const uint32_t keep = left >= 4 ? 0xFFFFFFFFu : (left <= 0 ? 0u : (1u << (8 * left)) - 1u);
-            u[i] = w & keep;
+            u[i] = (i & 3) == 0 ? raw.x : (i & 3) == 1 ? raw.y : (i & 3) == 2 ? raw.z : raw.w;
+        }
+        if (__builtin_expect(ragged, 0)) {  // zero the bytes at or past d_in
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int left = din - (c * kChunkCols + 4 * i);  // bytes before d_in: 0..4
+                u[i] &= left >= 4 ? 0xFFFFFFFFu : (left <= 0 ? 0u : (1u << (8 * left)) - 1u);
+            }
         }
         int sum = 0;
 #pragma unroll
@@ -522,7 +536,7 @@ __global__ void __launch_bounds__(kThreads) gemv_w4a8_stream_kernel(
         }
         rec.qsum = sum;
         rec.pad[0] = rec.pad[1] = rec.pad[2] = 0;
-        qsh[(int64_t)m * (cpr + 1) + c] = rec;
+        if (idx < n_chunks) qsh[m * (cpr_i + 1) + c] = rec;
     }
     if (threadIdx.x < MT) {
         XChunk8 zero;
@@ -539,19 +553,20 @@ __global__ void __launch_bounds__(kThreads) gemv_w4a8_stream_kernel(
         float v[RW][MT];
         int a[RW][MT];
     };
-    auto compute_batch = [&](const Batch &bt, Out &out) {
+    int carry[RW][MT];  // a row's sums from its earlier segments
+    auto compute_batch = [&](const Batch &bt, Out &out, int sg) {
         int acc[RW][MT];
 #pragma unroll
         for (int r = 0; r < RW; ++r)
 #pragma unroll
-            for (int m = 0; m < MT; ++m) acc[r][m] = 0;
+            for (int m = 0; m < MT; ++m) acc[r][m] = sg == 0 ? 0 : carry[r][m];
 #pragma unroll
         for (int t = 0; t < T; ++t) {
             uint32_t xe[MT][4], xo[MT][4];
             int qs[MT];
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
-                const XChunk8 &rec = qsh[(int64_t)m * (cpr + 1) + xofs[t]];
+                const XChunk8 &rec = qsh[(int64_t)m * (cpr + 1) + xofs[sg][t]];
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     xe[m][j] = rec.even[j];
@@ -576,6 +591,13 @@ __global__ void __launch_bounds__(kThreads) gemv_w4a8_stream_kernel(
 #pragma unroll
                 for (int m = 0; m < MT; ++m) acc[r][m] -= 8 * qs[m];
             }
+        }
+        if (sg < SEG - 1) {
+#pragma unroll
+            for (int r = 0; r < RW; ++r)
+#pragma unroll
+                for (int m = 0; m < MT; ++m) carry[r][m] = acc[r][m];
+            return;
         }
 #pragma unroll
         for (int r = 0; r < RW; ++r) {
@@ -619,16 +641,17 @@ __global__ void __launch_bounds__(kThreads) gemv_w4a8_stream_kernel(
         }
     };
 
-    Out out;  // the ring of the W4A16 kernel
+    Out out;  // the ring of the W4A16 kernel (b counts segments)
+    const int b_last = (R.b_last + 1) * SEG - 1;
     int b = 0;
     do {
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
-            if (b + i <= R.b_last) compute_batch(buf[i], out);
+            if (b + i <= b_last) compute_batch(buf[i], out, i % SEG);
             phase_fence();
-            load_batch(b + i + NB, buf[i]);
+            load_batch((b + i + NB) / SEG, i % SEG, buf[i]);
             phase_fence();
-            if (b + i <= R.b_last) store_batch(b + i, out);
+            if (i % SEG == SEG - 1 && b + i <= b_last) store_batch((b + i) / SEG, out);
         }
         b += NB;
     } while (b < n_batches);
@@ -754,11 +777,14 @@ hipError_t launch_w4a8_stream_t(const int8_t *q, int64_t ldq, int M, const float
                                 int64_t d_out, int64_t d_in, int64_t k_pad, void *y, int64_t ldy,
                                 bool out_f32, int32_t *acc, hipStream_t stream) {
     constexpr Shape S = stream_shape(T);
-    const StreamPlan p = plan_stream(d_out, T, S.rw, S.nb);
+    constexpr int SEG = MT == 1 && T >= 8 ? 2 : 1;  // see launch_w4a16_stream_t
+    static_assert(T % SEG == 0 && S.nb % SEG == 0, "segments");
+    constexpr int BT = SEG > 1 ? 2 * kThreads : kThreads;
+    const StreamPlan p = plan_stream(d_out, T, S.rw, S.nb, SEG, BT / kWave);
     const size_t lds = sizeof(XChunk8) * (size_t)MT * (size_t)(k_pad / kChunkCols + 1);
-    hipLaunchKernelGGL((gemv_w4a8_stream_kernel<MT, T, S.rw, S.nb>), dim3(p.grid), dim3(kThreads),
-                       lds, stream, q, ldq, M, s_x, qweight, s_w, bias, d_out, d_in, k_pad, y, ldy,
-                       out_f32 ? 1 : 0, acc, p.n_batches);
+    hipLaunchKernelGGL((gemv_w4a8_stream_kernel<MT, T / SEG, S.rw, S.nb, SEG, BT>), dim3(p.grid),
+                       dim3(BT), lds, stream, q, ldq, M, s_x, qweight, s_w, bias, d_out, d_in,
+                       k_pad, y, ldy, out_f32 ? 1 : 0, acc, p.n_batches);
     return hipGetLastError();
 }
 
@@ -845,7 +871,9 @@ hipError_t launch_w4a8_stream(const int8_t *q, const float *s_x, int64_t M, int6
                               int64_t d_out, int64_t d_in, int64_t k_pad, void *y, int64_t ldy,
                               bool out_f32, int32_t *acc, hipStream_t stream) {
     const int T = pick_steps(k_pad / kChunkCols);
-    const int tile = stream_token_tile(M, T);
+    int tile = stream_token_tile(M, T);
+    // the kernel addresses a tile's activations with 31-bit byte offsets; one token always fits
+    if ((int64_t)(tile - 1) * ldq + k_pad >= (int64_t)kOutOfRange) tile = 1;
     const size_t out_elem = out_f32 ? sizeof(float) : sizeof(uint16_t);
     for (int64_t m0 = 0; m0 < M; m0 += tile) {
         const int mt = static_cast<int>(M - m0 < tile ? M - m0 : tile);
