@@ -54,10 +54,9 @@ def source_hash(*files):
     return h.hexdigest()[:16]
 
 
-# the sources of the C2 gate/up GEMV's kernel and its dispatch: the committed traffic figure is
+# the sources of the C2 gate/up GEMV's kernel: the committed traffic figure is
 # reported only while their hash matches the one it was measured on
 TRAFFIC_SOURCES = ("int4_weight_only_amd/csrc/decode_i8.hip",
-                   "int4_weight_only_amd/csrc/decode.hip",
                    "int4_weight_only_amd/csrc/w4_device.h")
 
 

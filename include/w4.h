@@ -12,8 +12,8 @@
  * Conventions shared by every entry point
  *   - Array arguments are DEVICE pointers owned by the caller.  The library never allocates,
  *     frees or retains device memory and keeps no state between calls (thread-safe; calls on one
- *     stream are ordered by that stream).  Scratch memory, where a path needs it, is a workspace
- *     the caller passes in (w4_gemv).
+ *     stream are ordered by that stream).  No entry point needs scratch memory: partial sums
+ *     meet in LDS.
  *   - bf16 values travel as uint16_t bit patterns.  `stream` is a hipStream_t passed as void*
  *     (NULL = the default stream).  Calls enqueue kernels and return without synchronizing.
  *   - Arguments are validated on the host before anything is enqueued.  A failed check returns
@@ -52,8 +52,7 @@ typedef enum {
     W4_ERR_ALIGN = 4,       /* a pointer or leading dimension breaks the alignment rules       */
     W4_ERR_RANGE = 5,       /* a size beyond the limits stated for the entry point             */
     W4_ERR_UNSUPPORTED = 6, /* valid arguments this entry point does not serve (e.g. M > 64)   */
-    W4_ERR_HIP = 7,         /* a HIP launch or query failed; see w4_last_hip_error()           */
-    W4_ERR_WORKSPACE = 8    /* workspace missing or smaller than w4_gemv_workspace_bytes()     */
+    W4_ERR_HIP = 7          /* a HIP launch or query failed; see w4_last_hip_error()           */
 } w4_status;
 
 enum { W4_SYM = 0, W4_ASYM = 1 };         /* quantization mode                      */
@@ -91,14 +90,6 @@ int w4_pack(const float *w, int64_t d_out, int64_t d_in, int64_t ldw, int group_
             uint8_t *qweight, uint16_t *scales, uint16_t *zeros, void *stream);
 
 /*
- * w4_gemv_workspace_bytes -- host-only size query: bytes of device workspace w4_gemv needs for
- * these arguments (0 when it needs none, or when the arguments are invalid).
- * Two or more tokens with group_size 128, 256 or 0 take the matrix-core path, whose activation
- * fragments live in the workspace: about 4.1 KiB per 128 columns per 16 tokens.
- */
-size_t w4_gemv_workspace_bytes(int64_t M, int64_t d_out, int64_t d_in, int group_size);
-
-/*
  * w4_gemv -- W4A16 decode linear for 1 <= M <= 64 token rows, weights read once per call.
  * [Lab5 Prefill和Decode分流] (the small-M decode path), [Lab5 融合INT4反量化与矩阵乘]
  * (dequantize in registers inside the product, never a dense weight in memory),
@@ -109,24 +100,19 @@ size_t w4_gemv_workspace_bytes(int64_t M, int64_t d_out, int64_t d_in, int group
  *   y        [M][ldy], ldy >= d_out, element type out_dtype (W4_OUT_BF16 / W4_OUT_F32),
  *            naturally aligned.  Accumulation is fp32; the bf16 output is the round-to-nearest-
  *            even image of the fp32 result of the same call.
- *   workspace  device memory of at least w4_gemv_workspace_bytes(M, d_out, d_in, group_size)
- *            bytes, 16-byte aligned, owned by the caller (NULL allowed when that size is 0);
- *            overwritten by the call, so calls that may overlap in time need separate workspaces.
- *            W4_ERR_WORKSPACE if missing or too small.
  * M > 64 returns W4_ERR_UNSUPPORTED (use w4_gemm); d_in <= 65536 (else W4_ERR_RANGE).
  */
 int w4_gemv(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
             const uint16_t *scales, const uint16_t *zeros, const uint16_t *bias, int64_t d_out,
-            int64_t d_in, int group_size, void *y, int64_t ldy, int out_dtype, void *workspace,
-            size_t workspace_bytes, void *stream);
+            int64_t d_in, int group_size, void *y, int64_t ldy, int out_dtype, void *stream);
 
 /*
- * w4_gemm -- W4A16 prefill linear for any M >= 1 (the arguments of w4_gemv without the workspace,
- * and the same result).
+ * w4_gemm -- W4A16 prefill linear for any M >= 1 (the arguments of w4_gemv, and the same
+ * result within the tolerance).
  * [Lab5 Prefill和Decode分流] (large M: dequantize once per tile and run a dense matrix product).
- * Weight tiles are dequantized on chip to the exact integers (code - z) in bf16, multiplied on
- * the bf16 matrix cores with fp32 accumulation, and each group's partial product is scaled by
- * s[j][G] in fp32.  No dense weight is written to memory.
+ * Weight tiles are dequantized on chip to the fp32 values s (code - z), split into two bf16
+ * halves whose sum is exact, and multiplied on the bf16 matrix cores with fp32 accumulation.
+ * No dense weight is written to memory.
  */
 int w4_gemm(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
             const uint16_t *scales, const uint16_t *zeros, const uint16_t *bias, int64_t d_out,

@@ -17,7 +17,6 @@ import torch
 __all__ = [
     "W4_SYM", "W4_ASYM", "W4_OUT_BF16", "W4_OUT_F32", "W4Error", "packed_layout", "w4_pack",
     "w4_gemv", "w4_gemm", "act_quant_int8", "w4a8_gemv", "w4_linear", "library_path",
-    "gemv_workspace_bytes",
 ]
 
 W4_SYM, W4_ASYM = 0, 1
@@ -45,10 +44,8 @@ def _load():
                                      ctypes.POINTER(ctypes.c_size_t)]
     lib.w4_pack.argtypes = [p, i64, i64, i64, i32, i32, p, p, p, p]
     lin = [p, i64, i64, p, p, p, p, i64, i64, i32, p, i64, i32]
-    lib.w4_gemv.argtypes = lin + [p, ctypes.c_size_t, p]
+    lib.w4_gemv.argtypes = lin + [p]
     lib.w4_gemm.argtypes = lin + [p]
-    lib.w4_gemv_workspace_bytes.argtypes = [i64, i64, i64, i32]
-    lib.w4_gemv_workspace_bytes.restype = ctypes.c_size_t
     lib.act_quant_int8.argtypes = [p, i64, i64, i64, p, i64, p, p, p]
     lib.w4a8_gemv.argtypes = [p, p, i64, i64, p, p, p, i64, i64, p, i64, i32, p, p]
     for f in ("w4_packed_layout", "w4_pack", "w4_gemv", "w4_gemm", "act_quant_int8",
@@ -123,29 +120,7 @@ def w4_pack(w, group_size, mode, d_in=None):
     return qweight, scales, zeros
 
 
-def gemv_workspace_bytes(M, d_out, d_in, group_size):
-    """Bytes of device workspace w4_gemv needs for these arguments (host-only query)."""
-    return _lib.w4_gemv_workspace_bytes(M, d_out, d_in, group_size)
-
-
-# One cached workspace per (device, stream): calls queued on one stream run in order, so they can
-# share it; calls on different streams get their own.
-_workspaces = {}
-
-
-def _workspace(dev, nbytes):
-    if nbytes == 0:
-        return None
-    key = (dev.index, torch.cuda.current_stream(dev).cuda_stream)
-    ws = _workspaces.get(key)
-    if ws is None or ws.numel() < nbytes:
-        ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-        _workspaces[key] = ws
-    return ws
-
-
-def _linear(fn_name, x, qweight, scales, zeros, bias, d_in, group_size, out_dtype, out,
-            workspace=None):
+def _linear(fn_name, x, qweight, scales, zeros, bias, d_in, group_size, out_dtype, out):
     _need(x, "x", torch.bfloat16, dim=2)
     dev = x.device
     _need(qweight, "qweight", torch.uint8, dev, 2)
@@ -174,22 +149,13 @@ def _linear(fn_name, x, qweight, scales, zeros, bias, d_in, group_size, out_dtyp
     fn = getattr(_lib, fn_name)
     args = [_ptr(x), M, x.stride(0), _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(bias),
             d_out, d_in, group_size, _ptr(out), out.stride(0), out_dtype]
-    if fn_name == "w4_gemv":
-        if workspace is None:
-            workspace = _workspace(dev, gemv_workspace_bytes(M, d_out, d_in, group_size))
-        else:
-            _need(workspace, "workspace", torch.uint8, dev, 1)
-        args += [_ptr(workspace), 0 if workspace is None else workspace.numel()]
     _check(fn_name, fn(*args, _stream(dev)))
     return out
 
 
-def w4_gemv(x, qweight, scales, zeros, bias, d_in, group_size, out_dtype=W4_OUT_BF16, out=None,
-            workspace=None):
-    """Decode W4A16 linear, 1 <= M <= 64: y[M][d_out] = x . W_hat^T (+ b).  The workspace the
-    library needs (gemv_workspace_bytes) is cached per device and stream unless one is given."""
-    return _linear("w4_gemv", x, qweight, scales, zeros, bias, d_in, group_size, out_dtype, out,
-                   workspace)
+def w4_gemv(x, qweight, scales, zeros, bias, d_in, group_size, out_dtype=W4_OUT_BF16, out=None):
+    """Decode W4A16 linear, 1 <= M <= 64: y[M][d_out] = x . W_hat^T (+ b)."""
+    return _linear("w4_gemv", x, qweight, scales, zeros, bias, d_in, group_size, out_dtype, out)
 
 
 def w4_gemm(x, qweight, scales, zeros, bias, d_in, group_size, out_dtype=W4_OUT_BF16, out=None):

@@ -77,7 +77,6 @@ const char *w4_status_string(int status) {
         case W4_ERR_RANGE: return "size beyond the supported range";
         case W4_ERR_UNSUPPORTED: return "arguments not served by this entry point";
         case W4_ERR_HIP: return "HIP error (see w4_last_hip_error)";
-        case W4_ERR_WORKSPACE: return "workspace missing or smaller than w4_gemv_workspace_bytes";
         default: return "unknown status";
     }
 }
@@ -114,18 +113,9 @@ int w4_pack(const float *w, int64_t d_out, int64_t d_in, int64_t ldw, int group_
     return err == hipSuccess ? W4_OK : hip_fail(err);
 }
 
-size_t w4_gemv_workspace_bytes(int64_t M, int64_t d_out, int64_t d_in, int group_size) {
-    if (M < 1 || M > W4_GEMV_MAX_M || check_dims(d_out, d_in) != W4_OK || d_in > kDecodeMaxDin ||
-        !valid_group(group_size))
-        return 0;
-    const Layout L = layout_of(d_in, group_size);
-    return w4::gemv_workspace_bytes(M, d_out, L.k_pad, L.span, L.n_groups);
-}
-
 int w4_gemv(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
             const uint16_t *scales, const uint16_t *zeros, const uint16_t *bias, int64_t d_out,
-            int64_t d_in, int group_size, void *y, int64_t ldy, int out_dtype, void *workspace,
-            size_t workspace_bytes, void *stream) {
+            int64_t d_in, int group_size, void *y, int64_t ldy, int out_dtype, void *stream) {
     if (int st = check_linear(x, M, ldx, qweight, scales, zeros, bias, d_out, d_in, group_size,
                               y, ldy, out_dtype))
         return st;
@@ -133,12 +123,9 @@ int w4_gemv(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
     if (M > W4_GEMV_MAX_M) return W4_ERR_UNSUPPORTED;
     if (d_in > kDecodeMaxDin) return W4_ERR_RANGE;
     const Layout L = layout_of(d_in, group_size);
-    const size_t need = w4::gemv_workspace_bytes(M, d_out, L.k_pad, L.span, L.n_groups);
-    if (need > 0 && (!workspace || workspace_bytes < need)) return W4_ERR_WORKSPACE;
-    if (workspace && !aligned(workspace, 16)) return W4_ERR_ALIGN;
     const hipError_t err =
         w4::launch_gemv(x, M, ldx, qweight, scales, zeros, bias, d_out, d_in, L.k_pad, L.span,
-                        L.n_groups, y, ldy, out_dtype == W4_OUT_F32, workspace,
+                        L.n_groups, y, ldy, out_dtype == W4_OUT_F32,
                         static_cast<hipStream_t>(stream));
     return err == hipSuccess ? W4_OK : hip_fail(err);
 }

@@ -524,26 +524,19 @@ int log2_exact(int64_t v) {
 
 }  // namespace
 
-size_t gemv_workspace_bytes(int64_t M, int64_t d_out, int64_t k_pad, int64_t span,
-                            int64_t n_groups) {
-    return gemv_mfma_supported(M, d_out, k_pad, span, n_groups) ? gemv_mfma_workspace_bytes(M, k_pad)
-                                                                : 0;
-}
-
 hipError_t launch_gemv(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
                        const uint16_t *scales, const uint16_t *zeros, const uint16_t *bias,
                        int64_t d_out, int64_t d_in, int64_t k_pad, int64_t span,
-                       int64_t n_groups, void *y, int64_t ldy, bool out_f32, void *workspace,
-                       hipStream_t stream) {
+                       int64_t n_groups, void *y, int64_t ldy, bool out_f32, hipStream_t stream) {
     // Group-aligned shapes: the int8 matrix cores, with the codes as an operand as they are.
     if (gemv_i8_preferred(M, d_out, k_pad) &&
         gemv_i8_supported(M, d_out, d_in, k_pad, span, n_groups, ldx))
         return launch_gemv_i8(x, M, ldx, qweight, scales, zeros, bias, d_out, d_in, k_pad, span,
                               n_groups, y, ldy, out_f32, stream);
     // Two or more tokens: the matrix-core path reads the weights once for all of them.
-    if (gemv_mfma_supported(M, d_out, k_pad, span, n_groups))
+    if (gemv_mfma_supported(M, d_out, d_in, k_pad, span, n_groups, ldx, zeros != nullptr))
         return launch_gemv_mfma(x, M, ldx, qweight, scales, zeros, bias, d_out, d_in, k_pad, span,
-                                n_groups, y, ldy, out_f32, workspace, stream);
+                                n_groups, y, ldy, out_f32, stream);
     const int64_t cpr = k_pad / kChunkCols;
     // chunks per group is a power of two (group sizes 32..256); one group per row -> shift 62
     const int shift = n_groups == 1 ? 62 : log2_exact(span / kChunkCols);

@@ -6,28 +6,31 @@
 // 实践：super 分支从 9 tok/s 到 24 tok/s" (section "模型尺寸和 decode 的真实瓶颈": y = W x + b, and
 // decode time is the weight stream).
 //
-// Two kernels:
-//   * xprep: the activations, once per call, into fp16 MFMA fragments in a workspace.  For each
-//     token and 128-column chunk, a power-of-two exponent e is chosen so that the chunk's largest
-//     |x| * 2^-e lies in [2^14, 2^15); bf16 carries 8 significant bits and fp16 11, so every
-//     value down to 2^-17 of that range is exact (smaller ones are fp16 subnormals: absolute
-//     error at most 2^-25 * 2^e).  The chunk's sum of x * 2^-e is kept for zero points that are
-//     not small integers.
-//   * the decode kernel: a persistent grid, one block per slice of d_out / (number of compute
-//     units) output rows (two blocks per unit for slices above 96 rows), in tiles of 16 rows; the
-//     waves of a block split the K chunks, and their
-//     partial sums meet in LDS in a fixed order (deterministic).  Per chunk and tile a lane loads
-//     16 bytes of one row (32 codes), dequantizes them to the exact integers (c - z) in fp16 with
-//     the magic-number form ((w & 0x000F000F) | 0x64006400 = (1024 + c0, 1024 + c4), one packed
-//     fp16 add or fma removes 1024 + z), and four v_mfma_f32_16x16x32_f16 multiply them with the
-//     activation fragments: A = 16 tokens x 32 columns, B = 32 columns x 16 rows.  The fp32 result
-//     of the chunk is scaled by s[row][group] * 2^e[token] and accumulated in fp32.
+// One kernel, no workspace. A persistent grid gives each block a contiguous slice of d_out /
+// (number of compute units) output rows, as T tiles of 16 rows; the waves of the block split the
+// row's K range in pairs of 128-column chunks (a pair is one 128-byte line of each row), and each
+// wave streams the (pair, tile) units of its range:
+//   * activations: per pair, a lane (m, q) loads 64 bf16 values of token m (columns 32 q ..
+//     32 q + 31 of each chunk) straight from x, and converts them to the fp16 operand of
+//     v_mfma_f32_16x16x32_f16 (A = 16 tokens x 32 columns). Per token and pair a power of two
+//     2^-e scales the values so that the pair's largest |x| lies in [2^14, 2^15); bf16 carries 8
+//     significant bits and fp16 11, so every value down to 2^-17 of that maximum is exact (smaller
+//     ones lose bits as fp16 subnormals: absolute error at most 2^-25 2^e). Each chunk of x is
+//     converted once per block, by the wave that owns it, and never written back;
+//   * weights: a unit is 16 rows x 256 columns, two 16-byte loads per lane that read both halves
+//     of the rows' 128-byte lines back to back; the 32 codes of a load become the exact fp16
+//     integers (c - z) with the magic-number form ((w & 0x000F000F) | 0x64006400 = (1024 + c0,
+//     1024 + c4), one packed fp16 add or fma removes 1024 + z), and four MFMAs multiply them with
+//     the activation operand;
+//   * the chunk's fp32 result is scaled by s[row][group] 2^e[token] and accumulated in fp32.
+// A block's scales (and zero points, as the two fp16 pair constants the dequantization uses)
+// are read once, coalesced, into an LDS table. The waves' partial sums meet in LDS and are added
+// in wave order (deterministic).
 //
-// Weight loads are raw buffer loads through a descriptor covering exactly the block's rows, so a
-// row past the block or a chunk past the row reads zeros without touching memory; every load is
-// unconditional and sits in a ring of P chunks in flight per wave. They use the default cache
-// policy: a load covers one 64-byte half of 16 rows' lines and the same wave reads the other
-// half next, which the streaming (non-temporal) hint made about 10% slower.
+// Loads are raw buffer loads: a row past the block, a unit past a wave's share or a column past
+// the row end reads zeros without touching memory. Every load is unconditional; a unit or pair
+// past the wave's share gets bit 31 of its offset set arithmetically (a select on a wave-uniform
+// condition becomes a branch, and the waits after it would drain the ring).
 #include "w4_device.h"
 #include "w4_launch.h"
 
@@ -37,265 +40,389 @@ namespace {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kChunk = 128;        // columns per chunk (four 32-deep MFMAs)
-constexpr int kTokTile = 16;       // tokens per MFMA tile
-constexpr int kMaxWaves = 8;       // waves per decode block
-constexpr int kPrepThreads = 256;  // 16 tokens x 16 column octets
+constexpr int kTokThreads = 512;  // at most 8 waves per block
+constexpr int kTokMaxWaves = kTokThreads / kWave;
+constexpr int kTokTile = 16;      // tokens per MFMA tile
+constexpr uint32_t kTokLdsLimit = 160 * 1024;
+// Activation offset of a lane without a token: past the input (below 2^30, host-checked), and
+// still below 2^32 with bit 31 added.
+constexpr uint32_t kTokNoToken = 0x40000000u;
 
-// ---------------------------------------------------------------------------------------------
-// Workspace layout (all offsets in bytes from its start; tt = token tile, c = chunk):
-//   frag[tt][c][t][lane]  16 bytes: the 8 fp16 activations of MFMA t (0..3) for lane
-//                         lane = 16 q + m: token 16 tt + m, columns 128 c + 32 q + 8 t + {0..7}
-//                         in the order 0 4 1 5 2 6 3 7 (the order of the dequantized pairs)
-//   expo[tt][c][16]       int32 exponent e of each token of the tile
-//   xsum[tt][c][16]       fp32 sum of x * 2^-e over the chunk
-// ---------------------------------------------------------------------------------------------
-struct WsLayout {
-    int64_t frag, expo, xsum, total;
+// LDS layout (bytes): table [16 T rows][n_groups] entries -- symmetric: the fp32 scale; with zero
+// points: {fp32 scale, fp16 pair -(1024 + zi), fp16 pair -(64 + zi), fp32 residual z - zi}
+// (rows past the slice are never written: only lanes whose results are dropped read them); red
+// [W][T][64] fp32 x 4 partial sums; flags [W] (a wave's rows hold a non-integer zero point).
+struct TokLds {
+    uint32_t table, red, flags, total;
 };
 
-WsLayout ws_layout(int64_t M, int64_t k_pad) {
-    const int64_t tt = (M + kTokTile - 1) / kTokTile;
-    const int64_t C = (k_pad + kChunk - 1) / kChunk;
-    WsLayout L{};
-    L.frag = 0;
-    L.expo = tt * C * 4 * 64 * 16;
-    L.xsum = L.expo + tt * C * kTokTile * 4;
-    L.total = L.xsum + tt * C * kTokTile * 4;
+__host__ __device__ inline uint32_t tok_align16(uint32_t v) { return (v + 15u) & ~15u; }
+
+__host__ __device__ inline TokLds tok_lds(int T, int n_groups, int W, bool zp) {
+    TokLds L;
+    L.table = 0;
+    L.red = tok_align16(16u * T * n_groups * (zp ? 16u : 4u));
+    L.flags = L.red + static_cast<uint32_t>(W) * T * kWave * 16u;
+    L.total = L.flags + 16u * 4u;
     return L;
 }
 
-__global__ void __launch_bounds__(kPrepThreads) xprep_kernel(
-    const uint16_t *__restrict__ x, int M, int64_t ldx, int d_in, int C, uint4 *__restrict__ frag,
-    int *__restrict__ expo, float *__restrict__ xsum) {
-    const int c = blockIdx.x, tt = blockIdx.y;
-    const int tid = threadIdx.x;
-    const int m = tid >> 4;   // token within the tile
-    const int j = tid & 15;   // column octet within the chunk: j = 4 q + t
-    const int token = tt * kTokTile + m;
-    const int col = c * kChunk + 8 * j;
-    uint4 raw = make_uint4(0, 0, 0, 0);
-    if (token < M && col < d_in) raw = *reinterpret_cast<const uint4 *>(x + token * ldx + col);
-    const uint32_t u[4] = {raw.x, raw.y, raw.z, raw.w};
-    float v[8];
-    float amax = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const uint32_t bits = (e & 1) ? (u[e >> 1] >> 16) : (u[e >> 1] & 0xFFFFu);
-        v[e] = col + e < d_in ? bf16_to_f32(bits) : 0.0f;
-        amax = fmaxf(amax, fabsf(v[e]));
-    }
-    // the 16 threads of a token are 16 consecutive lanes
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
-    const int ex = amax > 0.0f ? ilogbf(amax) - 14 : 0;
-    _Float16 h[8];
-    float sum = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float s = ldexpf(v[e], -ex);
-        h[e] = static_cast<_Float16>(s);
-        sum += s;
-    }
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o, kWave);
-    const int q = j >> 2, t = j & 3;
-    half8_t out = {h[0], h[4], h[1], h[5], h[2], h[6], h[3], h[7]};
-    frag[((static_cast<int64_t>(tt) * C + c) * 4 + t) * 64 + q * 16 + m] =
-        *reinterpret_cast<const uint4 *>(&out);
-    if (j == 0) {
-        expo[(static_cast<int64_t>(tt) * C + c) * kTokTile + m] = ex;
-        xsum[(static_cast<int64_t>(tt) * C + c) * kTokTile + m] = sum;
-    }
-}
-
-// One ring slot: the activation fragments, exponents (and sums) of a chunk, and T tiles of
-// weights with their scales (and zero points).
-template <int T, bool ZP>
-struct Slot {
-    uint32_t xa[4][4];
-    uint32_t xe[4];
-    uint32_t xs[4];
-    uint32_t w[T][4];
-    uint32_t s[T];
-    uint32_t z[T];
-};
-
 // Exact fp16 (c - zi) pairs of the 8 codes of one packed dword, in the order
-// (c0, c4), (c1, c5), (c2, c6), (c3, c7).  zlo = (1024 + zi) and zhi = (64 + zi) as fp16 pairs.
+// (c0, c4), (c1, c5), (c2, c6), (c3, c7).  zlo = -(1024 + zi) and zhi = -(64 + zi) as fp16 pairs.
 __device__ __forceinline__ half8_t dequant8(uint32_t w, uint32_t zlo_neg, uint32_t zhi_neg) {
-    typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
     const uint32_t w8 = w >> 8;
     const uint32_t p0 = and_or(w, 0x000F000Fu, 0x64006400u);
     const uint32_t p1 = and_or(w, 0x00F000F0u, 0x64006400u);
     const uint32_t p2 = and_or(w8, 0x000F000Fu, 0x64006400u);
     const uint32_t p3 = and_or(w8, 0x00F000F0u, 0x64006400u);
-    const half2_t zl = __builtin_bit_cast(half2_t, zlo_neg);
-    const half2_t zh = __builtin_bit_cast(half2_t, zhi_neg);
+    const half2_t zl = as_half2(zlo_neg);
+    const half2_t zh = as_half2(zhi_neg);
     const half2_t sixteenth = {static_cast<_Float16>(0.0625f), static_cast<_Float16>(0.0625f)};
-    const half2_t v0 = __builtin_bit_cast(half2_t, p0) + zl;
-    const half2_t v1 = __builtin_bit_cast(half2_t, p1) * sixteenth + zh;
-    const half2_t v2 = __builtin_bit_cast(half2_t, p2) + zl;
-    const half2_t v3 = __builtin_bit_cast(half2_t, p3) * sixteenth + zh;
+    const half2_t v0 = as_half2(p0) + zl;
+    const half2_t v1 = as_half2(p1) * sixteenth + zh;
+    const half2_t v2 = as_half2(p2) + zl;
+    const half2_t v3 = as_half2(p3) * sixteenth + zh;
     half8_t r = {v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
     return r;
 }
 
-template <int T, int P, bool ZP>
-__global__ void __launch_bounds__(kMaxWaves * kWave) gemv_mfma_kernel(
+// The activations of one pair for one lane: 2 chunks x 4 pieces of 8 bf16 values.
+struct XRaw {
+    u32x4_t v[2][4];
+};
+
+// The converted pair: MFMA operands, the factors 2^e of the tokens whose D rows this lane holds,
+// and (for non-integer zero points) the sums of the scaled activations.
+struct XOp {
+    half8_t a[2][4];
+    float p[4];
+    floatx4_t sx[2];
+};
+
+// P: weight units in flight per wave, one pair's worth (at least 8 KiB): a unit's ring slot is a
+// constant in a loop body of two pairs (rings that do not match the tiles of a pair made the
+// register allocator spill); XR: pairs of activations in flight.
+template <int T>
+struct TokShape {
+    static constexpr int P = T == 1 ? 2 : T == 2 ? 4 : T;
+    static constexpr int XR = T == 1 ? 2 : 1;
+    static_assert((2 * T) % P == 0, "ring slots must repeat within two pairs");
+};
+
+template <int T, bool ZP>
+__global__ void __launch_bounds__(kTokThreads) gemv_tok_kernel(
+    const uint16_t *__restrict__ x, int64_t ldx, int M, int d_in,
     const uint8_t *__restrict__ qweight, const uint16_t *__restrict__ scales,
-    const uint16_t *__restrict__ zeros, const uint16_t *__restrict__ bias,
-    const uint4 *__restrict__ frag, const int *__restrict__ expo, const float *__restrict__ xsum,
-    int d_out, int row_bytes, int n_groups, int group_shift, int C, int M, int TT,
-    int rows_per_block, void *__restrict__ y, int64_t ldy, int out_f32) {
-    extern __shared__ floatx4_t red[];  // [W][T][64]
+    const uint16_t *__restrict__ zeros, const uint16_t *__restrict__ bias, int d_out,
+    int row_bytes, int n_groups, int gshift, int C, int rows_per_block, void *__restrict__ y,
+    int64_t ldy, int out_f32) {
+    constexpr int P = TokShape<T>::P;
+    constexpr int XR = TokShape<T>::XR;
+    extern __shared__ __align__(16) unsigned char lds[];
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int W = blockDim.x / kWave;
     const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int r0 = blockIdx.x * rows_per_block;
-    const int r1 = d_out < r0 + rows_per_block ? d_out : r0 + rows_per_block;
-    const int nrows = r1 - r0;
-    const int c0 = (C * w) / W, c1 = (C * (w + 1)) / W;  // this wave's chunks
-    const int L = c1 - c0;
+    const int R = d_out - r0 < rows_per_block ? d_out - r0 : rows_per_block;  // >= 1
     const int n = lane & 15, q = lane >> 4;
+    const int npairs = (C + 1) >> 1;
+    const int p0 = npairs * w / W;
+    const int np = npairs * (w + 1) / W - p0;  // this wave's pairs
+    const TokLds L = tok_lds(T, n_groups, W, ZP);
 
-    const rsrc_t rq = make_rsrc(qweight + static_cast<int64_t>(r0) * row_bytes,
-                                static_cast<uint32_t>(nrows) * static_cast<uint32_t>(row_bytes));
-    const uint32_t gbytes = static_cast<uint32_t>(nrows) * static_cast<uint32_t>(n_groups) * 2u;
-    const rsrc_t rs = make_rsrc(scales + static_cast<int64_t>(r0) * n_groups, gbytes);
-    const rsrc_t rz = make_rsrc(ZP ? zeros + static_cast<int64_t>(r0) * n_groups : scales,
-                                ZP ? gbytes : 0u);
-    const uint32_t frag_bytes = static_cast<uint32_t>(TT) * C * 4 * 64 * 16;
-    const uint32_t tok_bytes = static_cast<uint32_t>(TT) * C * kTokTile * 4;
-    const rsrc_t rf = make_rsrc(frag, frag_bytes);
-    const rsrc_t re = make_rsrc(expo, tok_bytes);
-    const rsrc_t rx = make_rsrc(xsum, tok_bytes);
+    const uint32_t rb = static_cast<uint32_t>(row_bytes);
+    const rsrc_t rq = make_rsrc(qweight + (int64_t)r0 * row_bytes, static_cast<uint32_t>(R) * rb);
+    // the activations' descriptor covers exactly the M x ldx input (the host keeps it below 2^31)
+    const rsrc_t rx = make_rsrc(x, static_cast<uint32_t>(M) * static_cast<uint32_t>(ldx) * 2u);
 
-    for (int tt = 0; tt < TT; ++tt) {
-        const bool tok_ok = tt * kTokTile + n < M;  // this lane's activation row holds a token
-        auto load = [&](int b, Slot<T, ZP> &S) {
-            const int c = c0 + b;
-            const bool ok = b < L;
-            const uint32_t fbase = ((static_cast<uint32_t>(tt) * C + c) * 4) * 1024u + lane * 16u;
+    // Offsets are a per-lane part, fixed for the whole kernel, plus a wave-uniform part passed
+    // through an opaque scalar (otherwise the compiler keeps one lane-part-plus-tile-offset VGPR
+    // per tile alive across the loop). A unit or pair past the wave's share has bit 31 set in the
+    // uniform part (the host keeps every sum below 2^31 before that bit).
+    auto uni = [](uint32_t v) {
+        asm volatile("" : "+s"(v));
+        return v;
+    };
+
+    // ---- weight units: unit (j, i) = pair pr = p0 + j of tile i; lane (n, q) reads row 16 i + n,
+    // bytes 128 pr + 16 q (first chunk) and 128 pr + 64 + 16 q (second chunk). In a row's last,
+    // partial pair the bytes past the row belong to the next row (or lie past the slice and read
+    // zeros): their activations are zero, so they add exactly nothing ----
+    const uint32_t w_lane = static_cast<uint32_t>(n) * rb + 16u * q;
+    auto wload = [&](int j, int i, u32x4_t &lo, u32x4_t &hi) {
+        const uint32_t past = static_cast<uint32_t>((np - 1 - j) >> 31) << 31;
+        const uint32_t u = uni((16u * static_cast<uint32_t>(i) * rb +
+                                128u * static_cast<uint32_t>(p0 + j)) | past);
+        lo = __builtin_amdgcn_raw_buffer_load_b128(rq, w_lane + u, 0, 0);
+        hi = __builtin_amdgcn_raw_buffer_load_b128(rq, w_lane + u + 64u, 0, 0);
+    };
+
+    // ---- activations of pair j for token tile tt: lane (m, q), token 16 tt + m, columns
+    // 256 pr + 128 h + 32 q + 8 t .. + 7 (columns past d_in are zeroed after the load) ----
+    auto xload = [&](int tt, int j, XRaw &X) {
+        const uint32_t past = static_cast<uint32_t>((np - 1 - j) >> 31) << 31;
+        const int token = tt * kTokTile + n;
+        const uint32_t x_lane =
+            token < M ? static_cast<uint32_t>(token) * static_cast<uint32_t>(ldx) * 2u + 64u * q
+                      : kTokNoToken;
+        const uint32_t u = uni((512u * static_cast<uint32_t>(p0 + j)) | past);
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const uint4 v = __builtin_bit_cast(
-                    uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                               rf, ok && tok_ok ? fbase + t * 1024u : kOutOfRange, 0, 0));
-                S.xa[t][0] = v.x; S.xa[t][1] = v.y; S.xa[t][2] = v.z; S.xa[t][3] = v.w;
-            }
-            const uint32_t tbase = ((static_cast<uint32_t>(tt) * C + c) * kTokTile + 4 * q) * 4u;
-            {
-                const uint4 v = __builtin_bit_cast(
-                    uint4, __builtin_amdgcn_raw_buffer_load_b128(re, ok ? tbase : kOutOfRange, 0, 0));
-                S.xe[0] = v.x; S.xe[1] = v.y; S.xe[2] = v.z; S.xe[3] = v.w;
-            }
-            if (ZP) {
-                const uint4 v = __builtin_bit_cast(
-                    uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, ok ? tbase : kOutOfRange, 0, 0));
-                S.xs[0] = v.x; S.xs[1] = v.y; S.xs[2] = v.z; S.xs[3] = v.w;
-            }
-            const uint32_t kb = static_cast<uint32_t>(c) * 64u + 16u * q;  // byte within the row
-            const bool kok = ok && kb + 16u <= static_cast<uint32_t>(row_bytes);
-            const uint32_t G = static_cast<uint32_t>(c) >> group_shift;
-#pragma unroll
-            for (int i = 0; i < T; ++i) {
-                const uint32_t row = 16u * i + n;
-                const uint4 v = __builtin_bit_cast(
-                    uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                               rq, kok ? row * row_bytes + kb : kOutOfRange, 0, 0));
-                S.w[i][0] = v.x; S.w[i][1] = v.y; S.w[i][2] = v.z; S.w[i][3] = v.w;
-                const uint32_t go = ok ? (row * n_groups + G) * 2u : kOutOfRange;
-                S.s[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, go, 0, 0);
-                if (ZP) S.z[i] = __builtin_amdgcn_raw_buffer_load_b16(rz, go, 0, 0);
-            }
-        };
-
-        floatx4_t acc[T];
-#pragma unroll
-        for (int i = 0; i < T; ++i) acc[i] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
-
-        auto compute = [&](const Slot<T, ZP> &S) {
-            half8_t a[4];
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int t = 0; t < 4; ++t)
-                a[t] = __builtin_bit_cast(half8_t, make_uint4(S.xa[t][0], S.xa[t][1], S.xa[t][2],
-                                                              S.xa[t][3]));
-#pragma unroll
-            for (int i = 0; i < T; ++i) {
-                // zero point = integer zi (|zi| <= 1024, exact in the fp16 form) + residual zr
-                uint32_t zlo = 0xE408E408u;  // -(1024 + 8) as an fp16 pair
-                uint32_t zhi = 0xD480D480u;  // -(64 + 8)
-                float zr = 0.0f;
-                if (ZP) {
-                    const float z = bf16_to_f32(S.z[i]);
-                    float zi = __builtin_rintf(z);
-                    zi = fminf(fmaxf(zi, -1024.0f), 1024.0f);
-                    zr = z - zi;
-                    const uint32_t hl = __builtin_bit_cast(uint16_t, static_cast<_Float16>(-(1024.0f + zi)));
-                    const uint32_t hh = __builtin_bit_cast(uint16_t, static_cast<_Float16>(-(64.0f + zi)));
-                    zlo = hl | (hl << 16);
-                    zhi = hh | (hh << 16);
-                }
-                floatx4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    d = __builtin_amdgcn_mfma_f32_16x16x32_f16(a[t], dequant8(S.w[i][t], zlo, zhi),
-                                                               d, 0, 0, 0);
-                const float sv = bf16_to_f32(S.s[i]);
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const float f = ldexpf(sv, static_cast<int>(S.xe[r]));
-                    float v = d[r];
-                    if (ZP) v = fmaf(-zr, __uint_as_float(S.xs[r]), v);
-                    acc[i][r] = fmaf(f, v, acc[i][r]);
-                }
-            }
-        };
+                X.v[h][t] = __builtin_amdgcn_raw_buffer_load_b128(
+                    rx, x_lane + u + static_cast<uint32_t>(256 * h + 16 * t), 0, 0);
+    };
 
-        Slot<T, ZP> ring[P];
+    XRaw xr[XR];
+    u32x4_t rlo[P], rhi[P];
+    auto prime = [&](int tt) {
 #pragma unroll
-        for (int p = 0; p < P; ++p) {
+        for (int s = 0; s < XR; ++s) {
             phase_fence();
-            load(p, ring[p]);
+            xload(tt, s, xr[s]);
+        }
+#pragma unroll
+        for (int s = 0; s < P; ++s) {
+            phase_fence();
+            wload(s / T, s % T, rlo[s], rhi[s]);
         }
         phase_fence();
-        // Slots past the wave's last chunk were loaded out of range (zeros): computing them adds
-        // exactly 0, and leaving the computation unconditional keeps the loop free of branches
-        // (after a skipped slot, the compiler would wait for its loads before reusing registers).
-        int b = 0;
-        do {
-#pragma unroll
-            for (int p = 0; p < P; ++p) {
-                compute(ring[p]);
-                phase_fence();
-                load(b + p + P, ring[p]);
-                phase_fence();
-            }
-            b += P;
-        } while (b < L);
+    };
+    prime(0);  // the first loads are in flight while the table is built
 
-        // partial sums of the W waves meet in LDS; summed in wave order
+    // this wave's partial sums, [T][64] fp32 x 4 in LDS (read and written once per unit)
+    float4 *red = reinterpret_cast<float4 *>(lds + L.red);
+    float4 *mine = red + w * T * kWave + lane;
+    auto zero_mine = [&]() {
 #pragma unroll
-        for (int i = 0; i < T; ++i) red[(w * T + i) * kWave + lane] = acc[i];
+        for (int i = 0; i < T; ++i) mine[i * kWave] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    };
+    zero_mine();
+
+    // ---- scale / zero-point table of the slice ----
+    {
+        const int nent = R * n_groups;
+        const uint16_t *sp = scales + (int64_t)r0 * n_groups;
+        const uint16_t *zp = ZP ? zeros + (int64_t)r0 * n_groups : nullptr;
+        int frac = 0;
+        for (int e = tid; e < nent; e += blockDim.x) {
+            const float s = bf16_to_f32(sp[e]);
+            if (ZP) {
+                const float z = bf16_to_f32(zp[e]);
+                const float zi = fminf(fmaxf(__builtin_rintf(z), -1024.0f), 1024.0f);
+                const float zr = z - zi;
+                frac |= zr != 0.0f;
+                const uint32_t hl =
+                    __builtin_bit_cast(uint16_t, static_cast<_Float16>(-(1024.0f + zi)));
+                const uint32_t hh =
+                    __builtin_bit_cast(uint16_t, static_cast<_Float16>(-(64.0f + zi)));
+                const u32x4_t ent = {__float_as_uint(s), hl | (hl << 16), hh | (hh << 16),
+                                     __float_as_uint(zr)};
+                *reinterpret_cast<u32x4_t *>(lds + L.table + 16u * e) = ent;
+            } else {
+                *reinterpret_cast<float *>(lds + L.table + 4u * e) = s;
+            }
+        }
+        if (ZP) {
+            const bool any = __builtin_amdgcn_ballot_w64(frac != 0) != 0;
+            if (lane == 0) reinterpret_cast<int *>(lds + L.flags)[w] = any ? 1 : 0;
+        }
+    }
+    __syncthreads();
+    bool frac_any = false;
+    if (ZP) {
+        const int *fl = reinterpret_cast<const int *>(lds + L.flags);
+        int f = 0;
+        for (int i = 0; i < W; ++i) f |= fl[i];
+        frac_any = f != 0;
+    }
+
+    auto convert = [&](int j, const XRaw &X, XOp &O) {
+        const int colq = 256 * (p0 + j) + 32 * q;
+        uint32_t u[2][16];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                u[h][4 * t + 0] = X.v[h][t].x;
+                u[h][4 * t + 1] = X.v[h][t].y;
+                u[h][4 * t + 2] = X.v[h][t].z;
+                u[h][4 * t + 3] = X.v[h][t].w;
+            }
+        if (__builtin_expect(256 * (p0 + j + 1) > d_in, 0)) {  // zero the columns past d_in
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+#pragma unroll
+                for (int k = 0; k < 16; ++k) {
+                    const int col = colq + 128 * h + 8 * (k >> 2) + 2 * (k & 3);
+                    u[h][k] &= col + 1 < d_in ? 0xFFFFFFFFu : (col < d_in ? 0x0000FFFFu : 0u);
+                }
+        }
+        // largest magnitude of the pair for token m: bf16 magnitude bits are monotone in |x|
+        u16x2_t m2 = {0, 0};
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int k = 0; k < 16; ++k)
+                m2 = __builtin_elementwise_max(m2,
+                                               __builtin_bit_cast(u16x2_t, u[h][k] & 0x7FFF7FFFu));
+        uint32_t am = m2[0] > m2[1] ? m2[0] : m2[1];
+        am = max(am, static_cast<uint32_t>(__shfl_xor(static_cast<int>(am), 16, kWave)));
+        am = max(am, static_cast<uint32_t>(__shfl_xor(static_cast<int>(am), 32, kWave)));
+        const float amax = __uint_as_float(am << 16);
+        const int ex = amax > 0.0f ? ilogbf(amax) - 14 : 0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                __builtin_amdgcn_sched_barrier(0);  // one piece at a time: bounded registers
+                float f[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t d = u[h][4 * t + (e >> 1)];
+                    const uint32_t bits = (e & 1) ? (d & 0xFFFF0000u) : (d << 16);
+                    f[e] = ldexpf(__uint_as_float(bits), -ex);
+                }
+                // operand order (0, 4), (1, 5), (2, 6), (3, 7): the order of the dequantized pairs
+                half8_t a;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const half2_t hp = __builtin_bit_cast(
+                        half2_t, __builtin_amdgcn_cvt_pkrtz(f[k], f[k + 4]));
+                    a[2 * k] = hp[0];
+                    a[2 * k + 1] = hp[1];
+                }
+                O.a[h][t] = a;
+            }
+        // D lane (n, q) holds tokens 4 q .. 4 q + 3; their factors sit in lanes 4 q + r
+        const float pm = ldexpf(1.0f, ex);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) O.p[r] = __shfl(pm, 4 * q + r, kWave);
+        if (ZP && frac_any) {  // sums of the scaled activations, through a ones operand
+            const half8_t ones = {1, 1, 1, 1, 1, 1, 1, 1};
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                floatx4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    s = __builtin_amdgcn_mfma_f32_16x16x32_f16(O.a[h][t], ones, s, 0, 0, 0);
+                O.sx[h] = s;
+            }
+        }
+    };
+
+    const uint32_t t_lane = static_cast<uint32_t>(n) * n_groups;  // table row of lane's row n
+    auto compute = [&](int i, int j, const u32x4_t &wlo, const u32x4_t &whi, const XOp &O) {
+        // every LDS read first (sums, both table entries), then the two chunks' MFMA chains
+        // interleaved: they are independent, so neither waits for the other's results
+        const float4 a4 = mine[i * kWave];
+        float sc[2];
+        uint32_t zlo[2] = {0xE408E408u, 0xE408E408u};  // -(1024 + 8) as an fp16 pair
+        uint32_t zhi[2] = {0xD480D480u, 0xD480D480u};  // -(64 + 8)
+        float zr[2] = {0.0f, 0.0f};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            int G = (2 * (p0 + j) + h) >> gshift;
+            G = G < n_groups ? G : n_groups - 1;  // past the last chunk: x is zero there
+            const uint32_t e = t_lane + uni(static_cast<uint32_t>(16 * i * n_groups + G));
+            if (ZP) {
+                const u32x4_t ent = *reinterpret_cast<const u32x4_t *>(lds + L.table + 16u * e);
+                sc[h] = __uint_as_float(ent.x);
+                zlo[h] = ent.y;
+                zhi[h] = ent.z;
+                zr[h] = __uint_as_float(ent.w);
+            } else {
+                sc[h] = *reinterpret_cast<const float *>(lds + L.table + 4u * e);
+            }
+        }
+        floatx4_t d[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const uint32_t wd = (h ? whi : wlo)[t];
+                d[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(O.a[h][t],
+                                                              dequant8(wd, zlo[h], zhi[h]), d[h],
+                                                              0, 0, 0);
+            }
+        float acc[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float v = d[h][r];
+                if (ZP && frac_any) v = fmaf(-zr[h], O.sx[h][r], v);
+                acc[r] = fmaf(sc[h] * O.p[r], v, acc[r]);
+            }
+        mine[i * kWave] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    };
+
+    const int TT = (M + kTokTile - 1) / kTokTile;
+    for (int tt = 0; tt < TT; ++tt) {
+        if (tt > 0) {  // the previous tile's sums have been read (barrier below)
+            zero_mine();
+            prime(tt);
+        }
+        // bodies of two pairs: every unit and activation slot index is a constant
+        int j = 0;
+        for (; j + 2 <= np; j += 2) {
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                XOp O;
+                convert(j + jj, xr[jj % XR], O);
+                phase_fence();
+                xload(tt, j + jj + XR, xr[jj % XR]);
+                phase_fence();
+#pragma unroll
+                for (int i = 0; i < T; ++i) {
+                    const int ul = jj * T + i;
+                    const int s = ul % P;
+                    compute(i, j + jj, rlo[s], rhi[s], O);
+                    const int un = ul + P;
+                    phase_fence();
+                    wload(j + un / T, un % T, rlo[s], rhi[s]);
+                    phase_fence();
+                }
+            }
+        }
+        // an odd last pair: its activations sit in slot 0 and its units in slots 0 .. T - 1
+        // (j T is a multiple of P); nothing is loaded after them
+        if (j < np) {
+            XOp O;
+            convert(j, xr[0], O);
+#pragma unroll
+            for (int i = 0; i < T; ++i) compute(i, j, rlo[i % P], rhi[i % P], O);
+        }
+
+        // ---- partial sums of the W waves, in wave order ----
         __syncthreads();
         for (int e = tid; e < T * kWave; e += W * kWave) {
-            floatx4_t v = red[e];
+            float4 v = red[e];
             for (int ww = 1; ww < W; ++ww) {
-                const floatx4_t o = red[ww * T * kWave + e];
-                v[0] += o[0]; v[1] += o[1]; v[2] += o[2]; v[3] += o[3];
+                const float4 o = red[ww * T * kWave + e];
+                v.x += o.x;
+                v.y += o.y;
+                v.z += o.z;
+                v.w += o.w;
             }
             const int i = e / kWave, l = e % kWave;
-            const int row = r0 + 16 * i + (l & 15);
-            if (row < r1) {
-                const float bv = bias ? bf16_to_f32(bias[row]) : 0.0f;
+            const int row = 16 * i + (l & 15);
+            if (row < R) {
+                const int gr = r0 + row;
+                const float bv = bias ? bf16_to_f32(bias[gr]) : 0.0f;
+                const float vv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int token = tt * kTokTile + 4 * (l >> 4) + r;
-                    if (token < M) store_out(y, static_cast<int64_t>(token) * ldy + row, v[r] + bv,
-                                             out_f32 != 0);
+                    if (token < M)
+                        store_out(y, static_cast<int64_t>(token) * ldy + gr, vv[r] + bv,
+                                  out_f32 != 0);
                 }
             }
         }
@@ -304,113 +431,133 @@ __global__ void __launch_bounds__(kMaxWaves * kWave) gemv_mfma_kernel(
     // the ring's last loads (zeros, out of range) have no memory traffic; nothing else is pending
 }
 
-template <int T, int P, bool ZP>
-hipError_t launch_t(const uint8_t *qweight, const uint16_t *scales, const uint16_t *zeros,
-                    const uint16_t *bias, const uint4 *frag, const int *expo, const float *xsum,
-                    int d_out, int row_bytes, int n_groups, int group_shift, int C, int M, int TT,
-                    int rows_per_block, int blocks, int W, void *y, int64_t ldy, bool out_f32,
-                    hipStream_t stream) {
-    const size_t lds = static_cast<size_t>(W) * T * kWave * sizeof(floatx4_t);
-    hipLaunchKernelGGL((gemv_mfma_kernel<T, P, ZP>), dim3(blocks), dim3(W * kWave), lds, stream,
-                       qweight, scales, zeros, bias, frag, expo, xsum, d_out, row_bytes, n_groups,
-                       group_shift, C, M, TT, rows_per_block, y, ldy, out_f32 ? 1 : 0);
-    return hipGetLastError();
-}
+struct TokPlan {
+    int blocks, rows_per_block, T, W;
+    bool ok;
+};
 
-template <bool ZP>
-hipError_t launch_zp(int T, const uint8_t *qweight, const uint16_t *scales, const uint16_t *zeros,
-                     const uint16_t *bias, const uint4 *frag, const int *expo, const float *xsum,
-                     int d_out, int row_bytes, int n_groups, int group_shift, int C, int M,
-                     int TT, int rows_per_block, int blocks, int W, void *y, int64_t ldy,
-                     bool out_f32, hipStream_t stream) {
-#define W4_MFMA_CASE(TV, PV)                                                                     \
-    case TV:                                                                                     \
-        return launch_t<TV, PV, ZP>(qweight, scales, zeros, bias, frag, expo, xsum, d_out,     \
-                                    row_bytes, n_groups, group_shift, C, M, TT, rows_per_block, \
-                                    blocks, W, y, ldy, out_f32, stream);
-    switch (T) {
-        W4_MFMA_CASE(1, 4)
-        W4_MFMA_CASE(2, 4)
-        W4_MFMA_CASE(3, 2)
-        W4_MFMA_CASE(4, 2)
-        W4_MFMA_CASE(6, 2)
-        default: return hipErrorInvalidValue;
-    }
-#undef W4_MFMA_CASE
-}
+constexpr int kTokTiles[] = {1, 2, 3, 4, 5, 6, 8, 10, 12};
+constexpr int kTokMaxT = 12;
 
-// Tiles per block are rounded up to an instantiated count.
-constexpr int kMaxTiles = 6;
-int round_tiles(int t) {
-    static const int kT[] = {1, 2, 3, 4, 6};
-    for (int v : kT)
+int round_tok_tiles(int t) {
+    for (int v : kTokTiles)
         if (t <= v) return v;
     return 0;
 }
 
-}  // namespace
-
-bool gemv_mfma_supported(int64_t M, int64_t d_out, int64_t k_pad, int64_t span, int64_t n_groups) {
-    if (M < 2 || M > 64) return false;
-    // a group must cover whole 128-column chunks (128 or 256), or be the whole row
-    if (n_groups != 1 && span != 128 && span != 256) return false;
-    // 32-bit offsets within a block's rows
-    (void)d_out;
-    return int64_t(kMaxTiles * 16) * (k_pad / 2) < (int64_t(1) << 31);
+// Rows: one slice per compute unit (more slices when one would exceed the tile cap or the LDS);
+// waves: the row's pairs split evenly (the most waves within 5% of an even split, else the best).
+TokPlan plan_tok(int64_t d_out, int64_t k_pad, int64_t n_groups, bool zp) {
+    TokPlan p{};
+    const int64_t cus = device_cu_count();
+    const int64_t C = (k_pad + 127) / 128;
+    const int64_t npairs = (C + 1) / 2;
+    int W = 1;
+    if (npairs <= kTokMaxWaves) {
+        W = static_cast<int>(npairs);
+    } else {
+        double best = 1e30;
+        for (int cand = kTokMaxWaves; cand >= 4; --cand) {
+            const double waste = static_cast<double>((npairs + cand - 1) / cand) * cand / npairs;
+            if (waste <= 1.05) {
+                W = cand;
+                break;
+            }
+            if (waste < best) {
+                best = waste;
+                W = cand;
+            }
+        }
+    }
+    for (int64_t split = 1; split <= 64; split *= 2) {
+        const int64_t blocks_target = cus * split;
+        int64_t rpb = (d_out + blocks_target - 1) / blocks_target;
+        if (rpb < 1) rpb = 1;
+        const int T = round_tok_tiles(static_cast<int>((rpb + 15) / 16));
+        if (T == 0 || T > kTokMaxT) continue;
+        if (tok_lds(T, static_cast<int>(n_groups), W, zp).total > kTokLdsLimit) continue;
+        p.rows_per_block = static_cast<int>(rpb);
+        p.blocks = static_cast<int>((d_out + rpb - 1) / rpb);
+        p.T = T;
+        p.W = W;
+        p.ok = true;
+        return p;
+    }
+    p.ok = false;
+    return p;
 }
 
-size_t gemv_mfma_workspace_bytes(int64_t M, int64_t k_pad) {
-    return static_cast<size_t>(ws_layout(M, k_pad).total);
+template <int T, bool ZP>
+hipError_t launch_tok_t(const TokPlan &p, const uint16_t *x, int64_t ldx, int64_t M, int64_t d_in,
+                        const uint8_t *qweight, const uint16_t *scales, const uint16_t *zeros,
+                        const uint16_t *bias, int64_t d_out, int64_t k_pad, int64_t n_groups,
+                        int gshift, void *y, int64_t ldy, bool out_f32, hipStream_t stream) {
+    const size_t lds = tok_lds(T, static_cast<int>(n_groups), p.W, ZP).total;
+    const int C = static_cast<int>((k_pad + 127) / 128);
+    hipLaunchKernelGGL((gemv_tok_kernel<T, ZP>), dim3(p.blocks), dim3(p.W * kWave), lds, stream, x,
+                       ldx, static_cast<int>(M), static_cast<int>(d_in), qweight, scales, zeros,
+                       bias, static_cast<int>(d_out), static_cast<int>(k_pad / 2),
+                       static_cast<int>(n_groups), gshift, C, p.rows_per_block, y, ldy,
+                       out_f32 ? 1 : 0);
+    return hipGetLastError();
+}
+
+template <bool ZP>
+hipError_t launch_tok_zp(const TokPlan &p, const uint16_t *x, int64_t ldx, int64_t M, int64_t d_in,
+                         const uint8_t *qweight, const uint16_t *scales, const uint16_t *zeros,
+                         const uint16_t *bias, int64_t d_out, int64_t k_pad, int64_t n_groups,
+                         int gshift, void *y, int64_t ldy, bool out_f32, hipStream_t stream) {
+#define W4_TOK_CASE(TV)                                                                          \
+    case TV:                                                                                     \
+        return launch_tok_t<TV, ZP>(p, x, ldx, M, d_in, qweight, scales, zeros, bias, d_out,    \
+                                    k_pad, n_groups, gshift, y, ldy, out_f32, stream);
+    switch (p.T) {
+        W4_TOK_CASE(1)
+        W4_TOK_CASE(2)
+        W4_TOK_CASE(3)
+        W4_TOK_CASE(4)
+        W4_TOK_CASE(5)
+        W4_TOK_CASE(6)
+        W4_TOK_CASE(8)
+        W4_TOK_CASE(10)
+        W4_TOK_CASE(12)
+        default:
+            return hipErrorInvalidValue;
+    }
+#undef W4_TOK_CASE
+}
+
+}  // namespace
+
+bool gemv_mfma_supported(int64_t M, int64_t d_out, int64_t d_in, int64_t k_pad, int64_t span,
+                         int64_t n_groups, int64_t ldx, bool zp) {
+    if (M < 2 || M > 64 || d_out < 1 || d_in < 1) return false;
+    // a group must cover whole 128-column chunks (128 or 256), or be the whole row
+    if (n_groups != 1 && span != 128 && span != 256) return false;
+    if (d_in > k_pad || k_pad % 32 != 0) return false;
+    const TokPlan p = plan_tok(d_out, k_pad, n_groups, zp);
+    if (!p.ok) return false;
+    // 31-bit offsets: the weight rows of a block's tiles (plus a pair past the row), and the
+    // activations of every token
+    const int64_t C = (k_pad + 127) / 128;
+    if (int64_t(16) * p.T * (k_pad / 2) + 128 * (C + 2) >= (int64_t)kOutOfRange) return false;
+    return (M * ldx + 1024) * 2 < (int64_t)kTokNoToken;
 }
 
 hipError_t launch_gemv_mfma(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
                             const uint16_t *scales, const uint16_t *zeros, const uint16_t *bias,
                             int64_t d_out, int64_t d_in, int64_t k_pad, int64_t span,
-                            int64_t n_groups, void *y, int64_t ldy, bool out_f32, void *workspace,
+                            int64_t n_groups, void *y, int64_t ldy, bool out_f32,
                             hipStream_t stream) {
-    const WsLayout WL = ws_layout(M, k_pad);
-    char *ws = static_cast<char *>(workspace);
-    uint4 *frag = reinterpret_cast<uint4 *>(ws + WL.frag);
-    int *expo = reinterpret_cast<int *>(ws + WL.expo);
-    float *xsum = reinterpret_cast<float *>(ws + WL.xsum);
-    const int C = static_cast<int>((k_pad + kChunk - 1) / kChunk);
-    const int TT = static_cast<int>((M + kTokTile - 1) / kTokTile);
-    hipLaunchKernelGGL(xprep_kernel, dim3(C, TT), dim3(kPrepThreads), 0, stream, x,
-                       static_cast<int>(M), ldx, static_cast<int>(d_in), C, frag, expo, xsum);
-    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-
-    // rows: one slice per compute unit with up to 8 waves; a slice of more than kMaxTiles tiles
-    // is cut in two blocks of up to 4 waves each (registers bound the tiles per wave)
-    const int cus = device_cu_count();
-    int rows_per_block = static_cast<int>((d_out + cus - 1) / cus);
-    int max_waves = kMaxWaves;
-    if (rows_per_block > kMaxTiles * 16) {
-        rows_per_block = static_cast<int>((d_out + 2 * cus - 1) / (2 * cus));
-        if (rows_per_block > kMaxTiles * 16) rows_per_block = kMaxTiles * 16;
-        max_waves = kMaxWaves / 2;
-    }
-    const int blocks = static_cast<int>((d_out + rows_per_block - 1) / rows_per_block);
-    const int T = round_tiles((rows_per_block + 15) / 16);
-    // waves: split the chunks evenly (largest W within 5% of an even split, else the best one)
-    int W = 1;
-    double best = 1e30;
-    for (int cand = max_waves; cand >= 1; --cand) {
-        if (cand > C) continue;
-        const double waste = static_cast<double>((C + cand - 1) / cand) * cand / C;
-        if (waste <= 1.05) { W = cand; break; }
-        if (waste < best) { best = waste; W = cand; }
-    }
-    const int group_shift = n_groups == 1 ? 30 : (span == 256 ? 1 : 0);
-    const int row_bytes = static_cast<int>(k_pad / 2);
-    if (zeros)
-        return launch_zp<true>(T, qweight, scales, zeros, bias, frag, expo, xsum,
-                               static_cast<int>(d_out), row_bytes, static_cast<int>(n_groups),
-                               group_shift, C, static_cast<int>(M), TT, rows_per_block, blocks, W,
-                               y, ldy, out_f32, stream);
-    return launch_zp<false>(T, qweight, scales, zeros, bias, frag, expo, xsum,
-                            static_cast<int>(d_out), row_bytes, static_cast<int>(n_groups),
-                            group_shift, C, static_cast<int>(M), TT, rows_per_block, blocks, W, y,
-                            ldy, out_f32, stream);
+    const bool zp = zeros != nullptr;
+    const TokPlan p = plan_tok(d_out, k_pad, n_groups, zp);
+    if (!p.ok) return hipErrorInvalidValue;
+    const int gshift = n_groups == 1 ? 30 : (span == 256 ? 1 : 0);
+    if (zp)
+        return launch_tok_zp<true>(p, x, ldx, M, d_in, qweight, scales, zeros, bias, d_out, k_pad,
+                                   n_groups, gshift, y, ldy, out_f32, stream);
+    return launch_tok_zp<false>(p, x, ldx, M, d_in, qweight, scales, zeros, bias, d_out, k_pad,
+                                n_groups, gshift, y, ldy, out_f32, stream);
 }
 
 }  // namespace w4

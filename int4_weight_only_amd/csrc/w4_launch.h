@@ -14,15 +14,11 @@ hipError_t launch_pack(const float *w, int64_t d_out, int64_t d_in, int64_t ldw,
 hipError_t launch_act_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int8_t *q,
                             int64_t ldq, float *s_x, int32_t *q_sum, hipStream_t stream);
 
-// Decode W4A16 for 1 <= M <= 64.  `workspace` holds at least gemv_workspace_bytes(...) bytes
-// (16-byte aligned; may be null when that is 0).
-size_t gemv_workspace_bytes(int64_t M, int64_t d_out, int64_t k_pad, int64_t span,
-                            int64_t n_groups);
+// Decode W4A16 for 1 <= M <= 64 (no scratch memory).
 hipError_t launch_gemv(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
                        const uint16_t *scales, const uint16_t *zeros, const uint16_t *bias,
                        int64_t d_out, int64_t d_in, int64_t k_pad, int64_t span,
-                       int64_t n_groups, void *y, int64_t ldy, bool out_f32, void *workspace,
-                       hipStream_t stream);
+                       int64_t n_groups, void *y, int64_t ldy, bool out_f32, hipStream_t stream);
 
 hipError_t launch_w4a8(const int8_t *q, const float *s_x, int64_t M, int64_t ldq,
                        const uint8_t *qweight, const uint16_t *s_w, const uint16_t *bias,
@@ -47,14 +43,14 @@ hipError_t launch_w4a8_stream(const int8_t *q, const float *s_x, int64_t M, int6
                               int64_t d_out, int64_t d_in, int64_t k_pad, void *y, int64_t ldy,
                               bool out_f32, int32_t *acc, hipStream_t stream);
 
-// Few-token decode on the fp16 matrix cores (decode_mfma.hip): activations prepared once into
-// a workspace, then one pass over the weights for all tokens.
-bool gemv_mfma_supported(int64_t M, int64_t d_out, int64_t k_pad, int64_t span, int64_t n_groups);
-size_t gemv_mfma_workspace_bytes(int64_t M, int64_t k_pad);
+// Few-token decode on the fp16 matrix cores (decode_mfma.hip): activations converted inside
+// each block, one pass over the weights for all tokens of a 16-token tile; no workspace.
+bool gemv_mfma_supported(int64_t M, int64_t d_out, int64_t d_in, int64_t k_pad, int64_t span,
+                         int64_t n_groups, int64_t ldx, bool zp);
 hipError_t launch_gemv_mfma(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
                             const uint16_t *scales, const uint16_t *zeros, const uint16_t *bias,
                             int64_t d_out, int64_t d_in, int64_t k_pad, int64_t span,
-                            int64_t n_groups, void *y, int64_t ldy, bool out_f32, void *workspace,
+                            int64_t n_groups, void *y, int64_t ldy, bool out_f32,
                             hipStream_t stream);
 
 // One to four tokens on the int8 matrix cores (decode_i8.hip): activations as exact integer

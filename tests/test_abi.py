@@ -13,7 +13,7 @@ HEADER = os.path.join(ROOT, "include", "w4.h")
 LIB = os.path.join(ROOT, "int4_weight_only_amd", "libw4.so")
 
 W4_OK, W4_ERR_NULL, W4_ERR_SHAPE, W4_ERR_GROUP, W4_ERR_ALIGN, W4_ERR_RANGE = 0, 1, 2, 3, 4, 5
-W4_ERR_UNSUPPORTED, W4_ERR_HIP, W4_ERR_WORKSPACE = 6, 7, 8
+W4_ERR_UNSUPPORTED, W4_ERR_HIP = 6, 7
 
 
 def declared_functions():
@@ -32,10 +32,8 @@ def lib():
                                    ctypes.POINTER(ctypes.c_size_t)]
     L.w4_pack.argtypes = [p, i64, i64, i64, i32, i32, p, p, p, p]
     lin = [p, i64, i64, p, p, p, p, i64, i64, i32, p, i64, i32]
-    L.w4_gemv.argtypes = lin + [p, ctypes.c_size_t, p]
+    L.w4_gemv.argtypes = lin + [p]
     L.w4_gemm.argtypes = lin + [p]
-    L.w4_gemv_workspace_bytes.argtypes = [i64, i64, i64, i32]
-    L.w4_gemv_workspace_bytes.restype = ctypes.c_size_t
     L.act_quant_int8.argtypes = [p, i64, i64, i64, p, i64, p, p, p]
     L.w4a8_gemv.argtypes = [p, p, i64, i64, p, p, p, i64, i64, p, i64, i32, p, p]
     L.w4_status_string.restype = ctypes.c_char_p
@@ -46,7 +44,7 @@ def lib():
 def test_header_declares_the_five_entry_points():
     names = declared_functions()
     for n in ("w4_pack", "w4_gemv", "w4_gemm", "act_quant_int8", "w4a8_gemv",
-              "w4_packed_layout", "w4_gemv_workspace_bytes", "w4_status_string",
+              "w4_packed_layout", "w4_status_string",
               "w4_last_hip_error"):
         assert n in names
 
@@ -57,7 +55,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for s in range(9):
+    for s in range(8):
         assert lib.w4_status_string(s)
     assert lib.w4_last_hip_error() == b""
 
@@ -91,12 +89,10 @@ B, C, D, E = 0x20000, 0x30000, 0x40000, 0x50000
 
 def _lin(fn, **kw):
     a = dict(x=A, M=1, ldx=256, qw=B, sc=C, zr=None, bias=None, d_out=128, d_in=256, g=32, y=D,
-             ldy=128, out=0, ws=None, ws_bytes=0)
+             ldy=128, out=0)
     a.update(kw)
     args = [a["x"], a["M"], a["ldx"], a["qw"], a["sc"], a["zr"], a["bias"], a["d_out"],
             a["d_in"], a["g"], a["y"], a["ldy"], a["out"]]
-    if fn.__name__ == "w4_gemv":
-        args += [a["ws"], a["ws_bytes"]]
     return fn(*args, None)
 
 
@@ -128,30 +124,6 @@ def test_gemv_token_limit(lib):
     # M > 64 belongs to the prefill path
     assert _lin(lib.w4_gemv, M=65) == W4_ERR_UNSUPPORTED
     assert _lin(lib.w4_gemv, d_in=65544, ldx=65544) == W4_ERR_RANGE
-
-
-def test_gemv_workspace_query(lib):
-    """Matrix-core decode (M >= 2, groups of 128, 256 or one per row) needs a workspace of
-    4096 + 128 bytes per 128-column chunk per 16-token tile; the other paths need none."""
-    q = lib.w4_gemv_workspace_bytes
-    per = lambda M, k_pad: ((M + 15) // 16) * ((k_pad + 127) // 128) * (4096 + 128)
-    assert q(16, 37888, 3584, 128) == per(16, 3584)
-    assert q(8, 3584, 18944, 128) == per(8, 18944)
-    assert q(17, 3584, 3600, 128) == per(17, 3712)
-    assert q(2, 128, 256, 256) == per(2, 256)
-    assert q(64, 100, 70, 0) == per(64, 96)
-    assert q(1, 37888, 3584, 128) == 0      # one token: the streaming kernel
-    assert q(16, 128, 256, 32) == 0         # 32-column groups: the per-row kernels
-    assert q(16, 128, 256, 64) == 0
-    assert q(65, 128, 256, 128) == 0        # invalid arguments
-    assert q(16, 128, 70000, 128) == 0
-
-
-def test_gemv_requires_its_workspace(lib):
-    need = lib.w4_gemv_workspace_bytes(16, 128, 256, 128)
-    assert _lin(lib.w4_gemv, M=16, g=128) == W4_ERR_WORKSPACE
-    assert _lin(lib.w4_gemv, M=16, g=128, ws=E, ws_bytes=need - 1) == W4_ERR_WORKSPACE
-    assert _lin(lib.w4_gemv, M=16, g=128, ws=E + 8, ws_bytes=need) == W4_ERR_ALIGN
 
 
 def test_pack_rejects_bad_arguments(lib):

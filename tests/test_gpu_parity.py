@@ -307,6 +307,32 @@ def test_gemm_matches_gemv_small_m():
 
 
 @pytest.mark.parametrize("entry", ["w4_gemv", "w4_gemm"])
+def test_linear_zero_points_beyond_pack(entry, monkeypatch):
+    """Zero points that w4_pack never writes (non-integers, beyond the code range, negative,
+    large) still follow w = s (c - z): every decode kernel (forced where one token would pick
+    another) and the GEMM against the oracle, which takes z as given."""
+    d_out, d_in, g = 300, 1000, 128
+    w = workloads.weight(29, 0, d_out, d_in)
+    ph, pd = check_pack_bit_exact(w, g, ASYM, "zero points beyond pack")
+    rng = np.random.default_rng(29)
+    zf = rng.choice(np.array([0.5, 7.25, -3.0, 20.0, 300.0, -1000.0, 7.0, 15.0], np.float32),
+                    size=ph[2].shape)
+    zb = workloads.to_bf16_bits(zf)
+    ph2 = (ph[0], ph[1], zb)
+    pd2 = (pd[0], pd[1], dev_bf16(zb))
+    b = workloads.bias(29, 1, d_out)
+    paths = (None, "i8", "stream") if entry == "w4_gemv" else (None,)
+    for path in paths:
+        if path is None:
+            monkeypatch.delenv("W4_GEMV_PATH", raising=False)
+        else:
+            monkeypatch.setenv("W4_GEMV_PATH", path)
+        for M in (1, 2, 5, 16):
+            x = workloads.activations(29, M, M, d_in)
+            check_linear(entry, x, ph2, pd2, b, d_in, g, f"z beyond pack M={M} path={path}")
+
+
+@pytest.mark.parametrize("entry", ["w4_gemv", "w4_gemm"])
 def test_linear_deterministic(entry):
     d_out, d_in, g = 1000, 3584, 128
     w = workloads.weight(28, 0, d_out, d_in)
