@@ -22,7 +22,8 @@
 //     integers (c - z) with the magic-number form ((w & 0x000F000F) | 0x64006400 = (1024 + c0,
 //     1024 + c4), one packed fp16 add or fma removes 1024 + z), and four MFMAs multiply them with
 //     the activation operand;
-//   * the chunk's fp32 result is scaled by s[row][group] 2^e[token] and accumulated in fp32.
+//   * the chunks' fp32 results are scaled by s[row][group], added, scaled by 2^e[token] and
+//     accumulated in fp32.
 // A block's scales (and zero points, as the two fp16 pair constants the dequantization uses)
 // are read once, coalesced, into an LDS table. The waves' partial sums meet in LDS and are added
 // in wave order (deterministic).
@@ -51,7 +52,7 @@ constexpr uint32_t kTokLdsLimit = 160 * 1024;
 // still below 2^32 with bit 31 added.
 constexpr uint32_t kTokNoToken = 0x40000000u;
 
-// LDS layout (bytes): table [16 T rows][n_groups] entries -- symmetric: the fp32 scale; with zero
+// LDS layout (bytes): table [16 T rows][n_groups | 1] entries -- symmetric: the fp32 scale; with zero
 // points: {fp32 scale, fp16 pair -(1024 + zi), fp16 pair -(64 + zi), fp32 residual z - zi}
 // (rows past the slice are never written: only lanes whose results are dropped read them); red
 // [W][T][64] fp32 x 4 partial sums; flags [W] (a wave's rows hold a non-integer zero point).
@@ -61,10 +62,14 @@ struct TokLds {
 
 __host__ __device__ inline uint32_t tok_align16(uint32_t v) { return (v + 15u) & ~15u; }
 
+// Table rows are n_groups | 1 entries apart: with an odd stride the 16 rows a ds_read of one
+// tile touches fall into different LDS banks (with n_groups = 28 they fell into two).
+__host__ __device__ inline int tok_table_stride(int n_groups) { return n_groups | 1; }
+
 __host__ __device__ inline TokLds tok_lds(int T, int n_groups, int W, bool zp) {
     TokLds L;
     L.table = 0;
-    L.red = tok_align16(16u * T * n_groups * (zp ? 16u : 4u));
+    L.red = tok_align16(16u * T * tok_table_stride(n_groups) * (zp ? 16u : 4u));
     L.flags = L.red + static_cast<uint32_t>(W) * T * kWave * 16u;
     L.total = L.flags + 16u * 4u;
     return L;
@@ -210,7 +215,9 @@ __global__ void __launch_bounds__(kTokThreads) gemv_tok_kernel(
         const uint16_t *sp = scales + (int64_t)r0 * n_groups;
         const uint16_t *zp = ZP ? zeros + (int64_t)r0 * n_groups : nullptr;
         int frac = 0;
+        const int ts = tok_table_stride(n_groups);
         for (int e = tid; e < nent; e += blockDim.x) {
+            const int te = (e / n_groups) * ts + e % n_groups;  // its slot in the table
             const float s = bf16_to_f32(sp[e]);
             if (ZP) {
                 const float z = bf16_to_f32(zp[e]);
@@ -223,9 +230,9 @@ __global__ void __launch_bounds__(kTokThreads) gemv_tok_kernel(
                     __builtin_bit_cast(uint16_t, static_cast<_Float16>(-(64.0f + zi)));
                 const u32x4_t ent = {__float_as_uint(s), hl | (hl << 16), hh | (hh << 16),
                                      __float_as_uint(zr)};
-                *reinterpret_cast<u32x4_t *>(lds + L.table + 16u * e) = ent;
+                *reinterpret_cast<u32x4_t *>(lds + L.table + 16u * te) = ent;
             } else {
-                *reinterpret_cast<float *>(lds + L.table + 4u * e) = s;
+                *reinterpret_cast<float *>(lds + L.table + 4u * te) = s;
             }
         }
         if (ZP) {
@@ -317,7 +324,8 @@ __global__ void __launch_bounds__(kTokThreads) gemv_tok_kernel(
         }
     };
 
-    const uint32_t t_lane = static_cast<uint32_t>(n) * n_groups;  // table row of lane's row n
+    const int ts = tok_table_stride(n_groups);
+    const uint32_t t_lane = static_cast<uint32_t>(n) * ts;  // table row of lane's row n
     auto compute = [&](int i, int j, const u32x4_t &wlo, const u32x4_t &whi, const XOp &O) {
         // every LDS read first (sums, both table entries), then the two chunks' MFMA chains
         // interleaved: they are independent, so neither waits for the other's results
@@ -330,7 +338,7 @@ __global__ void __launch_bounds__(kTokThreads) gemv_tok_kernel(
         for (int h = 0; h < 2; ++h) {
             int G = (2 * (p0 + j) + h) >> gshift;
             G = G < n_groups ? G : n_groups - 1;  // past the last chunk: x is zero there
-            const uint32_t e = t_lane + uni(static_cast<uint32_t>(16 * i * n_groups + G));
+            const uint32_t e = t_lane + uni(static_cast<uint32_t>(16 * i * ts + G));
             if (ZP) {
                 const u32x4_t ent = *reinterpret_cast<const u32x4_t *>(lds + L.table + 16u * e);
                 sc[h] = __uint_as_float(ent.x);
@@ -351,15 +359,17 @@ __global__ void __launch_bounds__(kTokThreads) gemv_tok_kernel(
                                                               dequant8(wd, zlo[h], zhi[h]), d[h],
                                                               0, 0, 0);
             }
+        // sum = s0 d0 + s1 d1 per token, then acc += 2^e sum
         float acc[4] = {a4.x, a4.y, a4.z, a4.w};
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float v = d[h][r];
-                if (ZP && frac_any) v = fmaf(-zr[h], O.sx[h][r], v);
-                acc[r] = fmaf(sc[h] * O.p[r], v, acc[r]);
+        for (int r = 0; r < 4; ++r) {
+            float v0 = d[0][r], v1 = d[1][r];
+            if (ZP && frac_any) {
+                v0 = fmaf(-zr[0], O.sx[0][r], v0);
+                v1 = fmaf(-zr[1], O.sx[1][r], v1);
             }
+            acc[r] = fmaf(O.p[r], fmaf(sc[1], v1, sc[0] * v0), acc[r]);
+        }
         mine[i * kWave] = make_float4(acc[0], acc[1], acc[2], acc[3]);
     };
 
