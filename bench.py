@@ -257,17 +257,23 @@ def bench_c5(torch, w4, workloads, iters):
             for _ in copies:
                 w4.act_quant_int8(x, lin.d_in, with_sum=False)
 
-        gemv_ms_g = graph_ms(torch, gemvs, n_copies, max(1, iters // n_copies))
-        aq_ms_g = graph_ms(torch, quants, n_copies, max(1, iters // n_copies))
-        gemv_ms = gemv_ms_g
-        aq_ms = aq_ms_g
+        def fused():  # the quantization folded into the GEMV (w4a8_linear)
+            for c in copies:
+                w4.w4a8_linear(x, c[0], c[1], b, lin.d_in, out=y)
+
+        gemv_ms = graph_ms(torch, gemvs, n_copies, max(1, iters // n_copies))
+        aq_ms = graph_ms(torch, quants, n_copies, max(1, iters // n_copies))
+        fused_ms = graph_ms(torch, fused, n_copies, max(1, iters // n_copies))
         gb = linear_bytes(1, lin.d_out, lin.d_in, 0, False, bias=True, x_bytes=1) + 4
         aq_bytes = 2 * lin.d_in + lin.d_in + 4
+        fb = linear_bytes(1, lin.d_out, lin.d_in, 0, False, bias=True, x_bytes=2)
         out[f"{lin.d_out}x{lin.d_in}"] = dict(
             gemv_us=round(gemv_ms * 1e3, 2), gemv_gbs=round(gb / gemv_ms / 1e6, 1),
             gemv_hbm_frac=round(gb / gemv_ms / 1e6 / HBM_PEAK_GBS, 4),
             act_quant_us=round(aq_ms * 1e3, 2),
-            path_gbs=round((gb + aq_bytes) / (gemv_ms + aq_ms) / 1e6, 1))
+            path_gbs=round((gb + aq_bytes) / (gemv_ms + aq_ms) / 1e6, 1),
+            fused_us=round(fused_ms * 1e3, 2), fused_gbs=round(fb / fused_ms / 1e6, 1),
+            fused_hbm_frac=round(fb / fused_ms / 1e6 / HBM_PEAK_GBS, 4))
         del copies, base
     return out
 

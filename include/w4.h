@@ -150,6 +150,23 @@ int w4a8_gemv(const int8_t *q, const float *s_x, int64_t M, int64_t ldq, const u
               const uint16_t *s_w, const uint16_t *bias, int64_t d_out, int64_t d_in, void *y,
               int64_t ldy, int out_dtype, int32_t *acc, void *stream);
 
+/*
+ * w4a8_linear -- the W4A8 decode linear with the activation quantization folded in: the result
+ * of act_quant_int8 followed by w4a8_gemv, in one launch, without q in memory.
+ * [Orin 从 FP 线性层到 INT4 DP4A 的数学推导] (s_x = max|x|/127, q = clamp(rint(x/s_x), +-127)),
+ * [Orin INT32 accumulator 是否安全], and the kernel boundary that the W4A8 activation quantization
+ * adds as a separate launch [Orin 模型尺寸和 decode 的真实瓶颈].
+ *   x        bf16 [M][ldx], ldx >= d_in, ldx % 8 == 0, 16-byte aligned; only k < d_in is used
+ *   qweight, s_w, bias, y, out_dtype, acc: as for w4a8_gemv
+ *   s_x      fp32 [M] or NULL: receives the token scales
+ * The codes, s_x and acc are bit-identical to those of act_quant_int8 + w4a8_gemv on the same x.
+ * Every workgroup quantizes the whole activation row it needs; rows longer than the kernel's LDS
+ * stage (about 43,000 columns for one token) return W4_ERR_UNSUPPORTED: use the two calls.
+ */
+int w4a8_linear(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
+                const uint16_t *s_w, const uint16_t *bias, int64_t d_out, int64_t d_in, void *y,
+                int64_t ldy, int out_dtype, float *s_x, int32_t *acc, void *stream);
+
 /* Text for a w4_status value (static storage). */
 const char *w4_status_string(int status);
 

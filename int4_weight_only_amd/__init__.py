@@ -16,7 +16,8 @@ import torch
 
 __all__ = [
     "W4_SYM", "W4_ASYM", "W4_OUT_BF16", "W4_OUT_F32", "W4Error", "packed_layout", "w4_pack",
-    "w4_gemv", "w4_gemm", "act_quant_int8", "w4a8_gemv", "w4_linear", "library_path",
+    "w4_gemv", "w4_gemm", "act_quant_int8", "w4a8_gemv", "w4a8_linear", "w4_linear",
+    "library_path",
 ]
 
 W4_SYM, W4_ASYM = 0, 1
@@ -48,8 +49,9 @@ def _load():
     lib.w4_gemm.argtypes = lin + [p]
     lib.act_quant_int8.argtypes = [p, i64, i64, i64, p, i64, p, p, p]
     lib.w4a8_gemv.argtypes = [p, p, i64, i64, p, p, p, i64, i64, p, i64, i32, p, p]
+    lib.w4a8_linear.argtypes = [p, i64, i64, p, p, p, i64, i64, p, i64, i32, p, p, p]
     for f in ("w4_packed_layout", "w4_pack", "w4_gemv", "w4_gemm", "act_quant_int8",
-              "w4a8_gemv"):
+              "w4a8_gemv", "w4a8_linear"):
         getattr(lib, f).restype = i32
     lib.w4_status_string.argtypes = [i32]
     lib.w4_status_string.restype = ctypes.c_char_p
@@ -216,3 +218,38 @@ def w4a8_gemv(q, s_x, qweight, s_w, bias, d_in, out_dtype=W4_OUT_BF16, want_acc=
                                        _ptr(s_w), _ptr(bias), d_out, d_in, _ptr(out),
                                        out.stride(0), out_dtype, _ptr(acc), _stream(dev)))
     return (out, acc) if want_acc else out
+
+
+def w4a8_linear(x, qweight, s_w, bias, d_in, out_dtype=W4_OUT_BF16, want_acc=False,
+                want_scales=False, out=None):
+    """W4A8 decode linear on bf16 activations, quantized per token inside the kernel (the result
+    of act_quant_int8 + w4a8_gemv in one launch).  Returns y, then acc int32 [M][d_out] if
+    want_acc, then s_x fp32 [M] if want_scales."""
+    _need(x, "x", torch.bfloat16, dim=2)
+    dev = x.device
+    _need(qweight, "qweight", torch.uint8, dev, 2)
+    s_w = s_w.reshape(-1)
+    _need(s_w, "s_w", torch.bfloat16, dev, 1)
+    if bias is not None:
+        _need(bias, "bias", torch.bfloat16, dev, 1)
+    M = x.shape[0]
+    d_out = qweight.shape[0]
+    k_pad, _, _ = packed_layout(d_out, d_in, 0)
+    if tuple(qweight.shape) != (d_out, k_pad // 2) or not qweight.is_contiguous():
+        raise ValueError(f"qweight must be contiguous [{d_out}][{k_pad // 2}]")
+    if s_w.shape[0] != d_out or (bias is not None and bias.shape[0] != d_out):
+        raise ValueError(f"s_w and bias must have {d_out} elements")
+    if x.shape[1] < d_in:
+        raise ValueError(f"x has {x.shape[1]} columns, fewer than d_in={d_in}")
+    tdtype = torch.float32 if out_dtype == W4_OUT_F32 else torch.bfloat16
+    if out is None:
+        out = torch.empty((M, d_out), dtype=tdtype, device=dev)
+    else:
+        _need(out, "out", tdtype, dev, 2)
+    acc = torch.empty((M, d_out), dtype=torch.int32, device=dev) if want_acc else None
+    s_x = torch.empty(M, dtype=torch.float32, device=dev) if want_scales else None
+    _check("w4a8_linear", _lib.w4a8_linear(_ptr(x), M, x.stride(0), _ptr(qweight), _ptr(s_w),
+                                           _ptr(bias), d_out, d_in, _ptr(out), out.stride(0),
+                                           out_dtype, _ptr(s_x), _ptr(acc), _stream(dev)))
+    res = (out,) + ((acc,) if want_acc else ()) + ((s_x,) if want_scales else ())
+    return res if len(res) > 1 else out

@@ -6,6 +6,7 @@
 // Both kernels produce integers and bit patterns, so every fp32 step is one IEEE operation in a
 // fixed order (correctly rounded division, round-to-nearest-even, no contraction).
 #include "w4_device.h"
+#include "w4_quant.h"
 #include "w4_launch.h"
 
 namespace w4 {
@@ -114,7 +115,7 @@ __device__ __forceinline__ float chunk_absmax(const uint4 &v, int64_t col, int64
 
 // Quantizes the chunk at `col` and stores the codes of its columns < K; returns their sum.
 __device__ __forceinline__ int chunk_quantize(const uint4 &v, int64_t col, int64_t K, float a,
-                                              float s, int8_t *__restrict__ qr) {
+                                              float s, float r, int8_t *__restrict__ qr) {
 #pragma clang fp contract(off)
     const uint32_t u[4] = {v.x, v.y, v.z, v.w};
     int qi[8];
@@ -122,11 +123,8 @@ __device__ __forceinline__ int chunk_quantize(const uint4 &v, int64_t col, int64
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const uint32_t bits = (e & 1) ? (u[e >> 1] >> 16) : (u[e >> 1] & 0xFFFFu);
-        float t = bf16_to_f32(bits) / s;  // one correctly rounded fp32 division
-        t = __builtin_rintf(t);
-        t = fmaxf(t, -127.0f);
-        t = fminf(t, 127.0f);
-        qi[e] = (a != 0.0f && col + e < K) ? static_cast<int>(t) : 0;
+        const int t = quantize_int8_fast(bf16_to_f32(bits), s, r);
+        qi[e] = (a != 0.0f && col + e < K) ? t : 0;
         sum += qi[e];
     }
     if (col + 8 <= K) {
@@ -182,16 +180,17 @@ __global__ void __launch_bounds__(kAqThreads) act_quant_kernel(const uint16_t *_
 #pragma unroll
     for (int w = 1; w < kWaves; ++w) a = fmaxf(a, red_f[w]);
 
-    const float s = a / 127.0f;
+    const float s = token_scale_int8(a);
+    const float r = 1.0f / s;  // correctly rounded; quantize_int8_fast needs it
     int sum = 0;
 #pragma unroll
     for (int i = 0; i < kAqCache; ++i) {
         const int64_t c = tid + static_cast<int64_t>(i) * kAqThreads;
-        if (c < n_chunks) sum += chunk_quantize(cache[i], 8 * c, K, a, s, qr);
+        if (c < n_chunks) sum += chunk_quantize(cache[i], 8 * c, K, a, s, r, qr);
     }
     for (int64_t c = tid + static_cast<int64_t>(kAqCache) * kAqThreads; c < n_chunks;
          c += kAqThreads)
-        sum += chunk_quantize(*reinterpret_cast<const uint4 *>(xr + 8 * c), 8 * c, K, a, s, qr);
+        sum += chunk_quantize(*reinterpret_cast<const uint4 *>(xr + 8 * c), 8 * c, K, a, s, r, qr);
     sum = wave_sum(sum);
     if (lane == 0) red_i[wid] = sum;
     __syncthreads();

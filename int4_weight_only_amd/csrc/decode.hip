@@ -584,9 +584,9 @@ hipError_t launch_w4a8(const int8_t *q, const float *s_x, int64_t M, int64_t ldq
                        const uint8_t *qweight, const uint16_t *s_w, const uint16_t *bias,
                        int64_t d_out, int64_t d_in, int64_t k_pad, void *y, int64_t ldy,
                        bool out_f32, int32_t *acc, hipStream_t stream) {
-    if (w4a8_stream_supported(M, k_pad))  // see launch_gemv
-        return launch_w4a8_stream(q, s_x, M, ldq, qweight, s_w, bias, d_out, d_in, k_pad, y, ldy,
-                                  out_f32, acc, stream);
+    if (w4a8_stream_supported(M, k_pad, false))  // see launch_gemv
+        return launch_w4a8_stream(q, false, const_cast<float *>(s_x), M, ldq, qweight, s_w, bias,
+                                  d_out, d_in, k_pad, y, ldy, out_f32, acc, stream);
     const int64_t cpr = k_pad / kChunkCols;
     const size_t out_elem = out_f32 ? sizeof(float) : sizeof(uint16_t);
     int mt_max = 4;
@@ -621,6 +621,20 @@ hipError_t launch_w4a8(const int8_t *q, const float *s_x, int64_t M, int64_t ldq
         if (err != hipSuccess) return err;
     }
     return hipSuccess;
+}
+
+// The fused path is the streaming kernel only: the per-row fallback kernels take int8 codes.
+bool w4a8_linear_supported(int64_t M, int64_t k_pad) {
+    return w4a8_stream_supported(M, k_pad, true);
+}
+
+hipError_t launch_w4a8_linear(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
+                              const uint16_t *s_w, const uint16_t *bias, int64_t d_out,
+                              int64_t d_in, int64_t k_pad, void *y, int64_t ldy, bool out_f32,
+                              float *s_x, int32_t *acc, hipStream_t stream) {
+    if (!w4a8_linear_supported(M, k_pad)) return hipErrorInvalidValue;
+    return launch_w4a8_stream(x, true, s_x, M, ldx, qweight, s_w, bias, d_out, d_in, k_pad, y,
+                              ldy, out_f32, acc, stream);
 }
 
 }  // namespace w4

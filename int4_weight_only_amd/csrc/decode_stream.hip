@@ -23,6 +23,7 @@
 //     rows-share-one-activation-load idea of [Orin o2-all 和 o4-all 为什么能加速]);
 //   * rows are finished with DPP cross-lane adds, in a fixed order (deterministic).
 #include "w4_device.h"
+#include "w4_quant.h"
 #include "w4_launch.h"
 
 namespace w4 {
@@ -30,6 +31,7 @@ namespace w4 {
 namespace {
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kChunkCols = 32;
 constexpr int kThreads = 256;
@@ -54,6 +56,17 @@ struct alignas(16) XChunk8 {
     int qsum;
     int pad[3];
 };
+
+// Workgroup barrier for LDS-only dependencies, without a memory fence: the caller's LDS accesses
+// are completed first (lgkmcnt(0)), but the weight loads of the ring stay in flight across it (a
+// fenced barrier waits for every outstanding load). The empty asm statements keep the compiler
+// from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited for
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 // Batch shape: RW rows per batch and NB batches in the ring. Measured on MI355X for the 7B
 // shapes (3584 and 18944 columns), one row per batch and two buffers with 2-4 workgroups per CU
@@ -200,7 +213,6 @@ __global__ void __launch_bounds__(BT) gemv_w4a16_stream_kernel(
     // (a wave whose chunks all lie past the end skips the work: a wave-uniform branch that holds
     // no load, so the waits for the activation loads still leave the weight loads in flight)
     const bool ragged = (din & 7) != 0;  // the piece holding column d_in - 1 has columns past it
-    typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
     const half2_t ones = {static_cast<half_t>(1.0f), static_cast<half_t>(1.0f)};
 #pragma unroll
     for (int si = 0; si < SI; ++si) {
@@ -263,7 +275,7 @@ __global__ void __launch_bounds__(BT) gemv_w4a16_stream_kernel(
         zero.pad[0] = zero.pad[1] = 0;
         xsh[(int64_t)threadIdx.x * (cpr + 1) + cpr] = zero;
     }
-    __syncthreads();
+    lds_barrier();  // (the weight loads of the ring stay in flight)
 
     // ---- dequantize inside the dot products ([Lab5 融合INT4反量化与矩阵乘]):
     //   (w & 0x000F000F) | 0x6400_6400 = fp16 (1024 + c0, 1024 + c4), (w & 0x00F000F0) | ... =
@@ -416,14 +428,20 @@ __global__ void __launch_bounds__(BT) gemv_w4a16_stream_kernel(
 // ---------------------------------------------------------------------------------------------
 
 // (segments of long rows and BT threads per workgroup: see the W4A16 kernel)
-template <int MT, int T, int RW, int NB, int SEG, int BT>
+// FQ: the activations arrive as bf16 x ([M][ldq] elements) and are quantized here, token by
+// token, with the rule of act_quant_int8 (w4_quant.h): every workgroup takes the token's maximum
+// over the whole row and quantizes the chunks it stages, so q never goes through memory. The
+// token scales are then written to s_x (if given) by workgroup 0. Otherwise they arrive as int8
+// codes with their scales in s_x.
+template <int MT, int T, int RW, int NB, int SEG, int BT, bool FQ>
 __global__ void __launch_bounds__(BT) gemv_w4a8_stream_kernel(
-    const int8_t *__restrict__ q, int64_t ldq, int M, const float *__restrict__ s_x,
+    const void *__restrict__ act, int64_t ldq, int M, float *__restrict__ s_x,
     const uint8_t *__restrict__ qweight, const uint16_t *__restrict__ s_w,
     const uint16_t *__restrict__ bias, int64_t d_out, int64_t d_in, int64_t k_pad,
     void *__restrict__ y, int64_t ldy, int out_f32, int32_t *__restrict__ acc_out,
     int n_batches) {
-    extern __shared__ XChunk8 qsh[];  // [MT][cpr + 1], record cpr of each token is zero
+    // [MT][cpr + 1] records (record cpr of each token is zero), then (FQ) [MT] token maxima
+    extern __shared__ XChunk8 qsh[];
     const int lane = threadIdx.x & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     const int64_t cpr = k_pad / kChunkCols;
@@ -467,16 +485,21 @@ __global__ void __launch_bounds__(BT) gemv_w4a8_stream_kernel(
     };
     // activations and their scales first (see the W4A16 kernel), then the ring of batches
     float sx[MT];
+    if (!FQ) {
 #pragma unroll
-    for (int m = 0; m < MT; ++m) sx[m] = s_x[m < M ? m : M - 1];
-    // (q rows are ldq apart with ldq % 16 == 0: a 16-byte piece that starts before d_in lies
-    // inside its row; pieces past d_in and threads past the last chunk read zeros)
+        for (int m = 0; m < MT; ++m) sx[m] = s_x[m < M ? m : M - 1];
+    }
+    // (rows are ldq elements apart with ldq % 16 == 0 for int8 codes and ldq % 8 == 0 for bf16:
+    // a 16-byte piece that starts before d_in lies inside its row; pieces past d_in and threads
+    // past the last chunk read zeros)
     constexpr int SI = (MT * T * SEG * kWave + BT - 1) / BT;  // >= ceil(MT * cpr / BT)
+    constexpr int NP = FQ ? 4 : 2;                            // 16-byte pieces per chunk
+    constexpr int EB = FQ ? 2 : 1;                            // bytes per activation
     const int n_chunks = MT * static_cast<int>(cpr);
     const int cpr_i = static_cast<int>(cpr);
     const int din = static_cast<int>(d_in);
-    const rsrc_t rx = make_rsrc(q, 0x7FFFFFFFu);  // the host keeps the offsets below 2^31
-    uint4 qraw[SI][2];
+    const rsrc_t rx = make_rsrc(act, 0x7FFFFFFFu);  // the host keeps the offsets below 2^31
+    uint4 qraw[SI][NP];
 #pragma unroll
     for (int si = 0; si < SI; ++si) {
         const int idx = static_cast<int>(threadIdx.x) + si * BT;
@@ -484,10 +507,10 @@ __global__ void __launch_bounds__(BT) gemv_w4a8_stream_kernel(
         const int c = idx - m * cpr_i;
         const int mx = m < M ? m : M - 1;  // tokens of the tile past M repeat token M - 1
 #pragma unroll
-        for (int p = 0; p < 2; ++p) {
-            const int col = c * kChunkCols + 16 * p;
+        for (int p = 0; p < NP; ++p) {
+            const int col = c * kChunkCols + (16 / EB) * p;
             const uint32_t off = idx < n_chunks && col < din
-                                     ? static_cast<uint32_t>((int64_t)mx * ldq + col)
+                                     ? static_cast<uint32_t>(((int64_t)mx * ldq + col) * EB)
                                      : kOutOfRange;
             qraw[si][p] =
                 __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
@@ -501,6 +524,45 @@ __global__ void __launch_bounds__(BT) gemv_w4a8_stream_kernel(
     }
     phase_fence();
 
+    // FQ: each token's largest |x| over the row, on the bf16 magnitude bits (monotone in |x|)
+    uint32_t *tmax = reinterpret_cast<uint32_t *>(qsh + MT * (cpr + 1));
+    if (FQ) {
+        if (threadIdx.x < MT) tmax[threadIdx.x] = 0u;
+        lds_barrier();
+#pragma unroll
+        for (int si = 0; si < SI; ++si) {
+            if (si * BT + wid * kWave >= n_chunks) break;
+            const int idx = static_cast<int>(threadIdx.x) + si * BT;
+            const int m = MT == 1 ? 0 : idx / cpr_i;
+            const int c = idx - m * cpr_i;
+            // (columns past d_in hold whatever follows in memory: masked without a branch)
+            u16x2_t m2 = {0, 0};
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const uint4 &raw = qraw[si][k >> 2];
+                const uint32_t d = (k & 3) == 0 ? raw.x : (k & 3) == 1 ? raw.y
+                                   : (k & 3) == 2 ? raw.z : raw.w;
+                const int left = din - (c * kChunkCols + 2 * k);  // columns of d before d_in
+                const uint32_t keep = left >= 2 ? 0x7FFF7FFFu : (left == 1 ? 0x7FFFu : 0u);
+                m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2_t, d & keep));
+            }
+            uint32_t am = idx < n_chunks ? (m2[0] > m2[1] ? m2[0] : m2[1]) : 0u;
+            if (MT == 1) {  // one token: a wave-wide maximum, then one atomic per wave
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1)
+                    am = max(am, static_cast<uint32_t>(__shfl_xor(static_cast<int>(am), o, kWave)));
+                if (lane == 0) atomicMax(&tmax[0], am);
+            } else if (idx < n_chunks) {
+                atomicMax(&tmax[m], am);
+            }
+        }
+        lds_barrier();
+#pragma unroll
+        for (int m = 0; m < MT; ++m) sx[m] = token_scale_int8(__uint_as_float(tmax[m] << 16));
+        if (blockIdx.x == 0 && threadIdx.x < MT && static_cast<int>(threadIdx.x) < M && s_x)
+            s_x[threadIdx.x] = token_scale_int8(__uint_as_float(tmax[threadIdx.x] << 16));
+    }
+
     // permute to the nibble order ([Orin DP4A 做了什么]) and stage in LDS (a wave whose chunks
     // all lie past the end skips the work; see the W4A16 kernel)
     const bool ragged = (din & 15) != 0;  // the piece holding column d_in - 1 has bytes past it
@@ -511,12 +573,46 @@ __global__ void __launch_bounds__(BT) gemv_w4a8_stream_kernel(
         const int m = MT == 1 ? 0 : idx / cpr_i;
         const int c = idx - m * cpr_i;
         uint32_t u[8];
+        if (FQ) {  // quantize the chunk: int8 codes of columns c * 32 .. + 31, in column order
+            const float a = __uint_as_float(tmax[m] << 16);
+            const float sc = token_scale_int8(a);
+            const float rc = 1.0f / sc;  // correctly rounded
+            // the codes of quantize_int8_fast, with its exact fallback taken once per chunk
+            float t[kChunkCols];
+            bool slow = !(fabsf(rc) < 0x1.0p126f);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint4 &raw = qraw[si][i >> 2];
-            u[i] = (i & 3) == 0 ? raw.x : (i & 3) == 1 ? raw.y : (i & 3) == 2 ? raw.z : raw.w;
+            for (int e = 0; e < kChunkCols; ++e) {
+                const uint4 &raw = qraw[si][e >> 3];
+                const uint32_t d = ((e >> 1) & 3) == 0 ? raw.x : ((e >> 1) & 3) == 1 ? raw.y
+                                   : ((e >> 1) & 3) == 2 ? raw.z : raw.w;
+                const float xv = bf16_to_f32((e & 1) ? (d >> 16) : (d & 0xFFFFu));
+                t[e] = quantize_int8_band(xv, rc, slow);
+            }
+            if (__builtin_expect(slow, 0)) {
+#pragma unroll
+                for (int e = 0; e < kChunkCols; ++e) {
+                    const uint4 &raw = qraw[si][e >> 3];
+                    const uint32_t d = ((e >> 1) & 3) == 0 ? raw.x : ((e >> 1) & 3) == 1 ? raw.y
+                                       : ((e >> 1) & 3) == 2 ? raw.z : raw.w;
+                    const float xv = bf16_to_f32((e & 1) ? (d >> 16) : (d & 0xFFFFu));
+                    t[e] = static_cast<float>(quantize_int8(xv, sc));
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) u[i] = 0u;
+#pragma unroll
+            for (int e = 0; e < kChunkCols; ++e) {
+                const int qe = a != 0.0f && c * kChunkCols + e < din ? static_cast<int>(t[e]) : 0;
+                u[e >> 2] |= (static_cast<uint32_t>(qe) & 0xFFu) << (8 * (e & 3));
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint4 &raw = qraw[si][i >> 2];
+                u[i] = (i & 3) == 0 ? raw.x : (i & 3) == 1 ? raw.y : (i & 3) == 2 ? raw.z : raw.w;
+            }
         }
-        if (__builtin_expect(ragged, 0)) {  // zero the bytes at or past d_in
+        if (!FQ && __builtin_expect(ragged, 0)) {  // zero the bytes at or past d_in
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -546,7 +642,7 @@ __global__ void __launch_bounds__(BT) gemv_w4a8_stream_kernel(
         zero.pad[0] = zero.pad[1] = zero.pad[2] = 0;
         qsh[(int64_t)threadIdx.x * (cpr + 1) + cpr] = zero;
     }
-    __syncthreads();
+    lds_barrier();  // (the weight loads of the ring stay in flight)
 
     // sum_k (c - 8) q = sum_k c q - 8 sum_k q, exactly in int32 ([Orin INT32 accumulator 是否安全])
     struct Out {  // see the W4A16 kernel
@@ -699,10 +795,15 @@ struct StreamPlan {
 };
 
 // T: steps per row; SEG: segments per row (n_batches counts segments)
-StreamPlan plan_stream(int64_t d_out, int T, int RW, int NB, int SEG = 1, int waves = kWaves) {
+// (bpc_div > 1: that many times fewer workgroups per CU, for kernels with a larger per-workgroup
+// prologue that run with more waves per workgroup instead)
+StreamPlan plan_stream(int64_t d_out, int T, int RW, int NB, int SEG = 1, int waves = kWaves,
+                       int bpc_div = 1) {
     StreamPlan p{};
     const int64_t rows_per_round_per_block = (int64_t)waves * RW;
-    int64_t blocks = (int64_t)device_cu_count() * stream_blocks_per_cu(T, SEG, d_out);
+    int bpc = stream_blocks_per_cu(T, SEG, d_out) / bpc_div;
+    if (bpc < 1) bpc = 1;
+    int64_t blocks = (int64_t)device_cu_count() * bpc;
     const int64_t need = (d_out + rows_per_round_per_block - 1) / rows_per_round_per_block;
     if (blocks > need) blocks = need;
     p.grid = static_cast<int>(blocks);
@@ -771,25 +872,34 @@ hipError_t launch_w4a16_stream_mt(int T, bool zp, const uint16_t *x, int64_t ldx
 #undef W4_STREAM_CASE
 }
 
-template <int MT, int T>
-hipError_t launch_w4a8_stream_t(const int8_t *q, int64_t ldq, int M, const float *s_x,
+// LDS of the W4A8 kernel: the staged chunks, and (FQ) the token maxima
+size_t w4a8_lds_bytes(int MT, int64_t k_pad, bool fq) {
+    return sizeof(XChunk8) * (size_t)MT * (size_t)(k_pad / kChunkCols + 1) +
+           (fq ? 16u * (size_t)((MT + 3) / 4) : 0u);
+}
+
+template <int MT, int T, bool FQ>
+hipError_t launch_w4a8_stream_t(const void *act, int64_t ldq, int M, float *s_x,
                                 const uint8_t *qweight, const uint16_t *s_w, const uint16_t *bias,
                                 int64_t d_out, int64_t d_in, int64_t k_pad, void *y, int64_t ldy,
                                 bool out_f32, int32_t *acc, hipStream_t stream) {
     constexpr Shape S = stream_shape(T);
     constexpr int SEG = MT == 1 && T >= 8 ? 2 : 1;  // see launch_w4a16_stream_t
     static_assert(T % SEG == 0 && S.nb % SEG == 0, "segments");
-    constexpr int BT = SEG > 1 ? 2 * kThreads : kThreads;
-    const StreamPlan p = plan_stream(d_out, T, S.rw, S.nb, SEG, BT / kWave);
-    const size_t lds = sizeof(XChunk8) * (size_t)MT * (size_t)(k_pad / kChunkCols + 1);
-    hipLaunchKernelGGL((gemv_w4a8_stream_kernel<MT, T / SEG, S.rw, S.nb, SEG, BT>), dim3(p.grid),
-                       dim3(BT), lds, stream, q, ldq, M, s_x, qweight, s_w, bias, d_out, d_in,
-                       k_pad, y, ldy, out_f32 ? 1 : 0, acc, p.n_batches);
+    // 8-wave workgroups for segmented rows (see launch_w4a16_stream_t) and whenever the
+    // workgroup quantizes the activations itself: a CU then quantizes the row half as often
+    constexpr bool wide = SEG > 1 || FQ;
+    constexpr int BT = wide ? 2 * kThreads : kThreads;
+    const StreamPlan p = plan_stream(d_out, T, S.rw, S.nb, SEG, BT / kWave, FQ && SEG == 1 ? 2 : 1);
+    const size_t lds = w4a8_lds_bytes(MT, k_pad, FQ);
+    hipLaunchKernelGGL((gemv_w4a8_stream_kernel<MT, T / SEG, S.rw, S.nb, SEG, BT, FQ>),
+                       dim3(p.grid), dim3(BT), lds, stream, act, ldq, M, s_x, qweight, s_w, bias,
+                       d_out, d_in, k_pad, y, ldy, out_f32 ? 1 : 0, acc, p.n_batches);
     return hipGetLastError();
 }
 
-template <int MT>
-hipError_t launch_w4a8_stream_mt(int T, const int8_t *q, int64_t ldq, int M, const float *s_x,
+template <int MT, bool FQ>
+hipError_t launch_w4a8_stream_mt(int T, const void *act, int64_t ldq, int M, float *s_x,
                                  const uint8_t *qweight, const uint16_t *s_w,
                                  const uint16_t *bias, int64_t d_out, int64_t d_in,
                                  int64_t k_pad, void *y, int64_t ldy, bool out_f32, int32_t *acc,
@@ -799,8 +909,8 @@ hipError_t launch_w4a8_stream_mt(int T, const int8_t *q, int64_t ldq, int M, con
         if constexpr ((MT == 4 && TT > kMaxT4) || (MT == 2 && TT > kMaxT2))                       \
             return hipErrorInvalidValue;                                                          \
         else                                                                                      \
-            return launch_w4a8_stream_t<MT, TT>(q, ldq, M, s_x, qweight, s_w, bias, d_out, d_in,  \
-                                                k_pad, y, ldy, out_f32, acc, stream);
+            return launch_w4a8_stream_t<MT, TT, FQ>(act, ldq, M, s_x, qweight, s_w, bias, d_out,  \
+                                                    d_in, k_pad, y, ldy, out_f32, acc, stream);
     switch (T) {
         W4_STREAM8_CASE(1)
         W4_STREAM8_CASE(2)
@@ -826,10 +936,10 @@ bool gemv_stream_supported(int64_t M, int64_t k_pad) {
            kLdsLimit;
 }
 
-bool w4a8_stream_supported(int64_t M, int64_t k_pad) {
+bool w4a8_stream_supported(int64_t M, int64_t k_pad, bool fused_quant) {
     const int64_t cpr = k_pad / kChunkCols;
     if (pick_steps(cpr) == 0) return false;
-    return sizeof(XChunk8) * (size_t)stream_token_tile(M, pick_steps(cpr)) * (size_t)(cpr + 1) <=
+    return w4a8_lds_bytes(stream_token_tile(M, pick_steps(cpr)), k_pad, fused_quant) <=
            kLdsLimit;
 }
 
@@ -866,30 +976,40 @@ hipError_t launch_gemv_stream(const uint16_t *x, int64_t M, int64_t ldx, const u
     return hipSuccess;
 }
 
-hipError_t launch_w4a8_stream(const int8_t *q, const float *s_x, int64_t M, int64_t ldq,
-                              const uint8_t *qweight, const uint16_t *s_w, const uint16_t *bias,
-                              int64_t d_out, int64_t d_in, int64_t k_pad, void *y, int64_t ldy,
-                              bool out_f32, int32_t *acc, hipStream_t stream) {
+// act: int8 codes [M][ldq] with their token scales in s_x (fused_quant false), or bf16 x
+// [M][ldq] quantized inside the kernel, the scales written to s_x if it is given (true).
+hipError_t launch_w4a8_stream(const void *act, bool fused_quant, float *s_x, int64_t M,
+                              int64_t ldq, const uint8_t *qweight, const uint16_t *s_w,
+                              const uint16_t *bias, int64_t d_out, int64_t d_in, int64_t k_pad,
+                              void *y, int64_t ldy, bool out_f32, int32_t *acc,
+                              hipStream_t stream) {
     const int T = pick_steps(k_pad / kChunkCols);
     int tile = stream_token_tile(M, T);
+    const int64_t eb = fused_quant ? 2 : 1;  // bytes per activation
     // the kernel addresses a tile's activations with 31-bit byte offsets; one token always fits
-    if ((int64_t)(tile - 1) * ldq + k_pad >= (int64_t)kOutOfRange) tile = 1;
+    if (((int64_t)(tile - 1) * ldq + k_pad) * eb >= (int64_t)kOutOfRange) tile = 1;
     const size_t out_elem = out_f32 ? sizeof(float) : sizeof(uint16_t);
     for (int64_t m0 = 0; m0 < M; m0 += tile) {
         const int mt = static_cast<int>(M - m0 < tile ? M - m0 : tile);
-        const int8_t *qm = q + m0 * ldq;
+        const void *am_act = static_cast<const char *>(act) + m0 * ldq * eb;
+        float *sm = s_x ? s_x + m0 : nullptr;
         void *ym = static_cast<char *>(y) + m0 * ldy * out_elem;
         int32_t *am = acc ? acc + m0 * d_out : nullptr;
         hipError_t err;
+#define W4_W4A8_TILE(MTV)                                                                         \
+    (fused_quant ? launch_w4a8_stream_mt<MTV, true>(T, am_act, ldq, mt, sm, qweight, s_w, bias,   \
+                                                    d_out, d_in, k_pad, ym, ldy, out_f32, am,     \
+                                                    stream)                                       \
+                 : launch_w4a8_stream_mt<MTV, false>(T, am_act, ldq, mt, sm, qweight, s_w, bias,  \
+                                                     d_out, d_in, k_pad, ym, ldy, out_f32, am,    \
+                                                     stream))
         if (tile == 1)
-            err = launch_w4a8_stream_mt<1>(T, qm, ldq, mt, s_x + m0, qweight, s_w, bias, d_out,
-                                           d_in, k_pad, ym, ldy, out_f32, am, stream);
+            err = W4_W4A8_TILE(1);
         else if (tile == 2)
-            err = launch_w4a8_stream_mt<2>(T, qm, ldq, mt, s_x + m0, qweight, s_w, bias, d_out,
-                                           d_in, k_pad, ym, ldy, out_f32, am, stream);
+            err = W4_W4A8_TILE(2);
         else
-            err = launch_w4a8_stream_mt<4>(T, qm, ldq, mt, s_x + m0, qweight, s_w, bias, d_out,
-                                           d_in, k_pad, ym, ldy, out_f32, am, stream);
+            err = W4_W4A8_TILE(4);
+#undef W4_W4A8_TILE
         if (err != hipSuccess) return err;
     }
     return hipSuccess;

@@ -25,6 +25,13 @@ hipError_t launch_w4a8(const int8_t *q, const float *s_x, int64_t M, int64_t ldq
                        int64_t d_out, int64_t d_in, int64_t k_pad, void *y, int64_t ldy,
                        bool out_f32, int32_t *acc, hipStream_t stream);
 
+// W4A8 with the activation quantization folded into the GEMV (bf16 x in; s_x out, nullable).
+bool w4a8_linear_supported(int64_t M, int64_t k_pad);
+hipError_t launch_w4a8_linear(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
+                              const uint16_t *s_w, const uint16_t *bias, int64_t d_out,
+                              int64_t d_in, int64_t k_pad, void *y, int64_t ldy, bool out_f32,
+                              float *s_x, int32_t *acc, hipStream_t stream);
+
 hipError_t launch_gemm(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
                        const uint16_t *scales, const uint16_t *zeros, const uint16_t *bias,
                        int64_t d_out, int64_t d_in, int64_t k_pad, int64_t span,
@@ -32,16 +39,19 @@ hipError_t launch_gemm(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t 
 
 // Persistent streaming decode GEMVs (decode_stream.hip).
 bool gemv_stream_supported(int64_t M, int64_t k_pad);
-bool w4a8_stream_supported(int64_t M, int64_t k_pad);
+bool w4a8_stream_supported(int64_t M, int64_t k_pad, bool fused_quant);
 hipError_t launch_gemv_stream(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
                               const uint16_t *scales, const uint16_t *zeros, const uint16_t *bias,
                               int64_t d_out, int64_t d_in, int64_t k_pad, int chunk_group_shift,
                               int64_t n_groups, void *y, int64_t ldy, bool out_f32,
                               hipStream_t stream);
-hipError_t launch_w4a8_stream(const int8_t *q, const float *s_x, int64_t M, int64_t ldq,
-                              const uint8_t *qweight, const uint16_t *s_w, const uint16_t *bias,
-                              int64_t d_out, int64_t d_in, int64_t k_pad, void *y, int64_t ldy,
-                              bool out_f32, int32_t *acc, hipStream_t stream);
+// act: int8 codes [M][ldq] with their scales in s_x, or (fused_quant) bf16 x [M][ldq], quantized
+// per token inside the kernel with the act_quant rule, the scales written to s_x if given.
+hipError_t launch_w4a8_stream(const void *act, bool fused_quant, float *s_x, int64_t M,
+                              int64_t ldq, const uint8_t *qweight, const uint16_t *s_w,
+                              const uint16_t *bias, int64_t d_out, int64_t d_in, int64_t k_pad,
+                              void *y, int64_t ldy, bool out_f32, int32_t *acc,
+                              hipStream_t stream);
 
 // Few-token decode on the fp16 matrix cores (decode_mfma.hip): activations converted inside
 // each block, one pass over the weights for all tokens of a 16-token tile; no workspace.

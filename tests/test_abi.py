@@ -36,6 +36,7 @@ def lib():
     L.w4_gemm.argtypes = lin + [p]
     L.act_quant_int8.argtypes = [p, i64, i64, i64, p, i64, p, p, p]
     L.w4a8_gemv.argtypes = [p, p, i64, i64, p, p, p, i64, i64, p, i64, i32, p, p]
+    L.w4a8_linear.argtypes = [p, i64, i64, p, p, p, i64, i64, p, i64, i32, p, p, p]
     L.w4_status_string.restype = ctypes.c_char_p
     L.w4_last_hip_error.restype = ctypes.c_char_p
     return L
@@ -43,7 +44,7 @@ def lib():
 
 def test_header_declares_the_five_entry_points():
     names = declared_functions()
-    for n in ("w4_pack", "w4_gemv", "w4_gemm", "act_quant_int8", "w4a8_gemv",
+    for n in ("w4_pack", "w4_gemv", "w4_gemm", "act_quant_int8", "w4a8_gemv", "w4a8_linear",
               "w4_packed_layout", "w4_status_string",
               "w4_last_hip_error"):
         assert n in names
@@ -176,3 +177,33 @@ def test_w4a8_rejects_bad_arguments(lib):
     assert call(acc=E + 2) == W4_ERR_ALIGN
     big = (1 << 20) + 16
     assert call(d_in=big, ldq=big) == W4_ERR_RANGE
+
+
+def test_w4a8_linear_rejects_bad_arguments(lib):
+    f = lib.w4a8_linear
+
+    def call(**kw):
+        a = dict(x=A, M=1, ldx=256, qw=C, sw=D, bias=None, d_out=128, d_in=256, y=E, ldy=128,
+                 out=0, sx=None, acc=None)
+        a.update(kw)
+        return f(a["x"], a["M"], a["ldx"], a["qw"], a["sw"], a["bias"], a["d_out"], a["d_in"],
+                 a["y"], a["ldy"], a["out"], a["sx"], a["acc"], None)
+
+    assert call(x=None) == W4_ERR_NULL
+    assert call(qw=None) == W4_ERR_NULL
+    assert call(sw=None) == W4_ERR_NULL
+    assert call(y=None) == W4_ERR_NULL
+    assert call(M=0) == W4_ERR_SHAPE
+    assert call(M=65) == W4_ERR_UNSUPPORTED
+    assert call(d_out=0) == W4_ERR_SHAPE
+    assert call(ldx=255) == W4_ERR_SHAPE
+    assert call(ldy=127) == W4_ERR_SHAPE
+    assert call(ldx=260) == W4_ERR_ALIGN
+    assert call(x=A + 8) == W4_ERR_ALIGN
+    assert call(sx=B + 2) == W4_ERR_ALIGN
+    assert call(acc=B + 2) == W4_ERR_ALIGN
+    assert call(out=2) == W4_ERR_UNSUPPORTED
+    big = (1 << 20) + 16
+    assert call(d_in=big, ldx=big) == W4_ERR_RANGE
+    # rows longer than the fused kernel's activation stage: the two-call path serves them
+    assert call(d_in=60000, ldx=60000) == W4_ERR_UNSUPPORTED

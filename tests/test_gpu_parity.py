@@ -411,6 +411,23 @@ def check_w4a8(w, x_bits, bias_bits, what):
     y32h = host(y32)
     assert_close(y32h, y_ref, what)
     assert_bf16_is_rne_of_f32(y16, y32h, what)
+    # the same linear with the quantization folded in (w4a8_linear), on a strided x whose columns
+    # past d_in hold NaN: the token scales and the accumulators are those of the oracle's O5 -> O6
+    _announce("w4a8_linear", what, w.shape, x_bits.shape)
+    ldx = (d_in + 7) // 8 * 8 + 8
+    xj = np.full((x_bits.shape[0], ldx), 0x7FC0, dtype=np.uint16)
+    xj[:, :d_in] = x_bits
+    xd = dev_bf16(xj)
+    y32f, accf, sxf = w4.w4a8_linear(xd, pd[0], pd[1], b, d_in, F32, want_acc=True,
+                                     want_scales=True)
+    y16f = w4.w4a8_linear(xd, pd[0], pd[1], b, d_in, BF16)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(sxf).view(np.uint32), s_o.astype(np.float32).view(np.uint32)), \
+        f"{what}: fused token scales differ"
+    assert np.array_equal(host(accf), acc_o), f"{what}: fused int32 accumulators differ"
+    y32fh = host(y32f)
+    assert_close(y32fh, y_ref, what + " (fused)")
+    assert_bf16_is_rne_of_f32(y16f, y32fh, what + " (fused)")
 
 
 def test_w4a8_c5_full_size():
@@ -431,6 +448,59 @@ def test_w4a8_ragged_and_token_counts():
         check_w4a8(w, x, b if M % 2 else None, f"M={M} {d_out}x{d_in}")
 
 
+def _near_tie_activations():
+    """Tokens whose values sit on and next to the rounding ties s (k + 1/2) of their own scale
+    s = max|x| / 127, for every k in [-127, 126]; one token's maximum is so small that 1/s is
+    not a finite fp32 number."""
+    def f32(bits):
+        return (np.asarray(bits, np.uint32) << 16).view(np.float32)
+
+    rows = []
+    extra = np.exp(np.random.default_rng(31).uniform(np.log(1e-3), np.log(1e3), 30))
+    for a in (1.0, 3.0, 0.0118, 100.0, 2.5e-37, *extra):
+        ab = workloads.to_bf16_bits(np.array([a], np.float32))[0]
+        a32 = f32([ab])[0]
+        s = np.float32(a32 / np.float32(127.0))
+        ties = (np.arange(-127, 127, dtype=np.float64) + 0.5) * np.float64(s)
+        b = workloads.to_bf16_bits(ties.astype(np.float32)).astype(np.int64)
+        cand = np.concatenate([b, b + 1, b - 1]) & 0xFFFF
+        v = f32(cand)
+        keep = np.isfinite(v) & (np.abs(v) <= a32)  # the token's maximum stays a
+        rows.append(np.concatenate([cand[keep], [ab]]).astype(np.uint16))
+    K = max(len(r) for r in rows)
+    x = np.zeros((len(rows), K), dtype=np.uint16)
+    for i, r in enumerate(rows):
+        x[i, :len(r)] = r
+    return x
+
+
+def test_activation_codes_at_rounding_ties():
+    """act_quant_int8 and w4a8_linear (its codes read back through weights that pick one column
+    per row: code 9 at (j, j), 8 elsewhere, s_w = 1) against the oracle's O5, bit for bit."""
+    x = _near_tie_activations()
+    M, K = x.shape
+    _announce("activation codes at rounding ties", M, K)
+    q_o, s_o, _ = oracle.act_quant(x, K)
+    ldx = (K + 7) // 8 * 8
+    xp = np.zeros((M, ldx), dtype=np.uint16)
+    xp[:, :K] = x
+    q, s_x, _ = w4.act_quant_int8(dev_bf16(xp), K)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(q)[:, :K], q_o), "act_quant codes differ at rounding ties"
+    assert np.array_equal(host(s_x).view(np.uint32), s_o.view(np.uint32))
+    k_pad = (K + 31) // 32 * 32
+    codes = np.full((K, k_pad), 8, dtype=np.uint8)
+    codes[np.arange(K), np.arange(K)] = 9
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    qw = torch.from_numpy(packed).cuda()
+    sw = dev_bf16(np.full(K, 0x3F80, dtype=np.uint16))
+    _, acc, sxf = w4.w4a8_linear(dev_bf16(xp), qw, sw, None, K, F32, want_acc=True,
+                                 want_scales=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(acc), q_o.astype(np.int32)), "fused codes differ at rounding ties"
+    assert np.array_equal(host(sxf).view(np.uint32), s_o.view(np.uint32))
+
+
 @pytest.mark.parametrize("H", [3584, 18944])
 def test_w4a8_worst_case_accumulator(H):
     """All weight codes 0 (level -8) and all activations -127: acc = H * 1016 (3,641,344 for
@@ -446,3 +516,8 @@ def test_w4a8_worst_case_accumulator(H):
     if H == 3584:
         assert H * 1016 == 3641344
     assert host(y).tolist() == [[float(H * 1016)] * 4]
+    # fused: x = -1 everywhere quantizes to -127 everywhere (s_x = 1/127)
+    x = dev_bf16(np.full((1, H), 0xBF80, dtype=np.uint16))
+    y, acc = w4.w4a8_linear(x, qw, sw, None, H, F32, want_acc=True)
+    torch.cuda.synchronize()
+    assert host(acc).tolist() == [[H * 1016] * 4]
