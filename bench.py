@@ -170,9 +170,19 @@ def bench_c2(torch, w4, workloads, steps, warmup, rotate_bytes):
     dn_ms = med(lambda: graph_ms(torch, lambda: [down(c) for c in copies], n_copies, replays))
     b_gu = linear_bytes(1, gu.d_out, gu.d_in, gu.group_size, False)
     b_dn = linear_bytes(1, dn.d_out, dn.d_in, dn.group_size, False)
+    # the same gate/up weights with the SiLU(gate) * up epilogue (w4_gemv_glu): h has d_out / 2
+    # values
+    h_gu = torch.empty((1, gu.d_out // 2), dtype=torch.bfloat16, device=dev)
+
+    def gate_up_glu(c):
+        w4.w4_gemv_glu(x_gu, *c[0], None, gu.d_in, gu.group_size, out=h_gu)
+
+    glu_ms = med(lambda: graph_ms(torch, lambda: [gate_up_glu(c) for c in copies], n_copies,
+                                  replays))
+    b_glu = b_gu - (gu.d_out // 2) * 2
     return dict(step_ms=step_ms, bytes_step=b_gu + b_dn, gu_ms=gu_ms, dn_ms=dn_ms, b_gu=b_gu,
-                b_dn=b_dn, n_copies=n_copies, rotate_mb=n_copies * per_copy / 1e6,
-                steps_timed=replays * n_copies)
+                b_dn=b_dn, glu_ms=glu_ms, b_glu=b_glu, n_copies=n_copies,
+                rotate_mb=n_copies * per_copy / 1e6, steps_timed=replays * n_copies)
 
 
 def stream_copy_gbs(torch, nbytes=1 << 30, reps=20):
@@ -388,6 +398,10 @@ def main():
         log("C3 decoder step")
         secondary["C3_decoder_step"] = bench_c3(torch, w4, workloads, 5)
 
+    secondary["C2_gate_up_silu_mul"] = dict(
+        us=round(r["glu_ms"] * 1e3, 3), gbs=round(r["b_glu"] / r["glu_ms"] / 1e6, 1),
+        hbm_frac=round(r["b_glu"] / r["glu_ms"] / 1e6 / HBM_PEAK_GBS, 4),
+        plain_gate_up_us=round(r["gu_ms"] * 1e3, 3))
     value = r["bytes_step"] / r["step_ms"] / 1e6
     gu_gbs = r["b_gu"] / r["gu_ms"] / 1e6
     src = source_hash(*TRAFFIC_SOURCES)

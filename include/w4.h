@@ -107,6 +107,25 @@ int w4_gemv(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
             int64_t d_in, int group_size, void *y, int64_t ldy, int out_dtype, void *stream);
 
 /*
+ * w4_gemv_glu -- the gate/up half of the MLP with its gate fused into the epilogue:
+ *   h[m][j] = SiLU(g[m][j]) * u[m][j],  SiLU(v) = v / (1 + exp(-v)),
+ *   g = x W_gate^T (+ b_gate),  u = x W_up^T (+ b_up),
+ * [Lab5 基础] (FFN(x) = W_down [SiLU(W_gate x) (.) (W_up x)]), [Orin 后续还能继续优化什么] (the
+ * SwiGLU kernel boundary). One launch reads the fused weight once and writes only h.
+ *   qweight, scales, zeros: a packed weight of 2 d_ff rows, the gate rows [0, d_ff) then the
+ *            up rows [d_ff, 2 d_ff) (w4_pack of the stacked gate and up weights)
+ *   bias     bf16 [2 d_ff] (gate biases, then up biases) or NULL
+ *   y        [M][ldy], ldy >= d_ff: h, as fp32 or its round-to-nearest-even bf16 image
+ *   the other arguments as for w4_gemv.
+ * Served by the int8 matrix-core decode kernel: 1 <= M <= 4 tokens, group_size 128 or 256, or
+ * 0 with k_pad a multiple of 128, and k_pad <= 32768 / M (its activation stage); other arguments
+ * return W4_ERR_UNSUPPORTED (use w4_gemv on the fused weight and apply the gate separately).
+ */
+int w4_gemv_glu(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
+                const uint16_t *scales, const uint16_t *zeros, const uint16_t *bias, int64_t d_ff,
+                int64_t d_in, int group_size, void *y, int64_t ldy, int out_dtype, void *stream);
+
+/*
  * w4_gemm -- W4A16 prefill linear for any M >= 1 (the arguments of w4_gemv, and the same
  * result within the tolerance).
  * [Lab5 Prefill和Decode分流] (large M: dequantize once per tile and run a dense matrix product).
@@ -154,8 +173,8 @@ int w4a8_gemv(const int8_t *q, const float *s_x, int64_t M, int64_t ldq, const u
  * w4a8_linear -- the W4A8 decode linear with the activation quantization folded in: the result
  * of act_quant_int8 followed by w4a8_gemv, in one launch, without q in memory.
  * [Orin 从 FP 线性层到 INT4 DP4A 的数学推导] (s_x = max|x|/127, q = clamp(rint(x/s_x), +-127)),
- * [Orin INT32 accumulator 是否安全], and the kernel boundary that the W4A8 activation quantization
- * adds as a separate launch [Orin 模型尺寸和 decode 的真实瓶颈].
+ * [Orin INT32 accumulator 是否安全], and the kernel boundary between quantization and linear that
+ * [Orin 后续还能继续优化什么] names for further fusion.
  *   x        bf16 [M][ldx], ldx >= d_in, ldx % 8 == 0, 16-byte aligned; only k < d_in is used
  *   qweight, s_w, bias, y, out_dtype, acc: as for w4a8_gemv
  *   s_x      fp32 [M] or NULL: receives the token scales

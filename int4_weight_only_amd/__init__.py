@@ -16,7 +16,8 @@ import torch
 
 __all__ = [
     "W4_SYM", "W4_ASYM", "W4_OUT_BF16", "W4_OUT_F32", "W4Error", "packed_layout", "w4_pack",
-    "w4_gemv", "w4_gemm", "act_quant_int8", "w4a8_gemv", "w4a8_linear", "w4_linear",
+    "w4_gemv", "w4_gemv_glu", "w4_gemm", "act_quant_int8", "w4a8_gemv", "w4a8_linear",
+    "w4_linear",
     "library_path",
 ]
 
@@ -46,12 +47,13 @@ def _load():
     lib.w4_pack.argtypes = [p, i64, i64, i64, i32, i32, p, p, p, p]
     lin = [p, i64, i64, p, p, p, p, i64, i64, i32, p, i64, i32]
     lib.w4_gemv.argtypes = lin + [p]
+    lib.w4_gemv_glu.argtypes = lin + [p]
     lib.w4_gemm.argtypes = lin + [p]
     lib.act_quant_int8.argtypes = [p, i64, i64, i64, p, i64, p, p, p]
     lib.w4a8_gemv.argtypes = [p, p, i64, i64, p, p, p, i64, i64, p, i64, i32, p, p]
     lib.w4a8_linear.argtypes = [p, i64, i64, p, p, p, i64, i64, p, i64, i32, p, p, p]
-    for f in ("w4_packed_layout", "w4_pack", "w4_gemv", "w4_gemm", "act_quant_int8",
-              "w4a8_gemv", "w4a8_linear"):
+    for f in ("w4_packed_layout", "w4_pack", "w4_gemv", "w4_gemv_glu", "w4_gemm",
+              "act_quant_int8", "w4a8_gemv", "w4a8_linear"):
         getattr(lib, f).restype = i32
     lib.w4_status_string.argtypes = [i32]
     lib.w4_status_string.restype = ctypes.c_char_p
@@ -158,6 +160,44 @@ def _linear(fn_name, x, qweight, scales, zeros, bias, d_in, group_size, out_dtyp
 def w4_gemv(x, qweight, scales, zeros, bias, d_in, group_size, out_dtype=W4_OUT_BF16, out=None):
     """Decode W4A16 linear, 1 <= M <= 64: y[M][d_out] = x . W_hat^T (+ b)."""
     return _linear("w4_gemv", x, qweight, scales, zeros, bias, d_in, group_size, out_dtype, out)
+
+
+def w4_gemv_glu(x, qweight, scales, zeros, bias, d_in, group_size, out_dtype=W4_OUT_BF16,
+                out=None):
+    """Gate/up GEMV with the SiLU(gate) * up epilogue: qweight holds 2 d_ff rows (gate rows, then
+    up rows), bias 2 d_ff values or None; returns h [M][d_ff]."""
+    _need(x, "x", torch.bfloat16, dim=2)
+    dev = x.device
+    _need(qweight, "qweight", torch.uint8, dev, 2)
+    _need(scales, "scales", torch.bfloat16, dev, 2)
+    if zeros is not None:
+        _need(zeros, "zeros", torch.bfloat16, dev, 2)
+    if bias is not None:
+        _need(bias, "bias", torch.bfloat16, dev, 1)
+    M = x.shape[0]
+    rows = qweight.shape[0]
+    if rows % 2:
+        raise ValueError("a fused gate/up weight has an even number of rows")
+    d_ff = rows // 2
+    k_pad, n_groups, _ = packed_layout(rows, d_in, group_size)
+    if tuple(qweight.shape) != (rows, k_pad // 2) or not qweight.is_contiguous():
+        raise ValueError(f"qweight must be contiguous [{rows}][{k_pad // 2}]")
+    for name, t in (("scales", scales), ("zeros", zeros)):
+        if t is not None and (tuple(t.shape) != (rows, n_groups) or not t.is_contiguous()):
+            raise ValueError(f"{name} must be contiguous [{rows}][{n_groups}]")
+    if bias is not None and bias.shape[0] != rows:
+        raise ValueError(f"bias must have {rows} elements")
+    if x.shape[1] < d_in:
+        raise ValueError(f"x has {x.shape[1]} columns, fewer than d_in={d_in}")
+    tdtype = torch.float32 if out_dtype == W4_OUT_F32 else torch.bfloat16
+    if out is None:
+        out = torch.empty((M, d_ff), dtype=tdtype, device=dev)
+    else:
+        _need(out, "out", tdtype, dev, 2)
+    _check("w4_gemv_glu", _lib.w4_gemv_glu(_ptr(x), M, x.stride(0), _ptr(qweight), _ptr(scales),
+                                           _ptr(zeros), _ptr(bias), d_ff, d_in, group_size,
+                                           _ptr(out), out.stride(0), out_dtype, _stream(dev)))
+    return out
 
 
 def w4_gemm(x, qweight, scales, zeros, bias, d_in, group_size, out_dtype=W4_OUT_BF16, out=None):

@@ -180,6 +180,25 @@ int w4a8_gemv(const int8_t *q, const float *s_x, int64_t M, int64_t ldq, const u
     return err == hipSuccess ? W4_OK : hip_fail(err);
 }
 
+int w4_gemv_glu(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
+                const uint16_t *scales, const uint16_t *zeros, const uint16_t *bias, int64_t d_ff,
+                int64_t d_in, int group_size, void *y, int64_t ldy, int out_dtype, void *stream) {
+    if (int st = check_linear(x, M, ldx, qweight, scales, zeros, bias, d_ff, d_in, group_size, y,
+                              ldy, out_dtype))
+        return st;
+    if (zeros && !aligned(zeros, 2)) return W4_ERR_ALIGN;
+    if (2 * d_ff > W4_MAX_DIM) return W4_ERR_RANGE;
+    if (d_in > kDecodeMaxDin) return W4_ERR_RANGE;
+    const Layout L = layout_of(d_in, group_size);
+    if (!w4::gemv_i8_supported(M, d_ff, d_in, L.k_pad, L.span, L.n_groups, ldx, true))
+        return W4_ERR_UNSUPPORTED;
+    const hipError_t err =
+        w4::launch_gemv_i8(x, M, ldx, qweight, scales, zeros, bias, d_ff, d_in, L.k_pad, L.span,
+                           L.n_groups, y, ldy, out_dtype == W4_OUT_F32, true,
+                           static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? W4_OK : hip_fail(err);
+}
+
 int w4a8_linear(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
                 const uint16_t *s_w, const uint16_t *bias, int64_t d_out, int64_t d_in, void *y,
                 int64_t ldy, int out_dtype, float *s_x, int32_t *acc, void *stream) {

@@ -532,7 +532,7 @@ hipError_t launch_gemv(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t 
     if (gemv_i8_preferred(M, d_out, k_pad) &&
         gemv_i8_supported(M, d_out, d_in, k_pad, span, n_groups, ldx))
         return launch_gemv_i8(x, M, ldx, qweight, scales, zeros, bias, d_out, d_in, k_pad, span,
-                              n_groups, y, ldy, out_f32, stream);
+                              n_groups, y, ldy, out_f32, false, stream);
     // Two or more tokens: the matrix-core path reads the weights once for all of them.
     if (gemv_mfma_supported(M, d_out, d_in, k_pad, span, n_groups, ldx, zeros != nullptr))
         return launch_gemv_mfma(x, M, ldx, qweight, scales, zeros, bias, d_out, d_in, k_pad, span,

@@ -76,7 +76,13 @@ __host__ __device__ inline I8Lds i8_lds(int M, int n128, int n_groups, int T, bo
     return L;
 }
 
-template <int M, bool ZP, int XP>
+// GLU: the gate of the MLP fused into the epilogue ([Lab5 基础]: FFN(x) = W_down [SiLU(W_gate x)
+// (.) (W_up x)]; [Orin 后续还能继续优化什么] names this kernel boundary). The weight holds 2 d_out
+// rows, gate rows [0, d_out) then up rows [d_out, 2 d_out) (bias likewise, if given); a block's
+// slice is output rows [r0, r0 + R): its first T/2 tiles are those gate rows, the last T/2 the
+// up rows, each half through its own descriptor and LDS table half. The store writes
+// SiLU(g) u = g u / (1 + exp(-g)) in fp32.
+template <int M, bool ZP, int XP, bool GLU>
 __global__ void __launch_bounds__(kI8Threads) gemv_i8_kernel(
     const uint16_t *__restrict__ x, int64_t ldx, const uint8_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
@@ -89,7 +95,8 @@ __global__ void __launch_bounds__(kI8Threads) gemv_i8_kernel(
     const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int r0 = blockIdx.x * rows_per_block;
     const int R = d_out - r0 < rows_per_block ? d_out - r0 : rows_per_block;  // >= 1
-    const int T = (R + 15) >> 4;
+    const int Th = (R + 15) >> 4;  // tiles of one half (GLU) or of the slice
+    const int T = GLU ? 2 * Th : Th;
     const I8Lds L = i8_lds(M, n128, n_groups, T, ZP);
     // units are dealt in pairs: wave w takes units 16 m + 2 w and 16 m + 2 w + 1 (m = 0, 1, ...)
     // below U, so its two loads of a pair cover the same 128-byte lines
@@ -115,22 +122,35 @@ __global__ void __launch_bounds__(kI8Threads) gemv_i8_kernel(
         xr[p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
     }
     // ---- the slice's scales (and zeros): R * n_groups contiguous bf16 values ----
-    const int nsc = R * n_groups;  // <= kI8TableLoads * kI8Threads (host)
+    // (GLU: each half's table takes half of the loads)
+    constexpr int TL = GLU ? kI8TableLoads / 2 : kI8TableLoads;
+    const int nsc = R * n_groups;  // <= TL * kI8Threads (host)
+    const int64_t up0 = GLU ? (int64_t)d_out : 0;  // first up row (GLU)
     const rsrc_t rs = make_rsrc(scales + (int64_t)r0 * n_groups, static_cast<uint32_t>(nsc) * 2u);
     const rsrc_t rz = make_rsrc(ZP ? zeros + (int64_t)r0 * n_groups : scales,
                                 ZP ? static_cast<uint32_t>(nsc) * 2u : 0u);
-    uint32_t sv[kI8TableLoads], zv[ZP ? kI8TableLoads : 1];
+    const rsrc_t rs2 = make_rsrc(scales + (up0 + r0) * n_groups,
+                                 GLU ? static_cast<uint32_t>(nsc) * 2u : 0u);
+    const rsrc_t rz2 = make_rsrc(ZP ? zeros + (up0 + r0) * n_groups : scales,
+                                 GLU && ZP ? static_cast<uint32_t>(nsc) * 2u : 0u);
+    uint32_t sv[TL], zv[ZP ? TL : 1], sv2[GLU ? TL : 1], zv2[GLU && ZP ? TL : 1];
 #pragma unroll
-    for (int i = 0; i < kI8TableLoads; ++i) {
+    for (int i = 0; i < TL; ++i) {
         const uint32_t off = static_cast<uint32_t>(tid + i * kI8Threads) * 2u;  // past nsc: 0
         sv[i] = __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0);
         if (ZP) zv[ZP ? i : 0] = __builtin_amdgcn_raw_buffer_load_b16(rz, off, 0, 0);
+        if (GLU) {
+            sv2[GLU ? i : 0] = __builtin_amdgcn_raw_buffer_load_b16(rs2, off, 0, 0);
+            if (ZP) zv2[GLU && ZP ? i : 0] = __builtin_amdgcn_raw_buffer_load_b16(rz2, off, 0, 0);
+        }
     }
 
     // ---- the weight ring: the k-th unit of this wave is u = 16 (k / 2) + 2w + k % 2 =
     // (tile t, group G); from k to k + 1, u grows by 1 (k even) or by 15 (k odd) ----
     const uint32_t rb = static_cast<uint32_t>(row_bytes);
     const rsrc_t rq = make_rsrc(qweight + (int64_t)r0 * row_bytes, static_cast<uint32_t>(R) * rb);
+    const rsrc_t rq2 = make_rsrc(qweight + (up0 + r0) * row_bytes,
+                                 GLU ? static_cast<uint32_t>(R) * rb : 0u);
     const int jump = 2 * kI8Waves - 1;
     const int dt = jump / n128, dG = jump % n128;
     // offsets = a per-lane part (row n of the tile, k-block q) + a wave-uniform part (tile t,
@@ -142,7 +162,14 @@ __global__ void __launch_bounds__(kI8Threads) gemv_i8_kernel(
     const uint32_t w_lane = static_cast<uint32_t>(n) * rb + 16u * q;
     auto load = [&](int k, int t, int G, u32x4_t &dst) {
         const uint32_t past = static_cast<uint32_t>((nu - 1 - k) >> 31) << 31;
-        const uint32_t tc = static_cast<uint32_t>(t < T ? t : T);
+        uint32_t tc = static_cast<uint32_t>(t < T ? t : T);
+        if (GLU && tc >= static_cast<uint32_t>(Th)) {  // an up tile (the clamp lands past R)
+            tc -= static_cast<uint32_t>(Th);
+            const uint32_t wo =
+                w_lane + ((16u * tc * rb + 64u * static_cast<uint32_t>(G)) | past);
+            dst = __builtin_amdgcn_raw_buffer_load_b128(rq2, wo, 0, 0);
+            return;
+        }
         const uint32_t wo = w_lane + ((16u * tc * rb + 64u * static_cast<uint32_t>(G)) | past);
         dst = __builtin_amdgcn_raw_buffer_load_b128(rq, wo, 0, 0);
     };
@@ -172,12 +199,17 @@ __global__ void __launch_bounds__(kI8Threads) gemv_i8_kernel(
     // ---- tables, partial sums ----
     uint16_t *sct = reinterpret_cast<uint16_t *>(lds + L.sct);
     uint16_t *zct = reinterpret_cast<uint16_t *>(lds + L.zct);
+    const int up_table = 16 * Th * n_groups;  // GLU: the up rows' table starts at tile Th
 #pragma unroll
-    for (int i = 0; i < kI8TableLoads; ++i) {
+    for (int i = 0; i < TL; ++i) {
         const int idx = tid + i * kI8Threads;
         if (idx < nsc) {
             sct[idx] = static_cast<uint16_t>(sv[i]);
             if (ZP) zct[idx] = static_cast<uint16_t>(zv[ZP ? i : 0]);
+            if (GLU) {
+                sct[up_table + idx] = static_cast<uint16_t>(sv2[GLU ? i : 0]);
+                if (ZP) zct[up_table + idx] = static_cast<uint16_t>(zv2[GLU && ZP ? i : 0]);
+            }
         }
     }
     float *red = reinterpret_cast<float *>(lds + L.red);
@@ -350,15 +382,24 @@ __global__ void __launch_bounds__(kI8Threads) gemv_i8_kernel(
     __syncthreads();
 
     // ---- partial sums of the 8 waves, in wave order ----
-    for (int e = tid; e < T * kWave; e += kI8Threads) {
+    for (int e = tid; e < Th * kWave; e += kI8Threads) {
         const int t = e / kWave, l = e % kWave;
         float v = 0.0f;
 #pragma unroll
         for (int ww = 0; ww < kI8Waves; ++ww) v += red[(ww * T + t) * kWave + l];
+        float u = 0.0f;
+        if (GLU) {
+#pragma unroll
+            for (int ww = 0; ww < kI8Waves; ++ww) u += red[(ww * T + Th + t) * kWave + l];
+        }
         const int row = 16 * t + (l & 15), tk = l >> 4;
         if (tk < M && row < R) {
             const int gr = r0 + row;
             if (bias) v += bf16_to_f32(bias[gr]);
+            if (GLU) {
+                if (bias) u += bf16_to_f32(bias[up0 + gr]);
+                v = v * u / (1.0f + expf(-v));  // SiLU(g) u
+            }
             store_out(y, static_cast<int64_t>(tk) * ldy + gr, v, out_f32 != 0);
         }
     }
@@ -384,29 +425,33 @@ struct I8Plan {
 // tile: its missing rows read zeros and cost no memory traffic), at most kI8MaxTiles tiles and
 // at most as many rows as the prologue reads scales for. Every block gets the same number of
 // rows, so that no compute unit carries two slices while others carry one.
-I8Plan plan_i8(int64_t d_out, int64_t n128, int64_t n_groups) {
+// (glu: d_out counts output rows, each with a gate and an up row: half of the tiles and half of
+// the table loads per half)
+I8Plan plan_i8(int64_t d_out, int64_t n128, int64_t n_groups, bool glu = false) {
     I8Plan p{};
+    const int halves = glu ? 2 : 1;
     const int64_t blocks = (int64_t)device_cu_count() * i8_blocks_per_cu(n128);
     int64_t rpb = (d_out + blocks - 1) / blocks;
-    int64_t cap = (int64_t)kI8TableLoads * kI8Threads / n_groups;
-    if (cap > 16 * kI8MaxTiles) cap = 16 * kI8MaxTiles;
+    int64_t cap = (int64_t)kI8TableLoads / halves * kI8Threads / n_groups;
+    if (cap > 16 * kI8MaxTiles / halves) cap = 16 * kI8MaxTiles / halves;
     if (rpb > cap) rpb = cap;
     if (rpb < 1) rpb = 1;
     p.rows_per_block = static_cast<int>(rpb);
     p.blocks = static_cast<int>((d_out + rpb - 1) / rpb);
-    p.T = static_cast<int>((rpb + 15) / 16);
+    p.T = halves * static_cast<int>((rpb + 15) / 16);
     return p;
 }
 
-template <int M, bool ZP, int XP>
+template <int M, bool ZP, int XP, bool GLU>
 hipError_t launch_i8_t(const uint16_t *x, int64_t ldx, const uint8_t *qweight,
                        const uint16_t *scales, const uint16_t *zeros, const uint16_t *bias,
                        int64_t d_out, int64_t d_in, int64_t k_pad, int64_t n_groups, int gshift,
                        void *y, int64_t ldy, bool out_f32, hipStream_t stream) {
     const int n128 = static_cast<int>(k_pad / 128);
-    const I8Plan p = plan_i8(d_out, n128, n_groups);
+    const I8Plan p = plan_i8(d_out, n128, n_groups, GLU);
     const size_t lds = i8_lds(M, n128, static_cast<int>(n_groups), p.T, ZP).total;
-    hipLaunchKernelGGL((gemv_i8_kernel<M, ZP, XP>), dim3(p.blocks), dim3(kI8Threads), lds, stream, x,
+    hipLaunchKernelGGL((gemv_i8_kernel<M, ZP, XP, GLU>), dim3(p.blocks), dim3(kI8Threads), lds,
+                       stream, x,
                        ldx, qweight, scales, zeros, bias, static_cast<int>(d_out),
                        static_cast<int>(d_in), static_cast<int>(k_pad / 2), n128,
                        static_cast<int>(n_groups), gshift, p.rows_per_block, y, ldy,
@@ -435,17 +480,19 @@ bool gemv_i8_preferred(int64_t M, int64_t d_out, int64_t k_pad) {
 }
 
 bool gemv_i8_supported(int64_t M, int64_t d_out, int64_t d_in, int64_t k_pad, int64_t span,
-                       int64_t n_groups, int64_t ldx) {
+                       int64_t n_groups, int64_t ldx, bool glu) {
     if (M < 1 || M > kI8MaxTokens) return false;
     if (k_pad % 128 != 0 || d_in > k_pad || d_in > 65536) return false;
     // every 128-column group lies inside one quantization group
     if (n_groups != 1 && span != 128 && span != 256) return false;
     const int64_t n128 = k_pad / 128;
     if (M * n128 * 16 > (int64_t)kI8MaxPasses * kI8Threads) return false;
-    if (d_out < 1 || d_out > (int64_t(1) << 24) || n_groups > kI8TableLoads * kI8Threads)
+    const int64_t table_loads = glu ? kI8TableLoads / 2 : kI8TableLoads;  // per half
+    if (d_out < 1 || d_out * (glu ? 2 : 1) > (int64_t(1) << 24) ||
+        n_groups > table_loads * kI8Threads)
         return false;
-    const I8Plan p = plan_i8(d_out, n128, n_groups);
-    if ((int64_t)p.rows_per_block * n_groups > (int64_t)kI8TableLoads * kI8Threads) return false;
+    const I8Plan p = plan_i8(d_out, n128, n_groups, glu);
+    if ((int64_t)p.rows_per_block * n_groups > table_loads * kI8Threads) return false;
     if (i8_lds(static_cast<int>(M), static_cast<int>(n128), static_cast<int>(n_groups), p.T,
                true).total > kI8LdsLimit)
         return false;
@@ -458,17 +505,18 @@ bool gemv_i8_supported(int64_t M, int64_t d_out, int64_t d_in, int64_t k_pad, in
 hipError_t launch_gemv_i8(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
                           const uint16_t *scales, const uint16_t *zeros, const uint16_t *bias,
                           int64_t d_out, int64_t d_in, int64_t k_pad, int64_t span,
-                          int64_t n_groups, void *y, int64_t ldy, bool out_f32,
+                          int64_t n_groups, void *y, int64_t ldy, bool out_f32, bool glu,
                           hipStream_t stream) {
     const int gshift = n_groups == 1 ? 30 : (span == 256 ? 1 : 0);
     const bool zp = zeros != nullptr;
     const int64_t items = M * (k_pad / 128) * 16;
     const int xp = items <= kI8Threads ? 1 : items <= 2 * kI8Threads ? 2 : items <= 4 * kI8Threads ? 4 : 8;
-#define W4_I8_ZP(MV, XPV)                                                                        \
-    return zp ? launch_i8_t<MV, true, XPV>(x, ldx, qweight, scales, zeros, bias, d_out, d_in,    \
+#define W4_I8_GLU(MV, ZPV, XPV)                                                                  \
+    (glu ? launch_i8_t<MV, ZPV, XPV, true>(x, ldx, qweight, scales, zeros, bias, d_out, d_in,    \
                                            k_pad, n_groups, gshift, y, ldy, out_f32, stream)     \
-              : launch_i8_t<MV, false, XPV>(x, ldx, qweight, scales, zeros, bias, d_out, d_in,   \
-                                            k_pad, n_groups, gshift, y, ldy, out_f32, stream);
+         : launch_i8_t<MV, ZPV, XPV, false>(x, ldx, qweight, scales, zeros, bias, d_out, d_in,   \
+                                            k_pad, n_groups, gshift, y, ldy, out_f32, stream))
+#define W4_I8_ZP(MV, XPV) return zp ? W4_I8_GLU(MV, true, XPV) : W4_I8_GLU(MV, false, XPV);
 #define W4_I8_CASE(MV)                                                                           \
     case MV:                                                                                     \
         if (xp == 1) W4_I8_ZP(MV, 1)                                                             \
@@ -485,6 +533,7 @@ hipError_t launch_gemv_i8(const uint16_t *x, int64_t M, int64_t ldx, const uint8
     }
 #undef W4_I8_ZP
 #undef W4_I8_CASE
+#undef W4_I8_GLU
 }
 
 }  // namespace w4

@@ -65,13 +65,15 @@ hipError_t launch_gemv_mfma(const uint16_t *x, int64_t M, int64_t ldx, const uin
 
 // One to four tokens on the int8 matrix cores (decode_i8.hip): activations as exact integer
 // digits prepared inside each block, raw codes as the other operand; no workspace.
+// glu: the fused gate/up GEMV with the SiLU(gate) * up epilogue (2 d_out weight rows, d_out
+// outputs).
 bool gemv_i8_supported(int64_t M, int64_t d_out, int64_t d_in, int64_t k_pad, int64_t span,
-                       int64_t n_groups, int64_t ldx);
+                       int64_t n_groups, int64_t ldx, bool glu = false);
 bool gemv_i8_preferred(int64_t M, int64_t d_out, int64_t k_pad);
 hipError_t launch_gemv_i8(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
                           const uint16_t *scales, const uint16_t *zeros, const uint16_t *bias,
                           int64_t d_out, int64_t d_in, int64_t k_pad, int64_t span,
-                          int64_t n_groups, void *y, int64_t ldy, bool out_f32,
+                          int64_t n_groups, void *y, int64_t ldy, bool out_f32, bool glu,
                           hipStream_t stream);
 
 // Number of compute units of the current device (cached per device).

@@ -87,6 +87,8 @@ def _declare(lib):
     lib.oracle_act_quant.restype = None
     lib.oracle_w4a8.argtypes = [_p, _p, _i64, _i64, _p, _p, _p, _i64, _i64, _p, _p]
     lib.oracle_w4a8.restype = _i64
+    lib.oracle_silu_mul.argtypes = [_p, _p, _i64, _p]
+    lib.oracle_silu_mul.restype = None
     return lib
 
 
@@ -212,6 +214,26 @@ def w4a8(q, s_x, qweight, s_w, bias_bits, d_in):
     n = lib.oracle_w4a8(_ptr(q), _ptr(s_x), M, ldq, _ptr(qw), _ptr(sw), _ptr(b), d_out, d_in,
                         _ptr(acc), _ptr(y))
     return acc, y, int(n)
+
+
+def silu_mul(g, u):
+    """O7: h = SiLU(g) * u elementwise (fp64), SiLU(v) = v / (1 + exp(-v))."""
+    lib = _load()
+    g = _c(g, np.float64)
+    u = _c(u, np.float64)
+    if g.shape != u.shape:
+        raise ValueError("g and u must have the same shape")
+    h = np.zeros(g.shape, dtype=np.float64)
+    lib.oracle_silu_mul(_ptr(g), _ptr(u), g.size, _ptr(h))
+    return h
+
+
+def w4a16_silu_mul(x_bits, qweight, scales, zeros, bias_bits, d_in, group_size):
+    """O4 then O7 on a fused gate/up weight of 2H rows (gate rows [0, H), up rows [H, 2H)):
+    h [M][H] fp64."""
+    y = w4a16(x_bits, qweight, scales, zeros, bias_bits, d_in, group_size)
+    H = y.shape[1] // 2
+    return silu_mul(y[:, :H], y[:, H:])
 
 
 def tolerance_ok(y, y_ref, rel=2e-3):

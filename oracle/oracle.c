@@ -322,3 +322,16 @@ int64_t oracle_w4a8(const int8_t *q, const float *s_x, int64_t M, int64_t ldq,
     }
     return overflow;
 }
+
+/* ------------------------------------------------------------------------------------------ */
+/* O7: the gate of the MLP.  [Lab5 基础]: FFN(x) = W_down [SiLU(W_gate x) (.) (W_up x)] with      */
+/* SiLU(v) = v sigma(v) = v / (1 + exp(-v)).  Given the two linear outputs g = W_gate x (+ b_gate) */
+/* and u = W_up x (+ b_up) (O4 of the two halves of a fused gate/up weight), h_i = SiLU(g_i) u_i,  */
+/* in fp64.                                                                                       */
+/* ------------------------------------------------------------------------------------------ */
+void oracle_silu_mul(const double *g, const double *u, int64_t n, double *h) {
+    for (int64_t i = 0; i < n; ++i) {
+        const double sigma = 1.0 / (1.0 + exp(-g[i]));
+        h[i] = g[i] * sigma * u[i];
+    }
+}

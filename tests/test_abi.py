@@ -33,6 +33,7 @@ def lib():
     L.w4_pack.argtypes = [p, i64, i64, i64, i32, i32, p, p, p, p]
     lin = [p, i64, i64, p, p, p, p, i64, i64, i32, p, i64, i32]
     L.w4_gemv.argtypes = lin + [p]
+    L.w4_gemv_glu.argtypes = lin + [p]
     L.w4_gemm.argtypes = lin + [p]
     L.act_quant_int8.argtypes = [p, i64, i64, i64, p, i64, p, p, p]
     L.w4a8_gemv.argtypes = [p, p, i64, i64, p, p, p, i64, i64, p, i64, i32, p, p]
@@ -44,7 +45,8 @@ def lib():
 
 def test_header_declares_the_five_entry_points():
     names = declared_functions()
-    for n in ("w4_pack", "w4_gemv", "w4_gemm", "act_quant_int8", "w4a8_gemv", "w4a8_linear",
+    for n in ("w4_pack", "w4_gemv", "w4_gemv_glu", "w4_gemm", "act_quant_int8", "w4a8_gemv",
+              "w4a8_linear",
               "w4_packed_layout", "w4_status_string",
               "w4_last_hip_error"):
         assert n in names
@@ -207,3 +209,18 @@ def test_w4a8_linear_rejects_bad_arguments(lib):
     assert call(d_in=big, ldx=big) == W4_ERR_RANGE
     # rows longer than the fused kernel's activation stage: the two-call path serves them
     assert call(d_in=60000, ldx=60000) == W4_ERR_UNSUPPORTED
+
+
+def test_gemv_glu_rejects_bad_arguments(lib):
+    f = lib.w4_gemv_glu
+    assert _lin(f, x=None) == W4_ERR_NULL
+    assert _lin(f, M=0) == W4_ERR_SHAPE
+    assert _lin(f, d_out=0) == W4_ERR_SHAPE
+    assert _lin(f, ldy=64) == W4_ERR_SHAPE
+    assert _lin(f, g=96) == W4_ERR_GROUP
+    assert _lin(f, x=A + 8) == W4_ERR_ALIGN
+    assert _lin(f, zr=E + 1) == W4_ERR_ALIGN
+    # shapes the fused kernel does not serve: more than 4 tokens, 32- and 64-column groups
+    assert _lin(f, M=5, g=128) == W4_ERR_UNSUPPORTED
+    assert _lin(f, g=32) == W4_ERR_UNSUPPORTED
+    assert _lin(f, g=64) == W4_ERR_UNSUPPORTED

@@ -332,6 +332,71 @@ def test_linear_zero_points_beyond_pack(entry, monkeypatch):
             check_linear(entry, x, ph2, pd2, b, d_in, g, f"z beyond pack M={M} path={path}")
 
 
+def _glu_bound(x_bits, ph, bias_bits, d_in, g):
+    """Tolerance of h = SiLU(g) u, derived from the linear tolerance tau(v) = 2e-3 (1 + |v|) on g
+    and u: |dh| <= max|SiLU'| tau(g) (|u| + tau(u)) + (|SiLU(g)| + max|SiLU'| tau(g)) tau(u),
+    max|SiLU'| < 1.1, plus 2^-20 |h| for the fp32 epilogue (exp, division, products)."""
+    y = oracle.w4a16(x_bits, ph[0], ph[1], ph[2], bias_bits, d_in, g)
+    H = y.shape[1] // 2
+    gr, ur = y[:, :H], y[:, H:]
+    h_ref = oracle.silu_mul(gr, ur)
+    tg, tu = 2e-3 * (1 + np.abs(gr)), 2e-3 * (1 + np.abs(ur))
+    s = np.abs(oracle.silu_mul(gr, np.ones_like(gr)))
+    bound = 1.1 * tg * (np.abs(ur) + tu) + (s + 1.1 * tg) * tu + 2.0 ** -20 * np.abs(h_ref)
+    return h_ref, bound
+
+
+def check_glu(w, x_bits, bias_bits, g, mode, what, ldx=None):
+    _announce("w4_gemv_glu", what, w.shape, x_bits.shape, g, mode)
+    ph, pd = check_pack_bit_exact(w, g, mode, what)
+    d_in = w.shape[1]
+    M = x_bits.shape[0]
+    xb = x_bits
+    if ldx is not None and ldx > d_in:
+        xb = np.full((M, ldx), 0x7FC0, dtype=np.uint16)  # NaN past d_in: never read
+        xb[:, :d_in] = x_bits
+    x = dev_bf16(xb)
+    b = dev_bf16(bias_bits) if bias_bits is not None else None
+    h32 = w4.w4_gemv_glu(x, *pd, b, d_in, g, F32)
+    h16 = w4.w4_gemv_glu(x, *pd, b, d_in, g, BF16)
+    torch.cuda.synchronize()
+    h_ref, bound = _glu_bound(x_bits, ph, bias_bits, d_in, g)
+    h = host(h32).astype(np.float64)
+    bad = np.abs(h - h_ref) > bound
+    assert not bad.any(), f"{what}: {bad.sum()} outputs outside the derived bound"
+    assert_bf16_is_rne_of_f32(h16, host(h32), what)
+
+
+def test_gemv_glu_c2_gate_up_full_size():
+    """The C2 gate/up weight (37888 x 3584, g128 SYM, outliers) as a fused gate/up: h = SiLU of
+    rows [0, 18944) times rows [18944, 37888)."""
+    cfg = workloads.C2
+    gu = cfg.linears[0]
+    w = workloads.linear_weight(cfg, 0)
+    x = workloads.linear_x(cfg, 0, 1)
+    check_glu(w, x, None, gu.group_size, gu.mode, "C2 gate/up")
+
+
+@pytest.mark.parametrize("g", [128, 256, 0])
+@pytest.mark.parametrize("mode", [SYM, ASYM])
+def test_gemv_glu_ragged(g, mode):
+    """1-4 tokens, ragged d_ff and d_in (NaN past d_in), with and without bias."""
+    for M, d_ff, d_in in ((1, 1, 100), (2, 37, 1000), (3, 130, 3600), (4, 300, 4100)):
+        w = workloads.weight(43, M + d_ff + g, 2 * d_ff, d_in)
+        x = workloads.activations(43, g + mode, M, d_in)
+        b = workloads.bias(43, 1, 2 * d_ff) if M % 2 else None
+        if oracle.k_pad(d_in, g) % 128:  # one group per row, rows not whole 128-column groups
+            _, pd = check_pack_bit_exact(w, g, mode, "glu unsupported")
+            xp = np.zeros((M, (d_in + 7) // 8 * 8), dtype=np.uint16)
+            xp[:, :d_in] = x
+            with pytest.raises(w4.W4Error) as err:
+                w4.w4_gemv_glu(dev_bf16(xp), *pd, None, d_in, g, F32)
+            assert err.value.status == 6  # W4_ERR_UNSUPPORTED, the documented limit
+            continue
+        check_glu(w, x, b, g, mode, f"M={M} d_ff={d_ff} d_in={d_in}",
+                  ldx=(d_in + 7) // 8 * 8 + 8)
+
+
 @pytest.mark.parametrize("entry", ["w4_gemv", "w4_gemm"])
 def test_linear_deterministic(entry):
     d_out, d_in, g = 1000, 3584, 128

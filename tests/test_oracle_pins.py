@@ -413,3 +413,53 @@ def test_w4a8_end_to_end_within_quantization_bound():
     assert np.all(np.abs(y[0] - ref) <= bound * (1 + 1e-9) + 1e-9)
     assert np.all(np.abs(xf - xq) <= float(s_x[0]) / 2 * (1 + 1e-6))
     assert np.all(sw > 0)
+
+
+# ------------------------------------------------------------------------------------------
+# O7: the gate of the MLP [Lab5 基础]: FFN(x) = W_down [SiLU(W_gate x) (.) (W_up x)],
+# SiLU(v) = v sigma(v)
+# ------------------------------------------------------------------------------------------
+def test_silu_mul_closed_forms():
+    """sigma(ln 3) = 3/4 and sigma(-ln 3) = 1/4, so SiLU(+-ln 3) = +-ln 3 * {3/4, 1/4}; sigma(0) =
+    1/2; the logistic function at 1 is 0.7310585786300049 (e / (1 + e))."""
+    import math
+    ln3 = math.log(3.0)
+    g = np.array([ln3, -ln3, 0.0, 1.0, -1.0])
+    h = oracle.silu_mul(g, np.ones_like(g))
+    e = math.e
+    want = [ln3 * 0.75, -ln3 * 0.25, 0.0, e / (1 + e), -1.0 / (1 + e)]
+    assert np.allclose(h, want, rtol=1e-15, atol=0)
+    assert abs(h[3] - 0.7310585786300049) <= 1e-16
+
+
+def test_silu_mul_identities_and_limits():
+    """SiLU(v) - SiLU(-v) = v (sigma(v) + sigma(-v) = 1); SiLU(v) -> v for large v and -> 0- for
+    very negative v; h is linear in u; SiLU(v) >= -0.2785 (its minimum, at v = -1.2785)."""
+    v = np.linspace(-30.0, 30.0, 601)
+    one = np.ones_like(v)
+    d = oracle.silu_mul(v, one) - oracle.silu_mul(-v, one)
+    assert np.allclose(d, v, rtol=0, atol=1e-12)
+    big = oracle.silu_mul(np.array([40.0, -40.0, -800.0]), np.ones(3))
+    assert big[0] == 40.0 and -1e-15 < big[1] < 0.0 and big[2] == 0.0
+    u = np.random.default_rng(7).normal(size=v.shape)
+    assert np.allclose(oracle.silu_mul(v, 2.0 * u), 2.0 * oracle.silu_mul(v, u), rtol=1e-15)
+    assert oracle.silu_mul(v, one).min() >= -0.27846454276107
+
+
+def test_w4a16_silu_mul_takes_gate_then_up():
+    """A fused gate/up weight is gate rows [0, H) then up rows [H, 2H): with x = e_k the result is
+    SiLU(w_hat_gate[j][k]) * w_hat_up[j][k], computed here in Python floats from the dequantized
+    weights (each row pair has distinct gate and up values, so swapped halves fail)."""
+    import math
+    H, d_in = 8, 64
+    w = workloads.weight(41, 0, 2 * H, d_in)
+    w[:H] *= 40.0  # gate values far from the up values
+    qw, sc, zr = oracle.pack(w, 32, ASYM)
+    wh = oracle.dequant(qw, sc, zr, d_in, 32)
+    for k in (0, 5, 33, 63):
+        x = np.zeros((1, d_in), dtype=np.uint16)
+        x[0, k] = 0x3F80
+        h = oracle.w4a16_silu_mul(x, qw, sc, zr, None, d_in, 32)[0]
+        for j in range(H):
+            g, u = float(wh[j, k]), float(wh[H + j, k])
+            assert abs(h[j] - g / (1.0 + math.exp(-g)) * u) <= 1e-12 * (1.0 + abs(h[j]))
