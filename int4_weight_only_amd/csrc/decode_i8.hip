@@ -79,9 +79,11 @@ __host__ __device__ inline I8Lds i8_lds(int M, int n128, int n_groups, int T, bo
 // GLU: the gate of the MLP fused into the epilogue ([Lab5 基础]: FFN(x) = W_down [SiLU(W_gate x)
 // (.) (W_up x)]; [Orin 后续还能继续优化什么] names this kernel boundary). The weight holds 2 d_out
 // rows, gate rows [0, d_out) then up rows [d_out, 2 d_out) (bias likewise, if given); a block's
-// slice is output rows [r0, r0 + R): its first T/2 tiles are those gate rows, the last T/2 the
-// up rows, each half through its own descriptor and LDS table half. The store writes
-// SiLU(g) u = g u / (1 + exp(-g)) in fp32.
+// slice is output rows [r0, r0 + R), and tile t holds gate rows r0 + 8t .. + 7 in its rows 0..7
+// and the matching up rows in its rows 8..15, so a slice takes as many tiles as a plain slice of
+// 2R rows. One descriptor spans the gate rows to the end of the up rows; a lane whose row lies
+// past R reads zeros. The store combines lanes n and n + 8 of a tile: SiLU(g) u =
+// g u / (1 + exp(-g)) in fp32.
 template <int M, bool ZP, int XP, bool GLU>
 __global__ void __launch_bounds__(kI8Threads) gemv_i8_kernel(
     const uint16_t *__restrict__ x, int64_t ldx, const uint8_t *__restrict__ qweight,
@@ -95,8 +97,7 @@ __global__ void __launch_bounds__(kI8Threads) gemv_i8_kernel(
     const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int r0 = blockIdx.x * rows_per_block;
     const int R = d_out - r0 < rows_per_block ? d_out - r0 : rows_per_block;  // >= 1
-    const int Th = (R + 15) >> 4;  // tiles of one half (GLU) or of the slice
-    const int T = GLU ? 2 * Th : Th;
+    const int T = GLU ? (R + 7) >> 3 : (R + 15) >> 4;
     const I8Lds L = i8_lds(M, n128, n_groups, T, ZP);
     // units are dealt in pairs: wave w takes units 16 m + 2 w and 16 m + 2 w + 1 (m = 0, 1, ...)
     // below U, so its two loads of a pair cover the same 128-byte lines
@@ -149,8 +150,10 @@ __global__ void __launch_bounds__(kI8Threads) gemv_i8_kernel(
     // (tile t, group G); from k to k + 1, u grows by 1 (k even) or by 15 (k odd) ----
     const uint32_t rb = static_cast<uint32_t>(row_bytes);
     const rsrc_t rq = make_rsrc(qweight + (int64_t)r0 * row_bytes, static_cast<uint32_t>(R) * rb);
-    const rsrc_t rq2 = make_rsrc(qweight + (up0 + r0) * row_bytes,
-                                 GLU ? static_cast<uint32_t>(R) * rb : 0u);
+    // (GLU: the gate rows of the slice through the end of its up rows; the host keeps this below
+    // 2^31 bytes)
+    const rsrc_t rqg = make_rsrc(qweight + (int64_t)r0 * row_bytes,
+                                 GLU ? static_cast<uint32_t>(up0 + R) * rb : 0u);
     const int jump = 2 * kI8Waves - 1;
     const int dt = jump / n128, dG = jump % n128;
     // offsets = a per-lane part (row n of the tile, k-block q) + a wave-uniform part (tile t,
@@ -159,15 +162,17 @@ __global__ void __launch_bounds__(kI8Threads) gemv_i8_kernel(
     // ring. Such units may step past the last tile: t is clamped to T, so that every offset
     // stays below 2^31 before bit 31 is added (the host checks 16 (T + 1) rows) and the sum
     // cannot wrap around into the range.
-    const uint32_t w_lane = static_cast<uint32_t>(n) * rb + 16u * q;
+    const uint32_t w_lane =
+        GLU ? static_cast<uint32_t>(n < 8 ? n : up0 + n - 8) * rb + 16u * q
+            : static_cast<uint32_t>(n) * rb + 16u * q;
     auto load = [&](int k, int t, int G, u32x4_t &dst) {
         const uint32_t past = static_cast<uint32_t>((nu - 1 - k) >> 31) << 31;
-        uint32_t tc = static_cast<uint32_t>(t < T ? t : T);
-        if (GLU && tc >= static_cast<uint32_t>(Th)) {  // an up tile (the clamp lands past R)
-            tc -= static_cast<uint32_t>(Th);
+        const uint32_t tc = static_cast<uint32_t>(t < T ? t : T);
+        if (GLU) {  // 8 rows per half per tile; a lane past the slice's R rows reads zeros
             const uint32_t wo =
-                w_lane + ((16u * tc * rb + 64u * static_cast<uint32_t>(G)) | past);
-            dst = __builtin_amdgcn_raw_buffer_load_b128(rq2, wo, 0, 0);
+                w_lane + ((8u * tc * rb + 64u * static_cast<uint32_t>(G)) | past);
+            const bool in = static_cast<int>(8 * tc) + (n & 7) < R;
+            dst = __builtin_amdgcn_raw_buffer_load_b128(rqg, in ? wo : kOutOfRange, 0, 0);
             return;
         }
         const uint32_t wo = w_lane + ((16u * tc * rb + 64u * static_cast<uint32_t>(G)) | past);
@@ -199,16 +204,23 @@ __global__ void __launch_bounds__(kI8Threads) gemv_i8_kernel(
     // ---- tables, partial sums ----
     uint16_t *sct = reinterpret_cast<uint16_t *>(lds + L.sct);
     uint16_t *zct = reinterpret_cast<uint16_t *>(lds + L.zct);
-    const int up_table = 16 * Th * n_groups;  // GLU: the up rows' table starts at tile Th
 #pragma unroll
     for (int i = 0; i < TL; ++i) {
         const int idx = tid + i * kI8Threads;
         if (idx < nsc) {
-            sct[idx] = static_cast<uint16_t>(sv[i]);
-            if (ZP) zct[idx] = static_cast<uint16_t>(zv[ZP ? i : 0]);
-            if (GLU) {
-                sct[up_table + idx] = static_cast<uint16_t>(sv2[GLU ? i : 0]);
-                if (ZP) zct[up_table + idx] = static_cast<uint16_t>(zv2[GLU && ZP ? i : 0]);
+            if (GLU) {  // slice row r sits in table row 16 (r / 8) + r % 8 (gate), + 8 (up)
+                const int r = idx / n_groups;
+                const int tg = (16 * (r >> 3) + (r & 7)) * n_groups + (idx - r * n_groups);
+                const int tu = tg + 8 * n_groups;
+                sct[tg] = static_cast<uint16_t>(sv[i]);
+                sct[tu] = static_cast<uint16_t>(sv2[GLU ? i : 0]);
+                if (ZP) {
+                    zct[tg] = static_cast<uint16_t>(zv[ZP ? i : 0]);
+                    zct[tu] = static_cast<uint16_t>(zv2[GLU && ZP ? i : 0]);
+                }
+            } else {
+                sct[idx] = static_cast<uint16_t>(sv[i]);
+                if (ZP) zct[idx] = static_cast<uint16_t>(zv[ZP ? i : 0]);
             }
         }
     }
@@ -382,17 +394,18 @@ __global__ void __launch_bounds__(kI8Threads) gemv_i8_kernel(
     __syncthreads();
 
     // ---- partial sums of the 8 waves, in wave order ----
-    for (int e = tid; e < Th * kWave; e += kI8Threads) {
+    for (int e = tid; e < T * kWave; e += kI8Threads) {
         const int t = e / kWave, l = e % kWave;
+        if (GLU && (l & 15) >= 8) continue;  // up rows: combined by the lane 8 below
         float v = 0.0f;
 #pragma unroll
         for (int ww = 0; ww < kI8Waves; ++ww) v += red[(ww * T + t) * kWave + l];
         float u = 0.0f;
         if (GLU) {
 #pragma unroll
-            for (int ww = 0; ww < kI8Waves; ++ww) u += red[(ww * T + Th + t) * kWave + l];
+            for (int ww = 0; ww < kI8Waves; ++ww) u += red[(ww * T + t) * kWave + l + 8];
         }
-        const int row = 16 * t + (l & 15), tk = l >> 4;
+        const int row = GLU ? 8 * t + (l & 15) : 16 * t + (l & 15), tk = l >> 4;
         if (tk < M && row < R) {
             const int gr = r0 + row;
             if (bias) v += bf16_to_f32(bias[gr]);
@@ -425,8 +438,8 @@ struct I8Plan {
 // tile: its missing rows read zeros and cost no memory traffic), at most kI8MaxTiles tiles and
 // at most as many rows as the prologue reads scales for. Every block gets the same number of
 // rows, so that no compute unit carries two slices while others carry one.
-// (glu: d_out counts output rows, each with a gate and an up row: half of the tiles and half of
-// the table loads per half)
+// (glu: d_out counts output rows, each with a gate and an up row: 8 output rows per tile and
+// half of the table loads for each of the two)
 I8Plan plan_i8(int64_t d_out, int64_t n128, int64_t n_groups, bool glu = false) {
     I8Plan p{};
     const int halves = glu ? 2 : 1;
@@ -436,9 +449,10 @@ I8Plan plan_i8(int64_t d_out, int64_t n128, int64_t n_groups, bool glu = false) 
     if (cap > 16 * kI8MaxTiles / halves) cap = 16 * kI8MaxTiles / halves;
     if (rpb > cap) rpb = cap;
     if (rpb < 1) rpb = 1;
+    const int rows_per_tile = 16 / halves;
     p.rows_per_block = static_cast<int>(rpb);
     p.blocks = static_cast<int>((d_out + rpb - 1) / rpb);
-    p.T = halves * static_cast<int>((rpb + 15) / 16);
+    p.T = static_cast<int>((rpb + rows_per_tile - 1) / rows_per_tile);
     return p;
 }
 
@@ -499,7 +513,9 @@ bool gemv_i8_supported(int64_t M, int64_t d_out, int64_t d_in, int64_t k_pad, in
     // 31-bit offsets: the activations of the tile and the weight rows of a block (up to one
     // tile past the block's last, where the units past a wave's share are clamped)
     if (((M - 1) * ldx + k_pad) * 2 >= (int64_t)kOutOfRange) return false;
-    return (int64_t)(16 * (p.T + 1)) * (k_pad / 2) < (int64_t)kOutOfRange;
+    // (glu: the slice's descriptor spans the gate rows to the end of its up rows)
+    const int64_t rows_spanned = glu ? d_out + 8 * (p.T + 1) : 16 * (p.T + 1);
+    return rows_spanned * (k_pad / 2) < (int64_t)kOutOfRange;
 }
 
 hipError_t launch_gemv_i8(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
