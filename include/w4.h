@@ -179,8 +179,8 @@ int w4a8_gemv(const int8_t *q, const float *s_x, int64_t M, int64_t ldq, const u
  *   qweight, s_w, bias, y, out_dtype, acc: as for w4a8_gemv
  *   s_x      fp32 [M] or NULL: receives the token scales
  * The codes, s_x and acc are bit-identical to those of act_quant_int8 + w4a8_gemv on the same x.
- * Every workgroup quantizes the whole activation row it needs; rows longer than the kernel's LDS
- * stage (about 43,000 columns for one token) return W4_ERR_UNSUPPORTED: use the two calls.
+ * Every workgroup quantizes the whole activation row it needs; rows longer than the kernel's
+ * activation stage (k_pad > 32768) return W4_ERR_UNSUPPORTED: use the two calls.
  */
 int w4a8_linear(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
                 const uint16_t *s_w, const uint16_t *bias, int64_t d_out, int64_t d_in, void *y,

@@ -397,6 +397,26 @@ def test_gemv_glu_ragged(g, mode):
                   ldx=(d_in + 7) // 8 * 8 + 8)
 
 
+def test_linear_maximum_reduction_length():
+    """d_in = 65536, the decode entry points' limit (and far past every config): the decode
+    paths (one token, few tokens, both group modes), the gate epilogue, W4A8 (two calls and
+    fused; |acc| reaches 65536 * 8 * 127 = 66.6 M, well inside int32) and the GEMM."""
+    d_in, d_out = 65536, 48
+    for g, mode in ((128, ASYM), (32, SYM)):
+        w = workloads.weight(47, g, d_out, d_in)
+        ph, pd = check_pack_bit_exact(w, g, mode, f"d_in=65536 g={g}")
+        for M in (1, 5, 64):
+            x = workloads.activations(47, M, M, d_in)
+            check_linear("w4_gemv", x, ph, pd, None, d_in, g, f"d_in=65536 M={M} g={g}")
+        x = workloads.activations(47, 99, 130, d_in)
+        check_linear("w4_gemm", x, ph, pd, None, d_in, g, f"d_in=65536 M=130 g={g}")
+    w = workloads.weight(48, 0, 2 * d_out, 16384)
+    check_glu(w, workloads.activations(48, 1, 1, 16384), None, 128, ASYM, "glu d_in=16384")
+    w = workloads.weight(49, 0, d_out, d_in)
+    x = workloads.activations(49, 3, 3, d_in, 0.01, 20.0)
+    check_w4a8(w, x, workloads.bias(49, 1, d_out), "w4a8 d_in=65536")
+
+
 @pytest.mark.parametrize("entry", ["w4_gemv", "w4_gemm"])
 def test_linear_deterministic(entry):
     d_out, d_in, g = 1000, 3584, 128
@@ -483,6 +503,11 @@ def check_w4a8(w, x_bits, bias_bits, what):
     xj = np.full((x_bits.shape[0], ldx), 0x7FC0, dtype=np.uint16)
     xj[:, :d_in] = x_bits
     xd = dev_bf16(xj)
+    if oracle.k_pad(d_in, 0) > 32768:  # past the fused kernel's activation stage (documented)
+        with pytest.raises(w4.W4Error) as err:
+            w4.w4a8_linear(xd, pd[0], pd[1], b, d_in, F32)
+        assert err.value.status == 6  # W4_ERR_UNSUPPORTED
+        return
     y32f, accf, sxf = w4.w4a8_linear(xd, pd[0], pd[1], b, d_in, F32, want_acc=True,
                                      want_scales=True)
     y16f = w4.w4a8_linear(xd, pd[0], pd[1], b, d_in, BF16)
