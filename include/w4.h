@@ -186,6 +186,22 @@ int w4a8_linear(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweigh
                 const uint16_t *s_w, const uint16_t *bias, int64_t d_out, int64_t d_in, void *y,
                 int64_t ldy, int out_dtype, float *s_x, int32_t *acc, void *stream);
 
+/*
+ * w4a8_gemm -- W4A8 prefill linear for any M >= 1: the arguments and the result of w4a8_gemv
+ * (acc bit-identical, y within the same rounding), for token counts where the weight tile is
+ * reused across many tokens.
+ * [Orin 从 FP 线性层到 INT4 DP4A 的数学推导] (the integer form of the linear layer),
+ * [Infra 2.3] (int8 products with int32 accumulation for the compute-bound large-batch case).
+ * The codes (0..15) and the int8 activations are multiplied on the int8 matrix cores as they
+ * are; sum_k 8 q[m][k] is subtracted per token from the int32 sums, so acc is exact.
+ *   q, s_x, qweight, s_w, bias, y, out_dtype, acc: as for w4a8_gemv, with any M >= 1
+ * Limits (W4_ERR_RANGE beyond them): M <= W4_MAX_DIM, d_in <= W4_MAX_W4A8_D_IN, M * ldq < 2^31
+ * and d_out * k_pad / 2 < 2^31 (32-bit buffer offsets).
+ */
+int w4a8_gemm(const int8_t *q, const float *s_x, int64_t M, int64_t ldq, const uint8_t *qweight,
+              const uint16_t *s_w, const uint16_t *bias, int64_t d_out, int64_t d_in, void *y,
+              int64_t ldy, int out_dtype, int32_t *acc, void *stream);
+
 /* Text for a w4_status value (static storage). */
 const char *w4_status_string(int status);
 

@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "W4_SYM", "W4_ASYM", "W4_OUT_BF16", "W4_OUT_F32", "W4Error", "packed_layout", "w4_pack",
-    "w4_gemv", "w4_gemv_glu", "w4_gemm", "act_quant_int8", "w4a8_gemv", "w4a8_linear",
+    "w4_gemv", "w4_gemv_glu", "w4_gemm", "act_quant_int8", "w4a8_gemv", "w4a8_gemm", "w4a8_linear",
     "w4_linear",
     "library_path",
 ]
@@ -51,9 +51,10 @@ def _load():
     lib.w4_gemm.argtypes = lin + [p]
     lib.act_quant_int8.argtypes = [p, i64, i64, i64, p, i64, p, p, p]
     lib.w4a8_gemv.argtypes = [p, p, i64, i64, p, p, p, i64, i64, p, i64, i32, p, p]
+    lib.w4a8_gemm.argtypes = lib.w4a8_gemv.argtypes
     lib.w4a8_linear.argtypes = [p, i64, i64, p, p, p, i64, i64, p, i64, i32, p, p, p]
     for f in ("w4_packed_layout", "w4_pack", "w4_gemv", "w4_gemv_glu", "w4_gemm",
-              "act_quant_int8", "w4a8_gemv", "w4a8_linear"):
+              "act_quant_int8", "w4a8_gemv", "w4a8_gemm", "w4a8_linear"):
         getattr(lib, f).restype = i32
     lib.w4_status_string.argtypes = [i32]
     lib.w4_status_string.restype = ctypes.c_char_p
@@ -230,7 +231,18 @@ def act_quant_int8(x, K=None, with_sum=True):
 
 def w4a8_gemv(q, s_x, qweight, s_w, bias, d_in, out_dtype=W4_OUT_BF16, want_acc=False,
               out=None):
-    """W4A8 decode linear.  Returns y, or (y, acc int32 [M][d_out]) when want_acc."""
+    """W4A8 decode linear (M <= 64).  Returns y, or (y, acc int32 [M][d_out]) when want_acc."""
+    return _w4a8("w4a8_gemv", q, s_x, qweight, s_w, bias, d_in, out_dtype, want_acc, out)
+
+
+def w4a8_gemm(q, s_x, qweight, s_w, bias, d_in, out_dtype=W4_OUT_BF16, want_acc=False,
+              out=None):
+    """W4A8 prefill linear on the int8 matrix cores (any M), the arguments and result of
+    w4a8_gemv.  Returns y, or (y, acc int32 [M][d_out]) when want_acc."""
+    return _w4a8("w4a8_gemm", q, s_x, qweight, s_w, bias, d_in, out_dtype, want_acc, out)
+
+
+def _w4a8(name, q, s_x, qweight, s_w, bias, d_in, out_dtype, want_acc, out):
     _need(q, "q", torch.int8, dim=2)
     dev = q.device
     _need(s_x, "s_x", torch.float32, dev, 1)
@@ -254,9 +266,9 @@ def w4a8_gemv(q, s_x, qweight, s_w, bias, d_in, out_dtype=W4_OUT_BF16, want_acc=
     else:
         _need(out, "out", tdtype, dev, 2)
     acc = torch.empty((M, d_out), dtype=torch.int32, device=dev) if want_acc else None
-    _check("w4a8_gemv", _lib.w4a8_gemv(_ptr(q), _ptr(s_x), M, q.stride(0), _ptr(qweight),
-                                       _ptr(s_w), _ptr(bias), d_out, d_in, _ptr(out),
-                                       out.stride(0), out_dtype, _ptr(acc), _stream(dev)))
+    _check(name, getattr(_lib, name)(_ptr(q), _ptr(s_x), M, q.stride(0), _ptr(qweight),
+                                     _ptr(s_w), _ptr(bias), d_out, d_in, _ptr(out),
+                                     out.stride(0), out_dtype, _ptr(acc), _stream(dev)))
     return (out, acc) if want_acc else out
 
 

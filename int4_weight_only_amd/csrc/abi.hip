@@ -180,6 +180,27 @@ int w4a8_gemv(const int8_t *q, const float *s_x, int64_t M, int64_t ldq, const u
     return err == hipSuccess ? W4_OK : hip_fail(err);
 }
 
+int w4a8_gemm(const int8_t *q, const float *s_x, int64_t M, int64_t ldq, const uint8_t *qweight,
+              const uint16_t *s_w, const uint16_t *bias, int64_t d_out, int64_t d_in, void *y,
+              int64_t ldy, int out_dtype, int32_t *acc, void *stream) {
+    if (!q || !s_x || !qweight || !s_w || !y) return W4_ERR_NULL;
+    if (int st = check_dims(d_out, d_in)) return st;
+    if (M < 1 || ldq < d_in || ldy < d_out) return W4_ERR_SHAPE;
+    if (M > W4_MAX_DIM || d_in > W4_MAX_W4A8_D_IN || ldq > W4_MAX_DIM || ldy > W4_MAX_DIM)
+        return W4_ERR_RANGE;
+    if (out_dtype != W4_OUT_BF16 && out_dtype != W4_OUT_F32) return W4_ERR_UNSUPPORTED;
+    if (!aligned(q, 16) || ldq % 16 != 0 || !aligned(qweight, 16) || !aligned(s_x, 4) ||
+        !aligned(s_w, 2) || (bias && !aligned(bias, 2)) || (acc && !aligned(acc, 4)) ||
+        !aligned(y, out_dtype == W4_OUT_F32 ? 4 : 2))
+        return W4_ERR_ALIGN;
+    const Layout L = layout_of(d_in, 0);
+    if (!w4::gemm_w4a8_supported(M, d_out, ldq, L.k_pad)) return W4_ERR_RANGE;
+    const hipError_t err =
+        w4::launch_gemm_w4a8(q, s_x, M, ldq, qweight, s_w, bias, d_out, d_in, L.k_pad, y, ldy,
+                             out_dtype == W4_OUT_F32, acc, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? W4_OK : hip_fail(err);
+}
+
 int w4_gemv_glu(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
                 const uint16_t *scales, const uint16_t *zeros, const uint16_t *bias, int64_t d_ff,
                 int64_t d_in, int group_size, void *y, int64_t ldy, int out_dtype, void *stream) {

@@ -32,6 +32,13 @@ hipError_t launch_w4a8_linear(const uint16_t *x, int64_t M, int64_t ldx, const u
                               int64_t d_in, int64_t k_pad, void *y, int64_t ldy, bool out_f32,
                               float *s_x, int32_t *acc, hipStream_t stream);
 
+// W4A8 prefill GEMM on the int8 matrix cores (gemm_w4a8.hip), any M.
+bool gemm_w4a8_supported(int64_t M, int64_t d_out, int64_t ldq, int64_t k_pad);
+hipError_t launch_gemm_w4a8(const int8_t *q, const float *s_x, int64_t M, int64_t ldq,
+                            const uint8_t *qweight, const uint16_t *s_w, const uint16_t *bias,
+                            int64_t d_out, int64_t d_in, int64_t k_pad, void *y, int64_t ldy,
+                            bool out_f32, int32_t *acc, hipStream_t stream);
+
 hipError_t launch_gemm(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
                        const uint16_t *scales, const uint16_t *zeros, const uint16_t *bias,
                        int64_t d_out, int64_t d_in, int64_t k_pad, int64_t span,

@@ -37,6 +37,7 @@ def lib():
     L.w4_gemm.argtypes = lin + [p]
     L.act_quant_int8.argtypes = [p, i64, i64, i64, p, i64, p, p, p]
     L.w4a8_gemv.argtypes = [p, p, i64, i64, p, p, p, i64, i64, p, i64, i32, p, p]
+    L.w4a8_gemm.argtypes = L.w4a8_gemv.argtypes
     L.w4a8_linear.argtypes = [p, i64, i64, p, p, p, i64, i64, p, i64, i32, p, p, p]
     L.w4_status_string.restype = ctypes.c_char_p
     L.w4_last_hip_error.restype = ctypes.c_char_p
@@ -46,7 +47,7 @@ def lib():
 def test_header_declares_the_five_entry_points():
     names = declared_functions()
     for n in ("w4_pack", "w4_gemv", "w4_gemv_glu", "w4_gemm", "act_quant_int8", "w4a8_gemv",
-              "w4a8_linear",
+              "w4a8_gemm", "w4a8_linear",
               "w4_packed_layout", "w4_status_string",
               "w4_last_hip_error"):
         assert n in names
@@ -179,6 +180,42 @@ def test_w4a8_rejects_bad_arguments(lib):
     assert call(acc=E + 2) == W4_ERR_ALIGN
     big = (1 << 20) + 16
     assert call(d_in=big, ldq=big) == W4_ERR_RANGE
+
+
+def test_w4a8_gemm_rejects_bad_arguments(lib):
+    f = lib.w4a8_gemm
+
+    def call(**kw):
+        a = dict(q=A, sx=B, M=1000, ldq=256, qw=C, sw=D, bias=None, d_out=128, d_in=256, y=E,
+                 ldy=128, out=0, acc=None)
+        a.update(kw)
+        return f(a["q"], a["sx"], a["M"], a["ldq"], a["qw"], a["sw"], a["bias"], a["d_out"],
+                 a["d_in"], a["y"], a["ldy"], a["out"], a["acc"], None)
+
+    assert call(q=None) == W4_ERR_NULL
+    assert call(sx=None) == W4_ERR_NULL
+    assert call(qw=None) == W4_ERR_NULL
+    assert call(sw=None) == W4_ERR_NULL
+    assert call(y=None) == W4_ERR_NULL
+    assert call(M=0) == W4_ERR_SHAPE
+    assert call(d_out=0) == W4_ERR_SHAPE
+    assert call(ldq=255) == W4_ERR_SHAPE
+    assert call(ldy=127) == W4_ERR_SHAPE
+    assert call(ldq=264) == W4_ERR_ALIGN
+    assert call(q=A + 8) == W4_ERR_ALIGN
+    assert call(qw=C + 8) == W4_ERR_ALIGN
+    assert call(sx=B + 2) == W4_ERR_ALIGN
+    assert call(acc=E + 2) == W4_ERR_ALIGN
+    assert call(y=E + 2, out=1) == W4_ERR_ALIGN
+    assert call(out=2) == W4_ERR_UNSUPPORTED
+    big = (1 << 20) + 16
+    assert call(d_in=big, ldq=big) == W4_ERR_RANGE
+    assert call(M=(1 << 24) + 1) == W4_ERR_RANGE
+    # 32-bit buffer offsets: M * ldq and d_out * k_pad / 2 must stay below 2^31
+    assert call(M=1 << 22, ldq=1024, d_in=1024) == W4_ERR_RANGE
+    assert call(d_out=1 << 22, ldy=1 << 22, d_in=2048, ldq=2048) == W4_ERR_RANGE
+    # any token count: the decode limit of 64 does not apply
+    assert call(M=65, q=None) == W4_ERR_NULL
 
 
 def test_w4a8_linear_rejects_bad_arguments(lib):

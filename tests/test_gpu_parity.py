@@ -496,6 +496,7 @@ def check_w4a8(w, x_bits, bias_bits, what):
     y32h = host(y32)
     assert_close(y32h, y_ref, what)
     assert_bf16_is_rne_of_f32(y16, y32h, what)
+    check_w4a8_gemm(q_o, s_o, ph, pd, bias_bits, d_in, acc_o, y_ref, what)
     # the same linear with the quantization folded in (w4a8_linear), on a strided x whose columns
     # past d_in hold NaN: the token scales and the accumulators are those of the oracle's O5 -> O6
     _announce("w4a8_linear", what, w.shape, x_bits.shape)
@@ -518,6 +519,113 @@ def check_w4a8(w, x_bits, bias_bits, what):
     y32fh = host(y32f)
     assert_close(y32fh, y_ref, what + " (fused)")
     assert_bf16_is_rne_of_f32(y16f, y32fh, what + " (fused)")
+
+
+def _q_with_junk_pads(q_o, d_in, ldq, seed):
+    """Device int8 [M][ldq]: the codes in the first d_in columns, random bytes (any of -128..127,
+    as act_quant_int8 leaves them unset) after them."""
+    M = q_o.shape[0]
+    rng = np.random.default_rng(seed)
+    qh = rng.integers(-128, 128, size=(M, ldq), dtype=np.int64).astype(np.int8)
+    qh[:, :d_in] = q_o[:, :d_in]
+    return torch.from_numpy(qh).cuda()
+
+
+def check_w4a8_gemm(q_o, s_o, ph, pd, bias_bits, d_in, acc_o, y_ref, what, ldq=None,
+                    ldy=None):
+    """w4a8_gemm against the oracle's O6: int32 accumulators bit for bit, y within the bar, bf16
+    the RNE image of fp32; junk past d_in in q, optional strided q and y."""
+    _announce("w4a8_gemm", what, q_o.shape, d_in)
+    M = q_o.shape[0]
+    d_out = pd[0].shape[0]
+    ldq = ldq or (d_in + 15) // 16 * 16
+    q = _q_with_junk_pads(q_o, d_in, ldq, M + d_in)
+    s = torch.from_numpy(np.ascontiguousarray(s_o, dtype=np.float32)).cuda()
+    b = dev_bf16(bias_bits) if bias_bits is not None else None
+    if ldy is not None:
+        out = torch.full((M, ldy), float("nan"), dtype=torch.float32, device="cuda")
+        y32, acc = w4.w4a8_gemm(q, s, pd[0], pd[1], b, d_in, F32, want_acc=True, out=out)
+        y32 = y32[:, :d_out]
+    else:
+        y32, acc = w4.w4a8_gemm(q, s, pd[0], pd[1], b, d_in, F32, want_acc=True)
+    y16 = w4.w4a8_gemm(q, s, pd[0], pd[1], b, d_in, BF16)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(acc), acc_o), f"{what}: w4a8_gemm int32 accumulators differ"
+    y32h = host(y32)
+    assert_close(y32h, y_ref, what + " (w4a8_gemm)")
+    assert_bf16_is_rne_of_f32(y16, y32h, what + " (w4a8_gemm)")
+
+
+def test_w4a8_gemm_ragged_token_counts():
+    """Token counts across and between the 128-token tiles, ragged d_out and d_in (junk past d_in
+    in q), strided q and y, bias on and off."""
+    shapes = [(65, 1, 1), (127, 130, 90), (128, 128, 128), (129, 257, 1000), (300, 70, 3600),
+              (257, 1000, 4100), (200, 64, 18944), (1000, 33, 161)]
+    for i, (M, d_out, d_in) in enumerate(shapes):
+        w = workloads.weight(51, M + d_in, d_out, d_in)
+        ph, pd = check_pack_bit_exact(w, 0, SYM, f"w4a8_gemm {d_out}x{d_in}")
+        x = workloads.activations(51, M, M, d_in, 0.01, 20.0)
+        b = workloads.bias(51, 2, d_out) if i % 2 else None
+        q_o, s_o, _ = oracle.act_quant(x, d_in)
+        acc_o, y_ref, nov = oracle.w4a8(q_o, s_o, ph[0], ph[1][:, 0], b, d_in)
+        assert nov == 0
+        ldq = (d_in + 15) // 16 * 16 + 16 * (i % 3)
+        check_w4a8_gemm(q_o, s_o, ph, pd, b, d_in, acc_o, y_ref,
+                        f"M={M} {d_out}x{d_in}", ldq=ldq, ldy=d_out + 3 * (i % 2))
+
+
+def test_w4a8_gemm_c4_sampled_full_size():
+    """The C4 prefill shapes (M = 2048) with per-row symmetric packs: the whole output is
+    computed, and every row of sampled tokens is compared with the oracle's O6 (each token's
+    accumulators depend on that token's codes only)."""
+    cfg = workloads.C4
+    rng = np.random.default_rng(405)
+    for li, lin in enumerate(cfg.linears):
+        w = workloads.linear_weight(cfg, li)
+        ph, pd = check_pack_bit_exact(w, 0, SYM, f"C4/{lin.name} per-row")
+        del w
+        M = cfg.tokens[0]
+        x = workloads.linear_x(cfg, li, M)
+        q_o, s_o, _ = oracle.act_quant(x, lin.d_in)
+        _announce("w4a8_gemm", f"C4/{lin.name}", M)
+        q = _q_with_junk_pads(q_o, lin.d_in, (lin.d_in + 15) // 16 * 16, li)
+        s = torch.from_numpy(s_o.astype(np.float32)).cuda()
+        y32, acc = w4.w4a8_gemm(q, s, pd[0], pd[1], None, lin.d_in, F32, want_acc=True)
+        y16 = w4.w4a8_gemm(q, s, pd[0], pd[1], None, lin.d_in, BF16)
+        torch.cuda.synchronize()
+        y32h, acch = host(y32), host(acc)
+        assert_bf16_is_rne_of_f32(y16, y32h, f"C4/{lin.name}")
+        toks = np.concatenate([[0, 127, 128, M - 1], rng.choice(M, size=4, replace=False)])
+        acc_o, y_ref, nov = oracle.w4a8(q_o[toks], s_o[toks], ph[0], ph[1][:, 0], None,
+                                        lin.d_in)
+        assert nov == 0
+        assert np.array_equal(acch[toks], acc_o), f"C4/{lin.name}: accumulators differ"
+        assert_close(y32h[toks], y_ref, f"C4/{lin.name} sampled tokens")
+
+
+def test_w4a8_gemm_int32_extremes():
+    """d_in = W4_MAX_W4A8_D_IN = 2^20 with the extreme codes and activations: level 7 or -8 times
+    +-127 in every column (|acc| up to 8 * 127 * 2^20 = 1,065,353,216), checked against the
+    closed forms and the oracle's O6, exactly."""
+    d_in = 1 << 20
+    _announce("w4a8_gemm int32 extremes", d_in)
+    codes = np.empty((4, d_in), dtype=np.uint8)
+    codes[0], codes[1], codes[2] = 15, 0, 8
+    codes[3] = np.arange(d_in) % 16
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    q_o = np.empty((3, d_in), dtype=np.int8)
+    q_o[0], q_o[1] = 127, -127
+    q_o[2] = np.where(np.arange(d_in) % 2 == 0, 127, -127)
+    s_o = np.array([1.0, 0.5, 0.25], dtype=np.float32)
+    sw_bits = workloads.to_bf16_bits(np.array([1.0, 2.0, 1.0, 0.5], np.float32))
+    acc_o, y_ref, nov = oracle.w4a8(q_o, s_o, packed, sw_bits, None, d_in)
+    assert nov == 0
+    L = 127 * d_in
+    assert acc_o[:2, :3].tolist() == [[7 * L, -8 * L, 0], [-7 * L, 8 * L, 0]]
+    assert acc_o[0, 3] == -8 * 127 * (d_in // 16) and acc_o[2, :3].tolist() == [0, 0, 0]
+    ph = (packed, sw_bits[:, None], None)
+    pd = (torch.from_numpy(packed).cuda(), dev_bf16(sw_bits[:, None].copy()), None)
+    check_w4a8_gemm(q_o, s_o, ph, pd, None, d_in, acc_o, y_ref, "int32 extremes")
 
 
 def test_w4a8_c5_full_size():
@@ -606,6 +714,12 @@ def test_w4a8_worst_case_accumulator(H):
     if H == 3584:
         assert H * 1016 == 3641344
     assert host(y).tolist() == [[float(H * 1016)] * 4]
+    # the prefill GEMM over 130 tokens (two token tiles)
+    q = torch.full((130, H), -127, dtype=torch.int8, device="cuda")
+    s = torch.ones(130, dtype=torch.float32, device="cuda")
+    y, acc = w4.w4a8_gemm(q, s, qw, sw, None, H, F32, want_acc=True)
+    torch.cuda.synchronize()
+    assert host(acc).tolist() == [[H * 1016] * 4] * 130
     # fused: x = -1 everywhere quantizes to -127 everywhere (s_x = 1/127)
     x = dev_bf16(np.full((1, H), 0xBF80, dtype=np.uint16))
     y, acc = w4.w4a8_linear(x, qw, sw, None, H, F32, want_acc=True)
