@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, GB/s
 BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak, TFLOP/s
+INT8_MFMA_PEAK_TOPS = 5000.0    # MI355X dense int8 matrix peak, TOP/s
 INFINITY_CACHE_BYTES = 256 << 20
 
 METRIC = "W4A16 decode GEMV GB/s & % HBM peak (M=1); prefill GEMM TFLOP/s"
@@ -210,7 +211,7 @@ def bench_c4(torch, w4, workloads, iters):
     dev = torch.device("cuda", 0)
     M = cfg.tokens[0]
     out = {}
-    total_flop, total_ms = 0.0, 0.0
+    total_flop, total_ms, w8_ms = 0.0, 0.0, 0.0
     for li, lin in enumerate(cfg.linears):
         w = torch.from_numpy(workloads.linear_weight(cfg, li)).to(dev)
         qw, sc, zr = w4.w4_pack(w, lin.group_size, lin.mode)
@@ -233,10 +234,35 @@ def bench_c4(torch, w4, workloads, iters):
         total_ms += ms
         out[lin.name] = dict(ms=round(ms, 4), tflops=round(flop / ms / 1e9, 1),
                              mfma_frac=round(flop / ms / 1e9 / BF16_MFMA_PEAK_TFLOPS, 4))
-        del qw, sc, zr, x, y
+        del qw, sc, zr
+        # W4A8 on the same shape: a per-row symmetric pack, act_quant_int8 + w4a8_gemm
+        w = torch.from_numpy(workloads.linear_weight(cfg, li)).to(dev)
+        qw8, sw8, _ = w4.w4_pack(w, 0, w4.W4_SYM)
+        del w
+        q, s_x, _ = w4.act_quant_int8(x, lin.d_in, with_sum=False)
+        for _ in range(2):
+            w4.w4a8_gemm(q, s_x, qw8, sw8, None, lin.d_in, out=y)
+        torch.cuda.synchronize()
+        for _ in range(iters):
+            timer.start("aq")
+            w4.act_quant_int8(x, lin.d_in, with_sum=False, out=(q, s_x))
+            timer.stop("aq")
+            timer.start("w4a8")
+            w4.w4a8_gemm(q, s_x, qw8, sw8, None, lin.d_in, out=y)
+            timer.stop("w4a8")
+        torch.cuda.synchronize()
+        g_ms, aq_ms = timer.mean_ms("w4a8"), timer.mean_ms("aq")
+        w8_ms += g_ms + aq_ms
+        out[lin.name]["w4a8"] = dict(
+            gemm_ms=round(g_ms, 4), tops=round(flop / g_ms / 1e9, 1),
+            int8_mfma_frac=round(flop / g_ms / 1e9 / INT8_MFMA_PEAK_TOPS, 4),
+            act_quant_ms=round(aq_ms, 4), path_ms=round(g_ms + aq_ms, 4))
+        del qw8, sw8, q, s_x, x, y
     out["total"] = dict(gflop=round(total_flop / 1e9, 2), ms=round(total_ms, 4),
                         tflops=round(total_flop / total_ms / 1e9, 1),
-                        mfma_frac=round(total_flop / total_ms / 1e9 / BF16_MFMA_PEAK_TFLOPS, 4))
+                        mfma_frac=round(total_flop / total_ms / 1e9 / BF16_MFMA_PEAK_TFLOPS, 4),
+                        w4a8_path_ms=round(w8_ms, 4),
+                        w4a8_path_tops=round(total_flop / w8_ms / 1e9, 1))
     return out
 
 

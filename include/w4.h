@@ -196,7 +196,8 @@ int w4a8_linear(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweigh
  * are; sum_k 8 q[m][k] is subtracted per token from the int32 sums, so acc is exact.
  *   q, s_x, qweight, s_w, bias, y, out_dtype, acc: as for w4a8_gemv, with any M >= 1
  * Limits (W4_ERR_RANGE beyond them): M <= W4_MAX_DIM, d_in <= W4_MAX_W4A8_D_IN, M * ldq < 2^31
- * and d_out * k_pad / 2 < 2^31 (32-bit buffer offsets).
+ * and d_out * k_pad / 2 < 2^31 (32-bit buffer offsets), ceil(M / 128) * ceil(d_out / 256) < 2^23
+ * (the launch grid).
  */
 int w4a8_gemm(const int8_t *q, const float *s_x, int64_t M, int64_t ldq, const uint8_t *qweight,
               const uint16_t *s_w, const uint16_t *bias, int64_t d_out, int64_t d_in, void *y,

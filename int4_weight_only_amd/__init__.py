@@ -213,16 +213,25 @@ def w4_linear(x, qweight, scales, zeros, bias, d_in, group_size, out_dtype=W4_OU
     return fn(x, qweight, scales, zeros, bias, d_in, group_size, out_dtype, out)
 
 
-def act_quant_int8(x, K=None, with_sum=True):
+def act_quant_int8(x, K=None, with_sum=True, out=None):
     """Per-token int8 quantization.  Returns (q int8 [M][ldq], s_x fp32 [M], q_sum int32 [M] or
-    None); ldq is K rounded up to 16 (columns >= K are left unset)."""
+    None); ldq is K rounded up to 16 (columns >= K are left unset).  out=(q, s_x) reuses
+    caller tensors of those shapes."""
     _need(x, "x", torch.bfloat16, dim=2)
     M = x.shape[0]
     K = x.shape[1] if K is None else K
     dev = x.device
     ldq = (K + 15) // 16 * 16
-    q = torch.empty((M, ldq), dtype=torch.int8, device=dev)
-    s_x = torch.empty((M,), dtype=torch.float32, device=dev)
+    if out is None:
+        q = torch.empty((M, ldq), dtype=torch.int8, device=dev)
+        s_x = torch.empty((M,), dtype=torch.float32, device=dev)
+    else:
+        q, s_x = out
+        _need(q, "q", torch.int8, dev, 2)
+        _need(s_x, "s_x", torch.float32, dev, 1)
+        if q.shape[0] != M or q.shape[1] < K or q.stride(1) != 1 or s_x.shape[0] != M:
+            raise ValueError("out must be (q [M][>= K] row-major, s_x [M])")
+        ldq = q.stride(0)
     q_sum = torch.empty((M,), dtype=torch.int32, device=dev) if with_sum else None
     _check("act_quant_int8", _lib.act_quant_int8(_ptr(x), M, K, x.stride(0), _ptr(q), ldq,
                                                  _ptr(s_x), _ptr(q_sum), _stream(dev)))

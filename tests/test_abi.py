@@ -214,6 +214,8 @@ def test_w4a8_gemm_rejects_bad_arguments(lib):
     # 32-bit buffer offsets: M * ldq and d_out * k_pad / 2 must stay below 2^31
     assert call(M=1 << 22, ldq=1024, d_in=1024) == W4_ERR_RANGE
     assert call(d_out=1 << 22, ldy=1 << 22, d_in=2048, ldq=2048) == W4_ERR_RANGE
+    # the grid's thread count: (M / 128) (d_out / 256) 256 < 2^31
+    assert call(M=1 << 22, ldq=16, d_in=16, d_out=1 << 20, ldy=1 << 20) == W4_ERR_RANGE
     # any token count: the decode limit of 64 does not apply
     assert call(M=65, q=None) == W4_ERR_NULL
 
