@@ -24,12 +24,11 @@
 //     (w & 0x0F0F0F0F: the even columns) and the high ones ((w >> 4) & 0x0F0F0F0F: the odd), the
 //     operands of two MFMAs whose partners are the token's even and odd columns.
 // The next step's global loads are in flight while the current stage feeds the MFMAs. Loads are
-// raw buffer loads: a token past M, a row past d_out or a column past d_in reads zeros, and the
-// bytes of the last activation piece past d_in are masked (act_quant_int8 leaves them unset).
+// raw buffer loads: a token past M or a row past d_out reads zeros, and in the last step the
+// activation bytes at and past d_in are masked to zero (act_quant_int8 leaves them unset), which
+// also cancels whatever weight bytes meet them.
 #include "w4_device.h"
 #include "w4_launch.h"
-
-#include <cstdlib>
 
 namespace w4 {
 
@@ -43,7 +42,6 @@ constexpr int kG8Step = 128;     // columns per K step
 constexpr int kG8AStride = 144;  // LDS bytes per token row of a stage
 constexpr int kG8WStride = 80;   // LDS bytes per weight row of a stage
 constexpr int kG8TM = 4;         // 16-token MFMA tiles per wave
-constexpr int kG8TN = 8;         // 16-row MFMA tiles per wave
 constexpr int kG8Xcds = 8;
 
 // A block barrier that waits for the LDS accesses only: the next step's global loads stay in
@@ -55,11 +53,12 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-template <int WGM, int WGN>
+// WGM x WGN waves of 64 tokens x 16 TN weight rows each
+template <int WGM, int WGN, int TN>
 struct G8Shape {
     static constexpr int kThreads = kWave * WGM * WGN;
-    static constexpr int kBM = 16 * kG8TM * WGM;    // tokens per block
-    static constexpr int kBN = 16 * kG8TN * WGN;    // weight rows per block
+    static constexpr int kBM = 16 * kG8TM * WGM;  // tokens per block
+    static constexpr int kBN = 16 * TN * WGN;     // weight rows per block
     static constexpr int kAL = kBM * 8 / kThreads;  // 16-byte activation pieces per thread
     static constexpr int kWL = kBN * 4 / kThreads;  // 16-byte weight pieces per thread
     static constexpr int kABytes = kBM * kG8AStride;
@@ -68,14 +67,14 @@ struct G8Shape {
     static_assert(kAL * kThreads == kBM * 8 && kWL * kThreads == kBN * 4, "load split");
 };
 
-template <int WGM, int WGN, bool RAGGED>
-__global__ void __launch_bounds__(kWave * WGM * WGN, 2) gemm_w4a8_kernel(
+template <int WGM, int WGN, int TN, int MINW, bool RAGGED>
+__global__ void __launch_bounds__(kWave * WGM * WGN, MINW) gemm_w4a8_kernel(
     const int8_t *__restrict__ q, int M, int64_t ldq, const float *__restrict__ s_x,
     const uint8_t *__restrict__ qweight, const uint16_t *__restrict__ s_w,
     const uint16_t *__restrict__ bias, int d_out, int d_in, int row_bytes, int n_steps,
     int tiles_m, int tiles_n, void *__restrict__ y, int64_t ldy, int out_f32, int vec_store,
     int32_t *__restrict__ acc_out) {
-    using S = G8Shape<WGM, WGN>;
+    using S = G8Shape<WGM, WGN, TN>;
     extern __shared__ __align__(16) unsigned char lds[];
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -100,7 +99,7 @@ __global__ void __launch_bounds__(kWave * WGM * WGN, 2) gemm_w4a8_kernel(
     // loader roles: activation piece i of this thread is row L / 8, columns 16 (L % 8) .. + 15 of
     // the step with L = i T + tid; weight piece i is row L / 4, bytes 16 (L % 4) .. + 15.
     uint32_t a_off[S::kAL], a_lds[S::kAL], w_off[S::kWL], w_lds[S::kWL];
-    int a_col[S::kAL], w_col[S::kWL];
+    int a_col[S::kAL];
 #pragma unroll
     for (int i = 0; i < S::kAL; ++i) {
         const int L = i * S::kThreads + tid, row = L >> 3, slot = L & 7;
@@ -117,34 +116,29 @@ __global__ void __launch_bounds__(kWave * WGM * WGN, 2) gemm_w4a8_kernel(
         w_off[i] = n < d_out
                        ? static_cast<uint32_t>(n) * static_cast<uint32_t>(row_bytes) + 16u * slot
                        : kOutOfRange;
-        w_col[i] = 32 * slot;
         w_lds[i] = S::kABytes + row * kG8WStride + 16 * slot;
     }
 
+    // The step's column offset goes into the scalar offset of the loads. Pieces past d_in are only
+    // in the last step: their activation bytes are masked there (they may hold the next token's
+    // codes, or read as zeros past the end of q), and the weight bytes they meet are multiplied by
+    // those zeros whatever they hold (padding codes, the next row, zeros past the end).
     u32x4_t ra[S::kAL], rwt[S::kWL];
     auto gload = [&](int step) {
         const int c0 = step * kG8Step;
 #pragma unroll
-        for (int i = 0; i < S::kAL; ++i) {
-            const uint32_t off = c0 + a_col[i] < d_in && a_off[i] != kOutOfRange
-                                     ? a_off[i] + static_cast<uint32_t>(c0)
-                                     : kOutOfRange;
-            ra[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, off, 0, 0);
-        }
+        for (int i = 0; i < S::kAL; ++i)
+            ra[i] = __builtin_amdgcn_raw_buffer_load_b128(rq, a_off[i], c0, 0);
 #pragma unroll
-        for (int i = 0; i < S::kWL; ++i) {
-            const uint32_t off = c0 + w_col[i] < d_in && w_off[i] != kOutOfRange
-                                     ? w_off[i] + static_cast<uint32_t>(c0 / 2)
-                                     : kOutOfRange;
-            rwt[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, off, 0, 0);
-        }
+        for (int i = 0; i < S::kWL; ++i)
+            rwt[i] = __builtin_amdgcn_raw_buffer_load_b128(rw, w_off[i], c0 / 2, 0);
     };
 
     int qs[S::kAL];  // this thread's share of each of its rows' sums of q
 #pragma unroll
     for (int i = 0; i < S::kAL; ++i) qs[i] = 0;
-    // the step that holds column d_in - 1 when d_in % 32 != 0 masks its activation bytes
-    const int rag_step = RAGGED ? (d_in - 1) / kG8Step : -1;
+    // when d_in % 128 != 0 the last step masks the activation bytes at and past d_in
+    const int rag_step = RAGGED ? n_steps - 1 : -1;
 
     auto stage = [&](int step, int buf) {
         unsigned char *base = lds + buf * S::kStage;
@@ -172,20 +166,20 @@ __global__ void __launch_bounds__(kWave * WGM * WGN, 2) gemm_w4a8_kernel(
         for (int i = 0; i < S::kWL; ++i) *reinterpret_cast<u32x4_t *>(base + w_lds[i]) = rwt[i];
     };
 
-    i32x4_t acc[kG8TN][kG8TM];
+    i32x4_t acc[TN][kG8TM];
 #pragma unroll
-    for (int j = 0; j < kG8TN; ++j)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int i = 0; i < kG8TM; ++i) acc[j][i] = i32x4_t{0, 0, 0, 0};
 
     const uint32_t a_rd = (wm * 64 + r16) * kG8AStride + 32 * kq;
-    const uint32_t w_rd = S::kABytes + (wn * 128 + r16) * kG8WStride + 16 * kq;
+    const uint32_t w_rd = S::kABytes + (wn * 16 * TN + r16) * kG8WStride + 16 * kq;
     auto compute = [&](int buf) {
         const unsigned char *base = lds + buf * S::kStage;
         i32x4_t av[kG8TM][2];
-        u32x4_t wv[kG8TN];
+        u32x4_t wv[TN];
 #pragma unroll
-        for (int j = 0; j < kG8TN; ++j)
+        for (int j = 0; j < TN; ++j)
             wv[j] = *reinterpret_cast<const u32x4_t *>(base + w_rd + j * 16 * kG8WStride);
 #pragma unroll
         for (int i = 0; i < kG8TM; ++i) {
@@ -195,7 +189,7 @@ __global__ void __launch_bounds__(kWave * WGM * WGN, 2) gemm_w4a8_kernel(
 #pragma unroll
         for (int p = 0; p < 2; ++p) {  // the even columns, then the odd ones
 #pragma unroll
-            for (int j = 0; j < kG8TN; ++j) {
+            for (int j = 0; j < TN; ++j) {
                 const u32x4_t v = p == 0 ? wv[j] : wv[j] >> 4;
                 const u32x4_t c = v & 0x0F0F0F0Fu;
                 const i32x4_t wop = {static_cast<int>(c.x), static_cast<int>(c.y),
@@ -231,7 +225,7 @@ __global__ void __launch_bounds__(kWave * WGM * WGN, 2) gemm_w4a8_kernel(
     }
     lds_barrier();
 
-    // epilogue: acc[j][i] lane (r16, kq) holds rows nb + 128 wn + 16 j + 4 kq + r (r = 0..3) of
+    // epilogue: acc[j][i] lane (r16, kq) holds rows nb + 16 TN wn + 16 j + 4 kq + r (r = 0..3) of
     // token mb + 64 wm + 16 i + r16
 #pragma unroll
     for (int i = 0; i < kG8TM; ++i) {
@@ -241,8 +235,8 @@ __global__ void __launch_bounds__(kWave * WGM * WGN, 2) gemm_w4a8_kernel(
         const int tsum8 = 8 * qsum[mloc];
         const float sx = s_x[m];
 #pragma unroll
-        for (int j = 0; j < kG8TN; ++j) {
-            const int n = nb + wn * 128 + 16 * j + 4 * kq;
+        for (int j = 0; j < TN; ++j) {
+            const int n = nb + wn * 16 * TN + 16 * j + 4 * kq;
             if (n >= d_out) continue;
             float v[4];
             int a[4];
@@ -278,37 +272,25 @@ __global__ void __launch_bounds__(kWave * WGM * WGN, 2) gemm_w4a8_kernel(
     }
 }
 
-template <int WGM, int WGN>
+template <int WGM, int WGN, int TN, int MINW>
 hipError_t launch_g8(const int8_t *q, const float *s_x, int64_t M, int64_t ldq,
                      const uint8_t *qweight, const uint16_t *s_w, const uint16_t *bias,
                      int64_t d_out, int64_t d_in, int64_t k_pad, void *y, int64_t ldy,
                      bool out_f32, int32_t *acc, hipStream_t stream) {
-    using S = G8Shape<WGM, WGN>;
+    using S = G8Shape<WGM, WGN, TN>;
     const int tiles_m = static_cast<int>((M + S::kBM - 1) / S::kBM);
     const int tiles_n = static_cast<int>((d_out + S::kBN - 1) / S::kBN);
     const int n_steps = static_cast<int>((d_in + kG8Step - 1) / kG8Step);
     const size_t esz = out_f32 ? 4 : 2;
     const int vec = (ldy % 4 == 0) && (reinterpret_cast<uintptr_t>(y) % (4 * esz) == 0);
     const dim3 grid(static_cast<unsigned>(tiles_m) * static_cast<unsigned>(tiles_n));
-    auto kern = (d_in & 31) != 0 ? gemm_w4a8_kernel<WGM, WGN, true>
-                                 : gemm_w4a8_kernel<WGM, WGN, false>;
+    auto kern = d_in % kG8Step != 0 ? gemm_w4a8_kernel<WGM, WGN, TN, MINW, true>
+                                    : gemm_w4a8_kernel<WGM, WGN, TN, MINW, false>;
     hipLaunchKernelGGL(kern, grid, dim3(S::kThreads), S::kLds, stream, q, static_cast<int>(M),
                        ldq, s_x, qweight, s_w, bias, static_cast<int>(d_out),
                        static_cast<int>(d_in), static_cast<int>(k_pad / 2), n_steps, tiles_m,
                        tiles_n, y, ldy, out_f32 ? 1 : 0, vec, acc);
     return hipGetLastError();
-}
-
-// Block shape: 256 tokens x 256 rows (8 waves, one block per CU) when the grid still fills the
-// chip twice over, else 128 x 256 (4 waves, two blocks per CU). W4_W4A8_GEMM_TILE=256 or 128
-// forces one.
-int pick_tile(int64_t M, int64_t d_out) {
-    if (const char *e = std::getenv("W4_W4A8_GEMM_TILE")) {
-        const int v = std::atoi(e);
-        if (v == 128 || v == 256) return v;
-    }
-    const int64_t big = ((M + 255) / 256) * ((d_out + 255) / 256);
-    return big >= 2 * device_cu_count() ? 256 : 128;
 }
 
 }  // namespace
@@ -318,7 +300,7 @@ bool gemm_w4a8_supported(int64_t M, int64_t d_out, int64_t ldq, int64_t k_pad) {
     // 31-bit buffer offsets: the activations and the packed weights (plus one step past the row)
     if (M * ldq + kG8Step >= (int64_t)kOutOfRange) return false;
     if (d_out * (k_pad / 2) + kG8Step >= (int64_t)kOutOfRange) return false;
-    // the grid's thread count stays below 2^31 (one thread per 128 outputs in either block shape)
+    // the grid's thread count stays below 2^31 (one thread per 128 outputs)
     return ((M + 127) / 128) * ((d_out + 255) / 256) * 256 < ((int64_t)1 << 31);
 }
 
@@ -327,11 +309,11 @@ hipError_t launch_gemm_w4a8(const int8_t *q, const float *s_x, int64_t M, int64_
                             int64_t d_out, int64_t d_in, int64_t k_pad, void *y, int64_t ldy,
                             bool out_f32, int32_t *acc, hipStream_t stream) {
     if (!gemm_w4a8_supported(M, d_out, ldq, k_pad)) return hipErrorInvalidValue;
-    if (pick_tile(M, d_out) == 256)
-        return launch_g8<4, 2>(q, s_x, M, ldq, qweight, s_w, bias, d_out, d_in, k_pad, y, ldy,
-                               out_f32, acc, stream);
-    return launch_g8<2, 2>(q, s_x, M, ldq, qweight, s_w, bias, d_out, d_in, k_pad, y, ldy,
-                           out_f32, acc, stream);
+    // 128 tokens x 256 rows per block (4 waves; two blocks per CU). Blocks of 256 x 256 (8 waves,
+    // one per CU) measured no faster on the 7B prefill shapes, with or without the weight split
+    // moved from the MFMA loop into the staging.
+    return launch_g8<2, 2, 8, 2>(q, s_x, M, ldq, qweight, s_w, bias, d_out, d_in, k_pad, y, ldy,
+                                 out_f32, acc, stream);
 }
 
 }  // namespace w4
