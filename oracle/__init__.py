@@ -8,6 +8,8 @@ Every function follows the pages cited in oracle.c:
   [Lab5]  "Lab 5: Gemma4 端到端推理优化"
   [Orin]  "Jetson Orin AGX INT4 推理优化实践：super 分支从 9 tok/s 到 24 tok/s"
   [Infra] "【infra之路】12-投机解码、量化与推理引擎对比"
+  [QAT]   "Yeniden paketlenmiş QAT Gemma 4 26B-A4B, tek bir TPU v6e'de FP8 işlemenin 1.9 katı
+          verimle sunuluyor"
 
 Arrays: weights fp32 [d_out][d_in]; bf16 values travel as uint16 bit patterns; packed weights
 uint8 [d_out][k_pad/2] (earlier column in the low nibble); scales/zeros uint16 (bf16)
@@ -89,6 +91,8 @@ def _declare(lib):
     lib.oracle_w4a8.restype = _i64
     lib.oracle_silu_mul.argtypes = [_p, _p, _i64, _p]
     lib.oracle_silu_mul.restype = None
+    lib.oracle_qat_repack.argtypes = [_p, _i64, _i64, _i64, _p, _p, _p]
+    lib.oracle_qat_repack.restype = None
     return lib
 
 
@@ -234,6 +238,22 @@ def w4a16_silu_mul(x_bits, qweight, scales, zeros, bias_bits, d_in, group_size):
     y = w4a16(x_bits, qweight, scales, zeros, bias_bits, d_in, group_size)
     H = y.shape[1] // 2
     return silu_mul(y[:, :H], y[:, H:])
+
+
+def qat_repack(w_bits, d_in=None):
+    """O8: repack of bf16 weights that sit on a 16-level grid per group of 32 columns.
+    w_bits: u16 (bf16) [d_out][ldw >= d_in].  Returns (qweight u8 [d_out][k_pad/2],
+    scales u16 [d_out][n_groups], m u8 [d_out][n_groups]; m = 0 marks a group off the grid)."""
+    lib = _load()
+    w = _c(w_bits, np.uint16)
+    d_out, ldw = w.shape
+    d_in = ldw if d_in is None else d_in
+    kp = k_pad(d_in, 32)
+    qw = np.zeros((d_out, kp // 2), dtype=np.uint8)
+    sc = np.zeros((d_out, kp // 32), dtype=np.uint16)
+    m = np.zeros((d_out, kp // 32), dtype=np.uint8)
+    lib.oracle_qat_repack(_ptr(w), d_out, d_in, ldw, _ptr(qw), _ptr(sc), _ptr(m))
+    return qw, sc, m
 
 
 def tolerance_ok(y, y_ref, rel=2e-3):

@@ -55,6 +55,13 @@ MUTATIONS = [
      "const int64_t wq = (int64_t)code_at(qweight, k_pad, j, k) - 7;"),
     ("w4a8 scale dropped", "double r = (double)oracle_bf16_to_f32(s_w[j]) * (double)s_x[m]",
      "double r = (double)s_x[m]"),
+    ("qat step max/8", "const float s_m = amax / (float)m;", "const float s_m = amax / 8.0f;"),
+    ("qat search from 8 down", "for (int m = 1; m <= 8 && !found; ++m) {",
+     "for (int m = 8; m >= 1 && !found; --m) {"),
+    ("qat tolerance 1/2", "dev > 0.0625f", "dev > 0.5f"),
+    ("qat least squares dropped", "const float s32 = den > 0.0 ? (float)(num / den) : 0.0f;",
+     "const float s32 = amax / (float)found;"),
+    ("qat level +8 allowed", "l > 7.0f ||", "l > 8.0f ||"),
 ]
 
 

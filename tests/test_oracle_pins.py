@@ -463,3 +463,166 @@ def test_w4a16_silu_mul_takes_gate_then_up():
         for j in range(H):
             g, u = float(wh[j, k]), float(wh[H + j, k])
             assert abs(h[j] - g / (1.0 + math.exp(-g)) * u) <= 1e-12 * (1.0 + abs(h[j]))
+
+
+# ------------------------------------------------------------------------------------------
+# O8: repack of weights trained on the 4-bit grid.  [QAT] "Yeniden paketlenmiş QAT Gemma 4
+# 26B-A4B, tek bir TPU v6e'de FP8 işlemenin 1.9 katı verimle sunuluyor", section "Yeniden
+# nicelendirme değil, yeniden paketleme": 32-wide groups of bf16 weights on levels -8..7 times a
+# step; the step is the group maximum over the first m in 1..8 that reproduces the group,
+# refined by least squares; the max/8 rule re-rounds groups whose peak is below level 8.
+# ------------------------------------------------------------------------------------------
+def _rne_bf16(vals):
+    """fp32 -> bf16 bits, round to nearest even, with integer arithmetic on the fp32 bits."""
+    u = np.asarray(vals, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lower = u & 0xFFFF
+    upper = u >> 16
+    up = (lower > 0x8000) | ((lower == 0x8000) & ((upper & 1) == 1))
+    return (upper + up.astype(np.uint64)).astype(np.uint16)
+
+
+def _bits_f32(bits):
+    return (np.asarray(bits, dtype=np.uint32) << 16).view(np.float32)
+
+
+def _grid_groups(rng, n, peaks, steps):
+    """n groups of 32 levels in [-8, 7], each holding the level +-1 and its peak level (signed)."""
+    lv = np.zeros((n, 32), dtype=np.int64)
+    for i in range(n):
+        p = peaks[i % len(peaks)]
+        P = abs(p)
+        row = rng.integers(-min(P, 8), min(P, 7) + 1, size=32)
+        row = np.clip(row, -P, P if p > 0 else P - 1 if P == 8 else P)
+        row[rng.integers(0, 32)] = p
+        k = rng.integers(0, 32)
+        while row[k] == p:
+            k = rng.integers(0, 32)
+        row[k] = 1 if rng.random() < 0.5 else -1
+        lv[i] = row
+    st = np.asarray([steps[i % len(steps)] for i in range(n)], dtype=np.float64)
+    return lv, st
+
+
+def _nibbles(qw):
+    return np.stack([qw & 0xF, qw >> 4], axis=-1).reshape(qw.shape[0], -1)
+
+
+@pytest.mark.parametrize("peak", [7, -8, -7, 5, -3, 2, 1, 6, -5])
+def test_qat_repack_exact_grid_closed_form(peak):
+    """Steps with at most 4 significant bits: every s l is an exact bf16, so the group's codes are
+    its levels + 8, its m is the peak level's magnitude (a level +-1 rules out coarser m), and
+    the least-squares step is the step itself."""
+    rng = np.random.default_rng(80 + peak)
+    steps = [0.125, 0.01171875, 3.0, 2.0 ** -20 * 1.5, 0.4375]
+    lv, st = _grid_groups(rng, 10, [peak], steps)
+    w = _rne_bf16((lv * st[:, None]).astype(np.float32))
+    assert np.array_equal(_bits_f32(w).astype(np.float64), lv * st[:, None])  # exact on the grid
+    qw, sc, m = oracle.qat_repack(w.reshape(1, -1))
+    assert np.array_equal(_nibbles(qw)[0], (lv + 8).reshape(-1))
+    assert np.array_equal(_bits_f32(sc[0]).astype(np.float64), st)
+    assert np.all(m == abs(peak))
+    # the round trip is exact
+    assert np.array_equal(_bits_f32(sc[0])[:, None].astype(np.float64) * lv, _bits_f32(w).reshape(10, 32))
+
+
+def test_qat_repack_bf16_rounded_grid():
+    """Random bf16 steps: s l rounded to bf16, as a trained export stores it.  Every group is found
+    on the grid with its own levels; the refined step is the generating step or a neighbouring bf16
+    value, and most values come back bit for bit (the page reports 92.6%)."""
+    rng = np.random.default_rng(81)
+    n = 400
+    steps = _bits_f32(rng.integers(0x3A00, 0x3D80, size=n).astype(np.uint16)).astype(np.float64)
+    lv, st = _grid_groups(rng, n, [7, -8, 6, -7, 4, -5, 3], steps)
+    w = _rne_bf16((lv * st[:, None]).astype(np.float32))
+    qw, sc, m = oracle.qat_repack(w.reshape(4, -1))
+    assert np.array_equal(_nibbles(qw).reshape(n, 32), lv + 8)
+    assert np.all(m.reshape(-1) == np.abs(lv).max(axis=1))
+    s = _bits_f32(sc.reshape(-1)).astype(np.float64)
+    ulp = 2.0 ** (np.floor(np.log2(st)) - 7)
+    assert np.all(np.abs(s - st) <= ulp)
+    back = _rne_bf16((s[:, None] * lv).astype(np.float32))
+    frac = np.mean(back == w.reshape(n, 32))
+    assert frac >= 0.9, frac
+
+
+def test_qat_repack_least_squares_step():
+    """Levels fixed, the step is sum r l / sum l^2: with a peak of 7.03125 on a unit grid the
+    maximum over 7 would give 1.0045 (bf16 1.0078125); the least-squares step rounds to 1.0."""
+    lv = np.array([7, 1, -1, 3, -8, 2, 0, 5] * 4, dtype=np.int64)
+    lv[8:] = np.resize([1, -2, 4, -3, 6, 0, -7, 2], 24)
+    lv[4] = -5
+    r = lv.astype(np.float64)
+    r[0] = 7.03125  # bf16: 1.7578125 * 4
+    w = _rne_bf16(r.astype(np.float32))
+    assert np.array_equal(_bits_f32(w).astype(np.float64), r)
+    qw, sc, m = oracle.qat_repack(w.reshape(1, -1))
+    assert m[0, 0] == 7
+    assert np.array_equal(_nibbles(qw)[0], lv + 8)
+    ls = Fraction(0)
+    for t in range(32):
+        ls += Fraction(r[t]) * int(lv[t])
+    ls /= int((lv * lv).sum())
+    assert float(ls) == pytest.approx(1.0 + 0.03125 * 7 / int((lv * lv).sum()), rel=1e-12)
+    assert _bits_f32(sc[0])[0] == 1.0
+    assert np.float32(7.03125) / np.float32(7.0) > np.float32(1.00390625)  # max/7 would round up
+
+
+def test_qat_repack_reproduces_where_max_over_8_rerounds():
+    """A group whose peak is +7 steps: the max/8 rule takes the step 7/8 too small and moves
+    values off their levels; the search keeps every value."""
+    lv = np.array([7, -3, 1, 0, 5, -6, 2, -1] * 4, dtype=np.int64)
+    r = (lv * 0.25).astype(np.float32)
+    w = _rne_bf16(r)
+    qw, sc, m = oracle.qat_repack(w.reshape(1, -1))
+    s = _bits_f32(sc[0])[0]
+    assert m[0, 0] == 7 and s == 0.25
+    assert np.array_equal(s * (_nibbles(qw)[0].astype(np.float32) - 8), r)
+    s8 = np.float32(np.abs(r).max() / 8)
+    back8 = s8 * np.clip(np.rint(r / s8), -8, 7)
+    assert np.count_nonzero(back8 != r) > 0
+
+
+def test_qat_repack_off_grid_falls_back_to_rtn():
+    """Groups off the grid (normal samples) report m = 0 and are packed by the symmetric RTN
+    rule O1 applies to the same values."""
+    rng = np.random.default_rng(82)
+    r = rng.normal(0, 0.02, size=(3, 96)).astype(np.float32)
+    w = _rne_bf16(r)
+    qw, sc, m = oracle.qat_repack(w)
+    assert np.all(m == 0)
+    qw1, sc1, _ = oracle.pack(_bits_f32(w), 32, SYM)
+    assert np.array_equal(qw, qw1) and np.array_equal(sc, sc1)
+
+
+def test_qat_repack_tolerance_and_level_range():
+    """A value 0.047 of a level off its level is still on the grid; 0.078 is not; a peak at
+    +8 steps is not a level of the grid."""
+    base = np.array([7, -3, 1, 0, 5, -6, 2, -1] * 4, dtype=np.float32)
+    near, far, plus8 = base.copy(), base.copy(), base.copy()
+    near[1] = -3.046875
+    far[1] = -3.078125
+    plus8[0] = 8.0
+    w = _rne_bf16(np.stack([near, far, plus8]))
+    assert np.array_equal(_bits_f32(w), np.stack([near, far, plus8]))
+    qw, sc, m = oracle.qat_repack(w)
+    assert m[:, 0].tolist() == [7, 0, 0]
+    assert np.array_equal(_nibbles(qw)[0], base.astype(np.int64) + 8)
+
+
+def test_qat_repack_zero_group_pads_and_stride():
+    """An all-zero group (m = 1, scale +0, codes 8), a ragged last group whose pads are level 0,
+    and columns past d_in (NaN here) that are never read."""
+    d_in, ldw = 40, 48
+    w = np.full((2, ldw), 0x7FC0, dtype=np.uint16)
+    w[0, :d_in] = 0
+    lv = np.array([3, -2, 1, 0, -1, 2, 3, -3], dtype=np.int64)
+    w[1, :32] = _rne_bf16(np.resize(lv, 32).astype(np.float32) * 0.5)
+    w[1, 32:d_in] = _rne_bf16(lv.astype(np.float32) * 0.125)
+    qw, sc, m = oracle.qat_repack(w, d_in)
+    assert qw.shape == (2, 32) and sc.shape == (2, 2)
+    assert m[0].tolist() == [1, 1] and sc[0].tolist() == [0, 0]
+    assert np.all(_nibbles(qw)[0] == 8)
+    assert m[1].tolist() == [3, 3]
+    assert _bits_f32(sc[1]).tolist() == [0.5, 0.125]
+    codes = _nibbles(qw)[1]
+    assert np.array_equal(codes[32:40], lv + 8) and np.all(codes[40:] == 8)
