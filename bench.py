@@ -314,6 +314,42 @@ def bench_c5(torch, w4, workloads, iters):
     return out
 
 
+def bench_qat(torch, w4, workloads, iters):
+    """w4_qat_repack on the C4 gate/up shape (37888 x 3584, groups of 32): bf16 weights on the
+    4-bit grid, generated on the GPU with a seeded torch generator (timing only; parity of the
+    rule at full size is in the GPU tests).  HBM-bound: 2 B read and 0.5 B written per weight,
+    plus one bf16 scale per group."""
+    lin = workloads.C4.linears[1]
+    dev = torch.device("cuda", 0)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(workloads.C4.seed)
+    G = (lin.d_in + 31) // 32
+    steps = torch.exp2(torch.rand((lin.d_out, G, 1), generator=gen, device=dev) * 4 - 10)
+    steps = steps.to(torch.bfloat16).float()
+    levels = torch.randn((lin.d_out, G, 32), generator=gen, device=dev).mul_(2.5).round_()
+    w = (levels.clamp_(-8, 7) * steps).reshape(lin.d_out, G * 32)[:, :lin.d_in]
+    w = w.to(torch.bfloat16).contiguous()
+    del steps, levels
+    for _ in range(2):
+        w4.w4_qat_repack(w, lin.d_in)
+    torch.cuda.synchronize()
+    timer = Timer(torch)
+    for _ in range(iters):
+        timer.start("qat")
+        w4.w4_qat_repack(w, lin.d_in)
+        timer.stop("qat")
+    torch.cuda.synchronize()
+    ms = timer.mean_ms("qat")
+    nbytes = 2 * lin.d_out * lin.d_in + lin.d_out * G * 16 + lin.d_out * G * 2
+    _, _, m = w4.w4_qat_repack(w, lin.d_in, want_m=True)
+    torch.cuda.synchronize()
+    on_grid = float((m > 0).float().mean().item())
+    del w, m
+    return dict(shape=f"{lin.d_out}x{lin.d_in}", us=round(ms * 1e3, 2),
+                gbs=round(nbytes / ms / 1e6, 1), hbm_frac=round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
+                groups_on_grid=round(on_grid, 4))
+
+
 def bench_c3(torch, w4, workloads, iters):
     """28 layers x {qkv, o, gate/up, down}, asymmetric g128, weights generated on the GPU with a
     seeded torch generator (timing only; parity of these shapes is in the GPU tests)."""
@@ -385,7 +421,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
-    ap.add_argument("--only", choices=["c2", "c3", "c4", "c5"], default=None,
+    ap.add_argument("--only", choices=["c2", "c3", "c4", "c5", "qat"], default=None,
                     help="time one workload only (for profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -413,6 +449,8 @@ def main():
             secondary["C4_prefill_gemm"] = bench_c4(torch, w4, workloads, 10)
         elif args.only == "c5":
             secondary["C5_w4a8"] = bench_c5(torch, w4, workloads, 100)
+        elif args.only == "qat":
+            secondary["qat_repack"] = bench_qat(torch, w4, workloads, 10)
         if args.only != "c2":
             print(json.dumps(secondary), flush=True)
             return
@@ -423,6 +461,8 @@ def main():
         secondary["C5_w4a8"] = bench_c5(torch, w4, workloads, 100)
         log("C3 decoder step")
         secondary["C3_decoder_step"] = bench_c3(torch, w4, workloads, 5)
+        log("QAT repack")
+        secondary["qat_repack"] = bench_qat(torch, w4, workloads, 10)
 
     secondary["C2_gate_up_silu_mul"] = dict(
         us=round(r["glu_ms"] * 1e3, 3), gbs=round(r["b_glu"] / r["glu_ms"] / 1e6, 1),

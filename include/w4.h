@@ -8,6 +8,8 @@
  *   [Lab5]  "Lab 5: Gemma4 端到端推理优化"
  *   [Orin]  "Jetson Orin AGX INT4 推理优化实践：super 分支从 9 tok/s 到 24 tok/s"
  *   [Infra] "【infra之路】12-投机解码、量化与推理引擎对比"
+ *   [QAT]   "Yeniden paketlenmiş QAT Gemma 4 26B-A4B, tek bir TPU v6e'de FP8 işlemenin 1.9 katı
+ *            verimle sunuluyor"
  *
  * Conventions shared by every entry point
  *   - Array arguments are DEVICE pointers owned by the caller.  The library never allocates,
@@ -88,6 +90,25 @@ int w4_packed_layout(int64_t d_out, int64_t d_in, int group_size, int64_t *k_pad
  */
 int w4_pack(const float *w, int64_t d_out, int64_t d_in, int64_t ldw, int group_size, int mode,
             uint8_t *qweight, uint16_t *scales, uint16_t *zeros, void *stream);
+
+/*
+ * w4_qat_repack -- pack a weight trained on the 4-bit grid (a QAT export stored in bf16) without
+ * re-quantizing it: the g32 symmetric format of w4_pack (group_size = 32, W4_SYM).
+ * [QAT "Yeniden nicelendirme değil, yeniden paketleme"]: per row and group of 32 columns,
+ *   a = max|r|; for m = 1 .. 8 the step a / m is kept if it reproduces the whole group, i.e.
+ *   every v = r / (a / m) (fp32) is within 1/16 of a level l = rint(v) in [-8, 7];
+ *   the kept levels give the codes l + 8 and the least-squares step s = sum r l / sum l^2
+ *   (fp64 sums and quotient, rounded to fp32, stored as bf16).
+ * A group no m reproduces is off the grid: it is packed by w4_pack's symmetric rule and m = 0 is
+ * reported for it. An all-zero group has m = 1 and scale +0. Padded columns decode to 0.
+ *   w        bf16 [d_out][ldw], ldw >= d_in, ldw % 8 == 0, 16-byte aligned; only k < d_in is read
+ *   qweight  uint8 [d_out][k_pad/2], k_pad = ceil(d_in/32)*32, 16-byte aligned
+ *   scales   bf16 [d_out][k_pad/32]
+ *   m_out    uint8 [d_out][k_pad/32] or NULL: the m kept per group, 0 for groups off the grid
+ * The result is bit-identical to the CPU reference of the same rule.
+ */
+int w4_qat_repack(const uint16_t *w, int64_t d_out, int64_t d_in, int64_t ldw, uint8_t *qweight,
+                  uint16_t *scales, uint8_t *m_out, void *stream);
 
 /*
  * w4_gemv -- W4A16 decode linear for 1 <= M <= 64 token rows, weights read once per call.

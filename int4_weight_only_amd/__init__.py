@@ -17,6 +17,7 @@ import torch
 __all__ = [
     "W4_SYM", "W4_ASYM", "W4_OUT_BF16", "W4_OUT_F32", "W4Error", "packed_layout", "w4_pack",
     "w4_gemv", "w4_gemv_glu", "w4_gemm", "act_quant_int8", "w4a8_gemv", "w4a8_gemm", "w4a8_linear",
+    "w4_qat_repack",
     "w4_linear",
     "library_path",
 ]
@@ -45,6 +46,7 @@ def _load():
     lib.w4_packed_layout.argtypes = [i64, i64, i32, ctypes.POINTER(i64), ctypes.POINTER(i64),
                                      ctypes.POINTER(ctypes.c_size_t)]
     lib.w4_pack.argtypes = [p, i64, i64, i64, i32, i32, p, p, p, p]
+    lib.w4_qat_repack.argtypes = [p, i64, i64, i64, p, p, p, p]
     lin = [p, i64, i64, p, p, p, p, i64, i64, i32, p, i64, i32]
     lib.w4_gemv.argtypes = lin + [p]
     lib.w4_gemv_glu.argtypes = lin + [p]
@@ -53,7 +55,7 @@ def _load():
     lib.w4a8_gemv.argtypes = [p, p, i64, i64, p, p, p, i64, i64, p, i64, i32, p, p]
     lib.w4a8_gemm.argtypes = lib.w4a8_gemv.argtypes
     lib.w4a8_linear.argtypes = [p, i64, i64, p, p, p, i64, i64, p, i64, i32, p, p, p]
-    for f in ("w4_packed_layout", "w4_pack", "w4_gemv", "w4_gemv_glu", "w4_gemm",
+    for f in ("w4_packed_layout", "w4_pack", "w4_qat_repack", "w4_gemv", "w4_gemv_glu", "w4_gemm",
               "act_quant_int8", "w4a8_gemv", "w4a8_gemm", "w4a8_linear"):
         getattr(lib, f).restype = i32
     lib.w4_status_string.argtypes = [i32]
@@ -123,6 +125,23 @@ def w4_pack(w, group_size, mode, d_in=None):
     _check("w4_pack", _lib.w4_pack(_ptr(w), d_out, d_in, w.stride(0), group_size, mode,
                                    _ptr(qweight), _ptr(scales), _ptr(zeros), _stream(dev)))
     return qweight, scales, zeros
+
+
+def w4_qat_repack(w, d_in=None, want_m=False):
+    """Pack a bf16 weight [d_out][ldw] (first d_in columns) that lies on the 4-bit grid per group
+    of 32 columns, keeping its levels (the g32 symmetric format).  Returns (qweight, scales), plus
+    m uint8 [d_out][G] (the divisor kept per group, 0 off the grid) when want_m."""
+    _need(w, "w", torch.bfloat16, dim=2)
+    d_out, ldw = w.shape
+    d_in = ldw if d_in is None else d_in
+    k_pad, n_groups, _ = packed_layout(d_out, d_in, 32)
+    dev = w.device
+    qweight = torch.empty((d_out, k_pad // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((d_out, n_groups), dtype=torch.bfloat16, device=dev)
+    m = torch.empty((d_out, n_groups), dtype=torch.uint8, device=dev) if want_m else None
+    _check("w4_qat_repack", _lib.w4_qat_repack(_ptr(w), d_out, d_in, w.stride(0), _ptr(qweight),
+                                               _ptr(scales), _ptr(m), _stream(dev)))
+    return (qweight, scales, m) if want_m else (qweight, scales)
 
 
 def _linear(fn_name, x, qweight, scales, zeros, bias, d_in, group_size, out_dtype, out):

@@ -113,6 +113,20 @@ int w4_pack(const float *w, int64_t d_out, int64_t d_in, int64_t ldw, int group_
     return err == hipSuccess ? W4_OK : hip_fail(err);
 }
 
+int w4_qat_repack(const uint16_t *w, int64_t d_out, int64_t d_in, int64_t ldw, uint8_t *qweight,
+                  uint16_t *scales, uint8_t *m_out, void *stream) {
+    if (!w || !qweight || !scales) return W4_ERR_NULL;
+    if (int st = check_dims(d_out, d_in)) return st;
+    if (ldw < d_in) return W4_ERR_SHAPE;
+    if (ldw > W4_MAX_DIM) return W4_ERR_RANGE;
+    if (!aligned(w, 16) || ldw % 8 != 0 || !aligned(qweight, 16) || !aligned(scales, 2))
+        return W4_ERR_ALIGN;
+    if (!w4::qat_repack_supported(d_out, (d_in + 31) / 32)) return W4_ERR_RANGE;
+    const hipError_t err = w4::launch_qat_repack(w, d_out, d_in, ldw, qweight, scales, m_out,
+                                                 static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? W4_OK : hip_fail(err);
+}
+
 int w4_gemv(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
             const uint16_t *scales, const uint16_t *zeros, const uint16_t *bias, int64_t d_out,
             int64_t d_in, int group_size, void *y, int64_t ldy, int out_dtype, void *stream) {

@@ -32,6 +32,12 @@ hipError_t launch_w4a8_linear(const uint16_t *x, int64_t M, int64_t ldx, const u
                               int64_t d_in, int64_t k_pad, void *y, int64_t ldy, bool out_f32,
                               float *s_x, int32_t *acc, hipStream_t stream);
 
+// Repack of bf16 weights on the 4-bit grid into the g32 symmetric format (qat_repack.hip).
+bool qat_repack_supported(int64_t d_out, int64_t n_groups);
+hipError_t launch_qat_repack(const uint16_t *w, int64_t d_out, int64_t d_in, int64_t ldw,
+                             uint8_t *qweight, uint16_t *scales, uint8_t *m_out,
+                             hipStream_t stream);
+
 // W4A8 prefill GEMM on the int8 matrix cores (gemm_w4a8.hip), any M.
 bool gemm_w4a8_supported(int64_t M, int64_t d_out, int64_t ldq, int64_t k_pad);
 hipError_t launch_gemm_w4a8(const int8_t *q, const float *s_x, int64_t M, int64_t ldq,

@@ -31,6 +31,7 @@ def lib():
     L.w4_packed_layout.argtypes = [i64, i64, i32, ctypes.POINTER(i64), ctypes.POINTER(i64),
                                    ctypes.POINTER(ctypes.c_size_t)]
     L.w4_pack.argtypes = [p, i64, i64, i64, i32, i32, p, p, p, p]
+    L.w4_qat_repack.argtypes = [p, i64, i64, i64, p, p, p, p]
     lin = [p, i64, i64, p, p, p, p, i64, i64, i32, p, i64, i32]
     L.w4_gemv.argtypes = lin + [p]
     L.w4_gemv_glu.argtypes = lin + [p]
@@ -47,7 +48,7 @@ def lib():
 def test_header_declares_the_five_entry_points():
     names = declared_functions()
     for n in ("w4_pack", "w4_gemv", "w4_gemv_glu", "w4_gemm", "act_quant_int8", "w4a8_gemv",
-              "w4a8_gemm", "w4a8_linear",
+              "w4a8_gemm", "w4a8_linear", "w4_qat_repack",
               "w4_packed_layout", "w4_status_string",
               "w4_last_hip_error"):
         assert n in names
@@ -180,6 +181,29 @@ def test_w4a8_rejects_bad_arguments(lib):
     assert call(acc=E + 2) == W4_ERR_ALIGN
     big = (1 << 20) + 16
     assert call(d_in=big, ldq=big) == W4_ERR_RANGE
+
+
+def test_qat_repack_rejects_bad_arguments(lib):
+    f = lib.w4_qat_repack
+
+    def call(**kw):
+        a = dict(w=A, d_out=16, d_in=100, ldw=104, qw=C, sc=D, m=None)
+        a.update(kw)
+        return f(a["w"], a["d_out"], a["d_in"], a["ldw"], a["qw"], a["sc"], a["m"], None)
+
+    assert call(w=None) == W4_ERR_NULL
+    assert call(qw=None) == W4_ERR_NULL
+    assert call(sc=None) == W4_ERR_NULL
+    assert call(d_out=0) == W4_ERR_SHAPE
+    assert call(d_in=0) == W4_ERR_SHAPE
+    assert call(ldw=96) == W4_ERR_SHAPE
+    assert call(ldw=108) == W4_ERR_ALIGN
+    assert call(w=A + 8) == W4_ERR_ALIGN
+    assert call(qw=C + 8) == W4_ERR_ALIGN
+    assert call(sc=D + 1) == W4_ERR_ALIGN
+    assert call(d_in=(1 << 24) + 8, ldw=(1 << 24) + 8) == W4_ERR_RANGE
+    # the grid: d_out * ceil(d_in / 32) / 256 < 2^31
+    assert call(d_out=1 << 24, d_in=1 << 24, ldw=1 << 24) == W4_ERR_RANGE
 
 
 def test_w4a8_gemm_rejects_bad_arguments(lib):

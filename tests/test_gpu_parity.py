@@ -117,6 +117,77 @@ def test_pack_configs_full_size():
 
 
 # ------------------------------------------------------------------------------------------
+# w4_qat_repack
+# ------------------------------------------------------------------------------------------
+def check_qat(w_bits, d_in, what):
+    """w4_qat_repack against the oracle's O8: codes, scales and the kept m, bit for bit."""
+    _announce("w4_qat_repack", what, w_bits.shape, d_in)
+    qw_o, sc_o, m_o = oracle.qat_repack(w_bits, d_in)
+    qw, sc, m = w4.w4_qat_repack(dev_bf16(w_bits), d_in, want_m=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(m), m_o), f"{what}: kept m differs"
+    assert np.array_equal(host(qw), qw_o), f"{what}: codes differ"
+    assert np.array_equal(host_bits(sc), sc_o), f"{what}: scales differ"
+    return qw_o, sc_o, m_o
+
+
+def _qat_edge_groups():
+    """Groups on the edges of the rule: all zero, one value 0.047 and one 0.078 of a level off,
+    a peak at +8 steps, a peak at -8, subnormal steps, a coarser grid (all levels even), and a
+    group whose peak is rounded (the least-squares step differs from max / 7)."""
+    base = np.array([7, -3, 1, 0, 5, -6, 2, -1] * 4, dtype=np.float32)
+    rows = [np.zeros(32, np.float32)]
+    near, far, plus8, minus8 = base.copy(), base.copy(), base.copy(), base.copy()
+    near[1], far[1], plus8[0], minus8[2] = -3.046875, -3.078125, 8.0, -8.0
+    rows += [near, far, plus8, minus8]
+    rows += [base * np.float32(2.0 ** -130), base * np.float32(3 * 2.0 ** -127)]
+    rows += [np.array([6, -4, 2, 0, 4, -2, 2, -6] * 4, np.float32) * np.float32(0.375)]
+    peak = base.copy()
+    peak[0] = 7.03125
+    rows.append(peak)
+    edge = base.copy()
+    edge[1] = -3.0625  # exactly 1/16 of a level off: still on the grid
+    rows.append(edge)
+    tiny = base.copy()
+    tiny[3] = 2.0 ** -12  # a nonzero value far below a level: no divisor is ruled out early
+    rows.append(tiny)
+    return workloads.to_bf16_bits(np.concatenate(rows).reshape(1, -1))
+
+
+def test_qat_repack_ragged_and_edges():
+    for i, (d_out, d_in, ldw) in enumerate([(1, 1, 8), (3, 40, 48), (17, 100, 104), (64, 1000, 1000),
+                                            (5, 3600, 3616), (300, 4100, 4104)]):
+        w = workloads.qat_grid_weight(61, i, d_out, ldw, off_grid_frac=0.1)
+        w[:, d_in:] = 0x7FC0  # NaN past d_in: never read
+        check_qat(w, d_in, f"{d_out}x{d_in} ldw={ldw}")
+    w = _qat_edge_groups()
+    qw, sc, m = check_qat(w, w.shape[1], "edge groups")
+    assert m[0].tolist() == [1, 7, 0, 0, 8, 7, 7, 3, 7, 7, 7]
+
+
+def test_qat_repack_c4_full_size():
+    """The C4 q/k/v and down shapes (g32), 1% of the groups off the grid."""
+    for li in (0, 2):
+        lin = workloads.C4.linears[li]
+        w = workloads.qat_grid_weight(workloads.C4.seed, li, lin.d_out, lin.d_in, 0.01)
+        _, _, m = check_qat(w, lin.d_in, f"C4/{lin.name}")
+        assert 0 < np.count_nonzero(m == 0) < m.size // 50
+
+
+def test_qat_repack_feeds_the_linear():
+    """The repacked weight is a g32 symmetric pack: w4_gemv and w4_gemm on it against O4 on the
+    oracle's repack."""
+    d_out, d_in = 200, 1000
+    w = workloads.qat_grid_weight(62, 0, d_out, d_in, 0.05)
+    qw_o, sc_o, _ = oracle.qat_repack(w, d_in)
+    qw, sc = w4.w4_qat_repack(dev_bf16(w), d_in)
+    for M in (1, 5, 130):
+        x = workloads.activations(62, M, M, d_in)
+        check_linear("w4_gemv" if M <= 64 else "w4_gemm", x, (qw_o, sc_o, None), (qw, sc, None),
+                     None, d_in, 32, f"repacked M={M}")
+
+
+# ------------------------------------------------------------------------------------------
 # act_quant_int8
 # ------------------------------------------------------------------------------------------
 def check_act_quant(x_bits, what, K=None):

@@ -46,6 +46,26 @@ def weight(seed: int, lin: int, d_out: int, d_in: int, sigma: float = W_SIGMA) -
     return rng(seed, tid(lin, TID_W)).normal(0.0, sigma, size=(d_out, d_in)).astype(np.float32)
 
 
+def qat_grid_weight(seed: int, lin: int, d_out: int, d_in: int,
+                    off_grid_frac: float = 0.0) -> np.ndarray:
+    """bf16 bit patterns [d_out][d_in] standing in for a weight trained on the 4-bit grid (a QAT
+    export stored in bf16): per row and 32-column group, a step drawn log-uniformly in
+    [2^-10, 2^-6] and rounded to bf16, times integer levels rint(N(0, 2.5^2)) clipped to [-8, 7],
+    the product rounded to bf16.  A fraction off_grid_frac of the groups holds N(0, 0.02^2) values
+    instead (off the grid).  Nothing here is derived from a weight: the grid is drawn, not found."""
+    r = rng(seed, tid(lin, TID_W))
+    n_groups = (d_in + 31) // 32
+    steps = np.exp2(r.uniform(-10.0, -6.0, size=(d_out, n_groups))).astype(np.float32)
+    steps = (to_bf16_bits(steps).astype(np.uint32) << 16).view(np.float32)
+    levels = np.clip(np.rint(r.normal(0.0, 2.5, size=(d_out, n_groups, 32))), -8, 7)
+    vals = (levels.astype(np.float32) * steps[:, :, None]).reshape(d_out, n_groups * 32)
+    if off_grid_frac > 0.0:
+        off = r.random((d_out, n_groups)) < off_grid_frac
+        noise = r.normal(0.0, W_SIGMA, size=(d_out, n_groups, 32)).astype(np.float32)
+        vals = np.where(np.repeat(off, 32, axis=1), noise.reshape(d_out, -1), vals)
+    return to_bf16_bits(np.ascontiguousarray(vals[:, :d_in]))
+
+
 def add_weight_outliers(w: np.ndarray, seed: int, lin: int, frac: float,
                         value: float) -> np.ndarray:
     """Replace round(frac * size) distinct uniformly chosen entries with +-value (fair sign)."""
