@@ -3,6 +3,7 @@
 TEST INFRASTRUCTURE ONLY: the test-suite, the smoke check and the CPU-baseline leg of the
 benchmark import this package; the product library never does, and this package imports nothing
 from it.  The arithmetic lives in oracle.c (plain C); this module only marshals numpy arrays.
+The GPTQ reference (O9) is numpy fp64 in oracle/gptq.py.
 
 Every function follows the pages cited in oracle.c:
   [Lab5]  "Lab 5: Gemma4 端到端推理优化"

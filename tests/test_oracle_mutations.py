@@ -112,3 +112,42 @@ def test_planted_mistake_is_caught(tmp_path, golden_dir, name, old, new):
     with oracle.use_library(str(lib)):
         caught = _any_pin_fails(golden_dir)
     assert caught is not None, f"no pin catches: {name}"
+
+
+# The GPTQ reference (oracle/gptq.py, numpy): each slip planted in a copy of the module makes at
+# least one GPTQ pin fail.
+GPTQ_PY = os.path.join(os.path.dirname(ORACLE_C), "gptq.py")
+GPTQ_MUTATIONS = [
+    ("gptq update sign", "W[:, i:] -= np.outer(e, U[i, i:])", "W[:, i:] += np.outer(e, U[i, i:])"),
+    ("gptq column of U", "W[:, i:] -= np.outer(e, U[i, i:])", "W[:, i:] -= np.outer(e, U[i:, i])"),
+    ("gptq error not normalised", "e = err / U[i, i]", "e = err"),
+    ("gptq no damping", "h[np.diag_indices_from(h)] += lam", "pass"),
+    ("gptq dead weights kept", "w[:, dead] = 0.0", "pass"),
+    ("gptq hessian 1/N", "(2.0 / x.shape[0])", "(1.0 / x.shape[0])"),
+    ("gptq loss without U_ii", "L += 0.5 * float(np.sum(err * err)) / (U[i, i] * U[i, i])",
+     "L += 0.5 * float(np.sum(err * err))"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", GPTQ_MUTATIONS, ids=[m[0] for m in GPTQ_MUTATIONS])
+def test_planted_gptq_mistake_is_caught(monkeypatch, name, old, new):
+    import types
+    src = open(GPTQ_PY).read()
+    assert src.count(old) == 1, f"mutation anchor not unique/found: {name}"
+    mod = types.ModuleType("oracle.gptq_mut")
+    mod.__package__ = "oracle"
+    exec(compile(src.replace(old, new), GPTQ_PY, "exec"), mod.__dict__)
+    monkeypatch.setattr(pins, "gq", mod)
+    caught = None
+    for pname, fn, cases in _pin_tests():
+        if "gptq" not in pname:
+            continue
+        for kw in cases:
+            try:
+                fn(**kw)
+            except Exception:
+                caught = pname
+                break
+        if caught:
+            break
+    assert caught is not None, f"no pin catches: {name}"

@@ -626,3 +626,128 @@ def test_qat_repack_zero_group_pads_and_stride():
     assert _bits_f32(sc[1]).tolist() == [0.5, 0.125]
     codes = _nibbles(qw)[1]
     assert np.array_equal(codes[32:40], lv + 8) and np.all(codes[40:] == 8)
+
+
+# ------------------------------------------------------------------------------------------
+# O9: GPTQ.  [Lab5] "从 RTN 到 GPTQ": the layer objective ||X (W - Q)^T||_F^2, H = (2/N) X^T X,
+# dead columns, damping lambda = alpha mean(diag H), H^-1 = U^T U, e_i = (w_i - q_i) / U_ii,
+# W[:, i:] -= e_i U[i, i:], L_pred = 1/2 sum ||w_i - q_i||^2 / U_ii^2.
+# ------------------------------------------------------------------------------------------
+import oracle.gptq as gq  # noqa: E402
+
+
+def _calib(seed, N, d_in, dead=()):
+    """bf16 calibration activations with correlated channels (a few latent factors plus noise);
+    the listed columns are zero in every row."""
+    rng = np.random.default_rng(seed)
+    lat = rng.normal(size=(N, max(1, d_in // 4)))
+    mix = rng.normal(size=(lat.shape[1], d_in)) / 2.0
+    x = lat @ mix + 0.3 * rng.normal(size=(N, d_in))
+    x[:, list(dead)] = 0.0
+    return _rne_bf16(x.astype(np.float32))
+
+
+def _deq(codes, scales_bits, zeros_bits, d_in, span):
+    """s (code - z) per column, from the stored bits (plain arithmetic)."""
+    G = np.arange(d_in) // span
+    s = _bits_f32(scales_bits)[:, G].astype(np.float64)
+    z = _bits_f32(zeros_bits)[:, G].astype(np.float64) if zeros_bits is not None else 8.0
+    return s * (codes[:, :d_in].astype(np.float64) - z)
+
+
+@pytest.mark.parametrize("g,mode", [(32, SYM), (128, ASYM), (0, SYM)])
+def test_gptq_predicted_loss_is_the_objective(g, mode):
+    """With H = (2/N) X^T X + lambda I and the updates of the page, W - Q = E U row by row, so
+    1/2 (W - Q) H (W - Q)^T = 1/2 sum e_i^2 = L_pred: L_pred equals
+    (1/N) ||X (W - Q)^T||_F^2 + (lambda / 2) ||W - Q||_F^2, computed here from X, W and the packed
+    result alone."""
+    d_out, d_in, N = 24, 200, 96
+    w = workloads.weight(90, g + mode, d_out, d_in)
+    xb = _calib(90 + g, N, d_in)
+    r = gq.gptq(w, xb, g, mode)
+    kp = oracle.k_pad(d_in, g)
+    span = kp // oracle.n_groups(d_in, g)
+    q = _deq(r["codes"], r["scales"], r["zeros"], d_in, span)
+    x = _bits_f32(xb).astype(np.float64)
+    lam = 0.01 * np.mean(2.0 / N * np.sum(x * x, axis=0))
+    d = w.astype(np.float64) - q
+    obj = np.sum((x @ d.T) ** 2) / N + 0.5 * lam * np.sum(d * d)
+    assert r["L_pred"] == pytest.approx(obj, rel=1e-8)
+
+
+def test_gptq_diagonal_hessian_is_rtn():
+    """Orthogonal calibration columns (X = I): H is diagonal, U is diagonal, nothing propagates,
+    and GPTQ gives O1's codes and scales."""
+    d_out, d_in = 16, 96
+    w = workloads.weight(91, 0, d_out, d_in)
+    xb = _rne_bf16(np.eye(d_in, dtype=np.float32))
+    for g, mode in ((32, SYM), (32, ASYM), (0, SYM)):
+        r = gq.gptq(w, xb, g, mode)
+        qw, sc, zr = oracle.pack(w, g, mode)
+        assert np.array_equal(r["qweight"], qw) and np.array_equal(r["scales"], sc)
+        if mode == ASYM:
+            assert np.array_equal(r["zeros"], zr)
+
+
+def test_gptq_two_columns_obs_closed_form():
+    """Two columns in one group: after q0, the optimal-brain-surgeon update of the textbook,
+    w1' = w1 + (w0 - q0) H01 / H11 (damped H), and q1 = the code of w1' with the group's scale."""
+    rng = np.random.default_rng(92)
+    d_out, N = 64, 40
+    w = rng.normal(0, 0.02, size=(d_out, 2)).astype(np.float32)
+    xb = _calib(92, N, 2)
+    r = gq.gptq(w, xb, 32, SYM)
+    x = _bits_f32(xb).astype(np.float64)
+    H = 2.0 / N * (x.T @ x)
+    H += 0.01 * np.mean(np.diag(H)) * np.eye(2)
+    s = _bits_f32(r["scales"][:, 0]).astype(np.float64)
+    c0 = r["codes"][:, 0].astype(np.float64)
+    q0 = s * (c0 - 8.0)
+    w1p = w[:, 1].astype(np.float64) + (w[:, 0] - q0) * H[0, 1] / H[1, 1]
+    s32 = _bits_f32(r["scales"][:, 0])
+    c1 = np.clip(np.rint(w1p.astype(np.float32) / s32 + np.float32(8.0)), 0, 15)
+    assert np.array_equal(r["codes"][:, 1], c1.astype(np.uint8))
+    # column 0 itself is O1's code of w0 with the scale of the pair
+    c0_rtn = np.clip(np.rint(w[:, 0] / s32 + np.float32(8.0)), 0, 15)
+    assert np.array_equal(r["codes"][:, 0], c0_rtn.astype(np.uint8))
+
+
+@pytest.mark.parametrize("seed", [93, 94, 95])
+def test_gptq_beats_rtn_on_the_layer_objective(seed):
+    """On correlated calibration activations GPTQ's ||X (W - Q)^T|| is below RTN's (the point of
+    the section), with every result on the same grid of codes and scales."""
+    d_out, d_in, N = 32, 256, 128
+    w = workloads.weight(seed, 0, d_out, d_in)
+    xb = _calib(seed, N, d_in)
+    x = _bits_f32(xb).astype(np.float64)
+    for g, mode in ((32, SYM), (128, ASYM)):
+        r = gq.gptq(w, xb, g, mode)
+        qw, sc, zr = oracle.pack(w, g, mode)
+        span = oracle.k_pad(d_in, g) // oracle.n_groups(d_in, g)
+        codes_rtn = np.stack([qw & 0xF, qw >> 4], axis=-1).reshape(d_out, -1)
+        q_rtn = _deq(codes_rtn, sc, zr, d_in, span)
+        q_gptq = _deq(r["codes"], r["scales"], r["zeros"], d_in, span)
+        e_rtn = np.sum((x @ (w - q_rtn).T) ** 2)
+        e_gptq = np.sum((x @ (w - q_gptq).T) ** 2)
+        assert e_gptq < 0.9 * e_rtn, (g, mode, e_gptq, e_rtn)
+
+
+def test_gptq_dead_column():
+    """A column that is zero in every calibration row: its weights become 0 (the zero code), H's
+    diagonal entry becomes 1 before damping, and the loss identity still holds."""
+    d_out, d_in, N = 16, 64, 80
+    w = workloads.weight(96, 0, d_out, d_in)
+    xb = _calib(96, N, d_in, dead=(5, 40))
+    r = gq.gptq(w, xb, 32, SYM)
+    assert np.all(r["codes"][:, [5, 40]] == 8)
+    assert r["dead"][[5, 40]].all() and r["dead"].sum() == 2
+    x = _bits_f32(xb).astype(np.float64)
+    diag = 2.0 / N * np.sum(x * x, axis=0)
+    diag[[5, 40]] = 1.0
+    lam = 0.01 * np.mean(diag)
+    w0 = w.astype(np.float64)
+    w0[:, [5, 40]] = 0.0
+    q = _deq(r["codes"], r["scales"], None, d_in, 32)
+    d = w0 - q
+    obj = np.sum((x @ d.T) ** 2) / N + 0.5 * lam * np.sum(d * d) + 0.5 * np.sum(d[:, [5, 40]] ** 2)
+    assert r["L_pred"] == pytest.approx(obj, rel=1e-8)
