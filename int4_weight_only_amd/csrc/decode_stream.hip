@@ -26,6 +26,8 @@
 #include "w4_quant.h"
 #include "w4_launch.h"
 
+#include <type_traits>
+
 namespace w4 {
 
 namespace {
@@ -824,21 +826,34 @@ hipError_t launch_w4a16_stream_t(bool zp, const uint16_t *x, int64_t ldx, int M,
     // one token on rows of 8 or more steps: two segments per row (see the kernel)
     constexpr int SEG = MT == 1 && T >= 8 ? 2 : 1;
     static_assert(T % SEG == 0 && S.nb % SEG == 0, "segments");
-    // segmented long rows: 8-wave workgroups, so that the activations are converted once per
-    // 8 waves instead of once per 4
-    constexpr int BT = SEG > 1 ? 2 * kThreads : kThreads;
-    const StreamPlan p = plan_stream(d_out, T, S.rw, S.nb, SEG, BT / kWave);
     const size_t lds = sizeof(XChunk16) * (size_t)MT * (size_t)(k_pad / kChunkCols + 1);
-    if (zp)
-        hipLaunchKernelGGL((gemv_w4a16_stream_kernel<MT, T / SEG, S.rw, S.nb, true, SEG, BT>),
-                           dim3(p.grid), dim3(BT), lds, stream, x, ldx, M, qweight, scales,
-                           zeros, bias, d_out, d_in, k_pad, shift, n_groups, y, ldy,
-                           out_f32 ? 1 : 0, p.n_batches);
-    else
-        hipLaunchKernelGGL((gemv_w4a16_stream_kernel<MT, T / SEG, S.rw, S.nb, false, SEG, BT>),
-                           dim3(p.grid), dim3(BT), lds, stream, x, ldx, M, qweight, scales,
-                           zeros, bias, d_out, d_in, k_pad, shift, n_groups, y, ldy,
-                           out_f32 ? 1 : 0, p.n_batches);
+    auto launch = [&](auto bt) {
+        constexpr int BT = decltype(bt)::value;
+        const StreamPlan p = plan_stream(d_out, T, S.rw, S.nb, SEG, BT / kWave);
+        if (zp)
+            hipLaunchKernelGGL((gemv_w4a16_stream_kernel<MT, T / SEG, S.rw, S.nb, true, SEG, BT>),
+                               dim3(p.grid), dim3(BT), lds, stream, x, ldx, M, qweight, scales,
+                               zeros, bias, d_out, d_in, k_pad, shift, n_groups, y, ldy,
+                               out_f32 ? 1 : 0, p.n_batches);
+        else
+            hipLaunchKernelGGL((gemv_w4a16_stream_kernel<MT, T / SEG, S.rw, S.nb, false, SEG, BT>),
+                               dim3(p.grid), dim3(BT), lds, stream, x, ldx, M, qweight, scales,
+                               zeros, bias, d_out, d_in, k_pad, shift, n_groups, y, ldy,
+                               out_f32 ? 1 : 0, p.n_batches);
+    };
+    if (SEG > 1) {
+        // segmented long rows: one workgroup per CU of 7 or 8 waves (the activations are
+        // converted once per workgroup), whichever leaves fewer wave slots idle in the last
+        // round of rows (C2 down: 3584 rows = 2 rounds of 256 x 7 waves)
+        const int64_t cus = device_cu_count();
+        auto idle = [&](int64_t w) { return (d_out + cus * w - 1) / (cus * w) * cus * w - d_out; };
+        if (idle(7) < idle(8))
+            launch(std::integral_constant<int, 7 * kWave>());
+        else
+            launch(std::integral_constant<int, 2 * kThreads>());
+    } else {
+        launch(std::integral_constant<int, kThreads>());
+    }
     return hipGetLastError();
 }
 
