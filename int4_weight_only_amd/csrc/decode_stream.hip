@@ -903,13 +903,27 @@ hipError_t launch_w4a8_stream_t(const void *act, int64_t ldq, int M, float *s_x,
     static_assert(T % SEG == 0 && S.nb % SEG == 0, "segments");
     // 8-wave workgroups for segmented rows (see launch_w4a16_stream_t) and whenever the
     // workgroup quantizes the activations itself: a CU then quantizes the row half as often
+    // (segmented rows: 7 or 8 waves, as in launch_w4a16_stream_t)
     constexpr bool wide = SEG > 1 || FQ;
-    constexpr int BT = wide ? 2 * kThreads : kThreads;
-    const StreamPlan p = plan_stream(d_out, T, S.rw, S.nb, SEG, BT / kWave, FQ && SEG == 1 ? 2 : 1);
     const size_t lds = w4a8_lds_bytes(MT, k_pad, FQ);
-    hipLaunchKernelGGL((gemv_w4a8_stream_kernel<MT, T / SEG, S.rw, S.nb, SEG, BT, FQ>),
-                       dim3(p.grid), dim3(BT), lds, stream, act, ldq, M, s_x, qweight, s_w, bias,
-                       d_out, d_in, k_pad, y, ldy, out_f32 ? 1 : 0, acc, p.n_batches);
+    auto launch = [&](auto bt) {
+        constexpr int BT = decltype(bt)::value;
+        const StreamPlan p =
+            plan_stream(d_out, T, S.rw, S.nb, SEG, BT / kWave, FQ && SEG == 1 ? 2 : 1);
+        hipLaunchKernelGGL((gemv_w4a8_stream_kernel<MT, T / SEG, S.rw, S.nb, SEG, BT, FQ>),
+                           dim3(p.grid), dim3(BT), lds, stream, act, ldq, M, s_x, qweight, s_w,
+                           bias, d_out, d_in, k_pad, y, ldy, out_f32 ? 1 : 0, acc, p.n_batches);
+    };
+    if (SEG > 1) {
+        const int64_t cus = device_cu_count();
+        auto idle = [&](int64_t w) { return (d_out + cus * w - 1) / (cus * w) * cus * w - d_out; };
+        if (idle(7) < idle(8))
+            launch(std::integral_constant<int, 7 * kWave>());
+        else
+            launch(std::integral_constant<int, 2 * kThreads>());
+    } else {
+        launch(std::integral_constant<int, wide ? 2 * kThreads : kThreads>());
+    }
     return hipGetLastError();
 }
 
