@@ -186,24 +186,28 @@ def bench_c2(torch, w4, workloads, steps, warmup, rotate_bytes):
                 rotate_mb=n_copies * per_copy / 1e6, steps_timed=replays * n_copies)
 
 
-def stream_copy_gbs(torch, nbytes=1 << 30, reps=20):
-    """A measured streaming ceiling on the same GPU: torch's device copy of a 1 GiB buffer
-    (bytes read + bytes written per copy, over the copy time)."""
-    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+def stream_ceilings_gbs(torch, nbytes=1 << 30, reps=20):
+    """Measured streaming rates on the same GPU, bytes read + bytes written over the kernel time,
+    for a 1 GiB buffer: torch's device copy, and torch's elementwise xor of int32 (the faster of
+    torch's plain streaming kernels here; its reductions, read-only, run slower than either)."""
+    a = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
     b = torch.empty_like(a)
     a.fill_(1)
-    b.copy_(a)
-    torch.cuda.synchronize()
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    t0.record()
-    for _ in range(reps):
-        b.copy_(a)
-    t1.record()
-    torch.cuda.synchronize()
-    gbs = 2 * nbytes * reps / (t0.elapsed_time(t1) * 1e-3) / 1e9
+    out = {}
+    for name, fn in (("copy", lambda: b.copy_(a)),
+                     ("xor", lambda: torch.bitwise_xor(a, 1, out=b))):
+        fn()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(reps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        out[name] = round(2 * nbytes * reps / (t0.elapsed_time(t1) * 1e-3) / 1e9, 1)
     del a, b
-    return round(gbs, 1)
+    return out
 
 
 def bench_c4(torch, w4, workloads, iters):
@@ -483,7 +487,7 @@ def main():
         "avg_launch_us": round(r["gu_ms"] * 1e3, 3),
         "down_avg_launch_us": round(r["dn_ms"] * 1e3, 3),
         "down_gbs": round(r["b_dn"] / r["dn_ms"] / 1e6, 1),
-        "stream_copy_gbs": stream_copy_gbs(torch),
+        **{f"stream_{k}_gbs": v for k, v in stream_ceilings_gbs(torch).items()},
     }
     line = {
         "metric": METRIC,
