@@ -64,6 +64,7 @@ enum { W4_OUT_BF16 = 0, W4_OUT_F32 = 1 }; /* element type of y                  
 #define W4_MAX_DIM ((int64_t)1 << 24)  /* d_out, d_in, M, K                      */
 #define W4_MAX_W4A8_D_IN ((int64_t)1 << 20) /* keeps sum(code * q) within int32: 2^20*15*127 < 2^31 */
 #define W4_GEMV_MAX_M 64
+#define W4_MAX_GPTQ_D_IN 8192 /* the GPTQ factorization holds d_in x d_in fp32 matrices      */
 
 /*
  * w4_packed_layout -- host-only size query (no GPU work).
@@ -90,6 +91,45 @@ int w4_packed_layout(int64_t d_out, int64_t d_in, int group_size, int64_t *k_pad
  */
 int w4_pack(const float *w, int64_t d_out, int64_t d_in, int64_t ldw, int group_size, int mode,
             uint8_t *qweight, uint16_t *scales, uint16_t *zeros, void *stream);
+
+/*
+ * GPTQ -- quantization that compensates each column's rounding error in the columns after it,
+ * producing the packed format of w4_pack.  [Lab5 从 RTN 到 GPTQ]:
+ *   objective  min_Q ||X W^T - X Q^T||_F^2 over calibration activations X [N][d_in];
+ *   H = (2/N) X^T X; dead columns (H_ii = 0) get H_ii = 1 and zero weights; H += alpha mean(diag H) I;
+ *   H^-1 = U^T U (U upper triangular); columns in order: q_i = the code of w_i (the group's scale
+ *   and zero by w4_pack's rule from the current, already updated weights of the group at its first
+ *   column), e_i = (w_i - q_i) / U_ii, W[:, i:] -= e_i U[i, i:];
+ *   L_pred = 1/2 sum_i ||w_i - q_i||^2 / U_ii^2.
+ * Everything runs in fp32, as on the page.  Three calls, each enqueued on `stream`:
+ *
+ * w4_gptq_hessian -- h = (2/N) X^T X.
+ *   x  bf16 [N][ldx], ldx >= d_in, only k < d_in read;  h  fp32 [d_in][d_in] (written in full)
+ *
+ * w4_gptq_factor -- dead columns, damping, and U with (H + lambda I)^-1 = U^T U.
+ *   h     fp32 [d_in][d_in], in: the Hessian; destroyed (its lower triangle is worked in place)
+ *   alpha the damping factor (the reference uses 0.01), >= 0
+ *   u     fp32 [d_in][d_in], out: U (zeros below the diagonal)
+ *   work  fp32 [d_in][d_in], scratch (the reverse Cholesky factor V, H = V V^T, U = V^-1)
+ *   dead  uint8 [d_in], out: 1 for dead columns
+ *   The factorization launches about 2 d_in small kernels (an offline step).
+ *
+ * w4_gptq_quantize -- the column loop.
+ *   w        fp32 [d_out][ldw], in: the weights; destroyed (the error-updated working copy)
+ *   u, dead  from w4_gptq_factor (dead may be NULL: no dead columns)
+ *   group_size, mode, qweight, scales, zeros: as for w4_pack
+ *   work     fp32 [d_out][32], scratch (a block's errors)
+ *   row_loss fp32 [d_out] or NULL: each row's share of L_pred
+ * Limits: d_in <= W4_MAX_GPTQ_D_IN (W4_ERR_RANGE).
+ */
+int w4_gptq_hessian(const uint16_t *x, int64_t N, int64_t d_in, int64_t ldx, float *h,
+                    void *stream);
+int w4_gptq_factor(float *h, int64_t d_in, float alpha, float *u, float *work, uint8_t *dead,
+                   void *stream);
+int w4_gptq_quantize(float *w, int64_t d_out, int64_t d_in, int64_t ldw, const float *u,
+                     const uint8_t *dead, int group_size, int mode, uint8_t *qweight,
+                     uint16_t *scales, uint16_t *zeros, float *work, float *row_loss,
+                     void *stream);
 
 /*
  * w4_qat_repack -- pack a weight trained on the 4-bit grid (a QAT export stored in bf16) without

@@ -17,7 +17,7 @@ import torch
 __all__ = [
     "W4_SYM", "W4_ASYM", "W4_OUT_BF16", "W4_OUT_F32", "W4Error", "packed_layout", "w4_pack",
     "w4_gemv", "w4_gemv_glu", "w4_gemm", "act_quant_int8", "w4a8_gemv", "w4a8_gemm", "w4a8_linear",
-    "w4_qat_repack",
+    "w4_qat_repack", "gptq_hessian", "gptq_factor", "gptq_quantize", "gptq",
     "w4_linear",
     "library_path",
 ]
@@ -47,6 +47,9 @@ def _load():
                                      ctypes.POINTER(ctypes.c_size_t)]
     lib.w4_pack.argtypes = [p, i64, i64, i64, i32, i32, p, p, p, p]
     lib.w4_qat_repack.argtypes = [p, i64, i64, i64, p, p, p, p]
+    lib.w4_gptq_hessian.argtypes = [p, i64, i64, i64, p, p]
+    lib.w4_gptq_factor.argtypes = [p, i64, ctypes.c_float, p, p, p, p]
+    lib.w4_gptq_quantize.argtypes = [p, i64, i64, i64, p, p, i32, i32, p, p, p, p, p, p]
     lin = [p, i64, i64, p, p, p, p, i64, i64, i32, p, i64, i32]
     lib.w4_gemv.argtypes = lin + [p]
     lib.w4_gemv_glu.argtypes = lin + [p]
@@ -55,7 +58,8 @@ def _load():
     lib.w4a8_gemv.argtypes = [p, p, i64, i64, p, p, p, i64, i64, p, i64, i32, p, p]
     lib.w4a8_gemm.argtypes = lib.w4a8_gemv.argtypes
     lib.w4a8_linear.argtypes = [p, i64, i64, p, p, p, i64, i64, p, i64, i32, p, p, p]
-    for f in ("w4_packed_layout", "w4_pack", "w4_qat_repack", "w4_gemv", "w4_gemv_glu", "w4_gemm",
+    for f in ("w4_packed_layout", "w4_pack", "w4_qat_repack", "w4_gptq_hessian", "w4_gptq_factor",
+              "w4_gptq_quantize", "w4_gemv", "w4_gemv_glu", "w4_gemm",
               "act_quant_int8", "w4a8_gemv", "w4a8_gemm", "w4a8_linear"):
         getattr(lib, f).restype = i32
     lib.w4_status_string.argtypes = [i32]
@@ -142,6 +146,65 @@ def w4_qat_repack(w, d_in=None, want_m=False):
     _check("w4_qat_repack", _lib.w4_qat_repack(_ptr(w), d_out, d_in, w.stride(0), _ptr(qweight),
                                                _ptr(scales), _ptr(m), _stream(dev)))
     return (qweight, scales, m) if want_m else (qweight, scales)
+
+
+def gptq_hessian(x, d_in=None):
+    """H = (2/N) X^T X, fp32 [d_in][d_in], from bf16 calibration activations x [N][ldx]."""
+    _need(x, "x", torch.bfloat16, dim=2)
+    N = x.shape[0]
+    d_in = x.shape[1] if d_in is None else d_in
+    h = torch.empty((d_in, d_in), dtype=torch.float32, device=x.device)
+    _check("w4_gptq_hessian", _lib.w4_gptq_hessian(_ptr(x), N, d_in, x.stride(0), _ptr(h),
+                                                   _stream(x.device)))
+    return h
+
+
+def gptq_factor(h, alpha=0.01):
+    """Dead columns, damping and U with (H + lambda I)^-1 = U^T U.  h fp32 [d_in][d_in] is used as
+    the working matrix and destroyed.  Returns (u fp32 [d_in][d_in], dead uint8 [d_in])."""
+    _need(h, "h", torch.float32, dim=2)
+    d_in = h.shape[0]
+    if h.shape[1] != d_in or not h.is_contiguous():
+        raise ValueError("h must be a contiguous square matrix")
+    u = torch.empty_like(h)
+    work = torch.empty_like(h)
+    dead = torch.empty((d_in,), dtype=torch.uint8, device=h.device)
+    _check("w4_gptq_factor", _lib.w4_gptq_factor(_ptr(h), d_in, float(alpha), _ptr(u), _ptr(work),
+                                                 _ptr(dead), _stream(h.device)))
+    return u, dead
+
+
+def gptq_quantize(w, u, dead, group_size, mode, d_in=None):
+    """The GPTQ column loop on fp32 weights w [d_out][ldw] (used as the working copy and
+    destroyed).  Returns (qweight, scales, zeros or None, row_loss fp32 [d_out])."""
+    _need(w, "w", torch.float32, dim=2)
+    dev = w.device
+    _need(u, "u", torch.float32, dev, 2)
+    if dead is not None:
+        _need(dead, "dead", torch.uint8, dev, 1)
+    d_out, ldw = w.shape
+    d_in = ldw if d_in is None else d_in
+    if tuple(u.shape) != (d_in, d_in) or not u.is_contiguous():
+        raise ValueError(f"u must be contiguous [{d_in}][{d_in}]")
+    k_pad, n_groups, _ = packed_layout(d_out, d_in, group_size)
+    qweight = torch.empty((d_out, k_pad // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((d_out, n_groups), dtype=torch.bfloat16, device=dev)
+    zeros = torch.empty_like(scales) if mode == W4_ASYM else None
+    work = torch.empty((d_out, 32), dtype=torch.float32, device=dev)
+    row_loss = torch.empty((d_out,), dtype=torch.float32, device=dev)
+    _check("w4_gptq_quantize", _lib.w4_gptq_quantize(
+        _ptr(w), d_out, d_in, w.stride(0), _ptr(u), _ptr(dead), group_size, mode, _ptr(qweight),
+        _ptr(scales), _ptr(zeros), _ptr(work), _ptr(row_loss), _stream(dev)))
+    return qweight, scales, zeros, row_loss
+
+
+def gptq(w, x, group_size, mode, alpha=0.01, d_in=None):
+    """GPTQ of fp32 weights w [d_out][>= d_in] with bf16 calibration activations x [N][>= d_in]
+    (w is not modified).  Returns (qweight, scales, zeros or None, row_loss)."""
+    d_in = w.shape[1] if d_in is None else d_in
+    h = gptq_hessian(x, d_in)
+    u, dead = gptq_factor(h, alpha)
+    return gptq_quantize(w.clone(), u, dead, group_size, mode, d_in)
 
 
 def _linear(fn_name, x, qweight, scales, zeros, bias, d_in, group_size, out_dtype, out):

@@ -113,6 +113,50 @@ int w4_pack(const float *w, int64_t d_out, int64_t d_in, int64_t ldw, int group_
     return err == hipSuccess ? W4_OK : hip_fail(err);
 }
 
+int w4_gptq_hessian(const uint16_t *x, int64_t N, int64_t d_in, int64_t ldx, float *h,
+                    void *stream) {
+    if (!x || !h) return W4_ERR_NULL;
+    if (N < 1 || d_in < 1 || ldx < d_in) return W4_ERR_SHAPE;
+    if (N > W4_MAX_DIM || d_in > W4_MAX_GPTQ_D_IN || ldx > W4_MAX_DIM) return W4_ERR_RANGE;
+    if (!aligned(x, 2) || !aligned(h, 4)) return W4_ERR_ALIGN;
+    const hipError_t err =
+        w4::launch_gptq_hessian(x, N, d_in, ldx, h, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? W4_OK : hip_fail(err);
+}
+
+int w4_gptq_factor(float *h, int64_t d_in, float alpha, float *u, float *work, uint8_t *dead,
+                   void *stream) {
+    if (!h || !u || !work || !dead) return W4_ERR_NULL;
+    if (d_in < 1) return W4_ERR_SHAPE;
+    if (d_in > W4_MAX_GPTQ_D_IN) return W4_ERR_RANGE;
+    if (!(alpha >= 0.0f) || !(alpha < 1e30f)) return W4_ERR_RANGE;
+    if (!aligned(h, 4) || !aligned(u, 4) || !aligned(work, 4)) return W4_ERR_ALIGN;
+    const hipError_t err =
+        w4::launch_gptq_factor(h, d_in, alpha, u, work, dead, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? W4_OK : hip_fail(err);
+}
+
+int w4_gptq_quantize(float *w, int64_t d_out, int64_t d_in, int64_t ldw, const float *u,
+                     const uint8_t *dead, int group_size, int mode, uint8_t *qweight,
+                     uint16_t *scales, uint16_t *zeros, float *work, float *row_loss,
+                     void *stream) {
+    if (!w || !u || !qweight || !scales || !work) return W4_ERR_NULL;
+    if (mode != W4_SYM && mode != W4_ASYM) return W4_ERR_UNSUPPORTED;
+    if ((mode == W4_ASYM) != (zeros != nullptr)) return W4_ERR_NULL;
+    if (int st = check_dims(d_out, d_in)) return st;
+    if (ldw < d_in) return W4_ERR_SHAPE;
+    if (d_in > W4_MAX_GPTQ_D_IN || ldw > W4_MAX_DIM) return W4_ERR_RANGE;
+    if (!valid_group(group_size)) return W4_ERR_GROUP;
+    if (!aligned(w, 4) || !aligned(u, 4) || !aligned(qweight, 4) || !aligned(scales, 2) ||
+        (zeros && !aligned(zeros, 2)) || !aligned(work, 4) || (row_loss && !aligned(row_loss, 4)))
+        return W4_ERR_ALIGN;
+    const Layout L = layout_of(d_in, group_size);
+    const hipError_t err = w4::launch_gptq_quantize(
+        w, d_out, d_in, ldw, u, dead, L.span, mode, qweight, scales, zeros, L.n_groups, L.k_pad,
+        work, row_loss, static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? W4_OK : hip_fail(err);
+}
+
 int w4_qat_repack(const uint16_t *w, int64_t d_out, int64_t d_in, int64_t ldw, uint8_t *qweight,
                   uint16_t *scales, uint8_t *m_out, void *stream) {
     if (!w || !qweight || !scales) return W4_ERR_NULL;

@@ -1,0 +1,350 @@
+// gptq.hip -- the GPTQ quantizer on the GPU, in fp32, producing the packed format of w4_pack.
+//
+// Page: [Lab5] "Lab 5: Gemma4 端到端推理优化", section "从 RTN 到 GPTQ": the layer objective
+// ||X W^T - X Q^T||_F^2 over calibration activations X [N][d_in]; its Hessian H = (2/N) X^T X;
+// dead columns (diag H = 0: their weights are set to zero and H_ii to 1); damping
+// H += alpha mean(diag H) I; H^-1 = U^T U with U upper triangular; columns quantized in order,
+// e_i = (w_i - q_i) / U_ii and W[:, i:] -= e_i U[i, i:]; the predicted loss
+// L_pred = 1/2 sum_i ||w_i - q_i||^2 / U_ii^2. The page builds H, factors it and propagates the
+// error in fp32; so does this file.
+//
+// Steps (each a plain kernel; the host sequences them):
+//   * hessian: H = (2/N) X^T X, 64 x 64 output tiles, the tokens staged through LDS in fp32;
+//   * factor: dead columns and damping; the reverse Cholesky H = V V^T (V upper triangular, from
+//     the last column back, one launch per column updating the leading block); U = V^-1 by
+//     back substitution (one launch per row of V, updating the rows above it); then
+//     U^T U = V^-T V^-1 = H^-1. The per-column launches keep every step race-free and simple; the
+//     factorization is an offline step (tens of milliseconds at d_in = 3584);
+//   * quantize: blocks of 32 columns. One thread per output row runs the block's columns in
+//     order (the group's scale and zero by w4_pack's rule from the current weights at the group's
+//     first column, the code, e_i, the updates inside the block, the row's loss), then a GEMM
+//     applies the block's errors to the columns after it: W[:, b+32:] -= E U[b:b+32, b+32:].
+#include "w4_device.h"
+#include "w4_launch.h"
+
+#include <algorithm>
+
+namespace w4 {
+
+namespace {
+
+constexpr int kGqTile = 64;
+constexpr int kGqBlock = 32;  // columns per quantization block
+
+// H[a][b] = (2/N) sum_n x[n][a] x[n][b]; 256 threads, 4 x 4 outputs each.
+__global__ void __launch_bounds__(256) gptq_hessian_kernel(const uint16_t *__restrict__ x,
+                                                           int N, int d_in, int64_t ldx,
+                                                           float scale, float *__restrict__ h) {
+    __shared__ float xa[16][kGqTile + 1], xb[16][kGqTile + 1];
+    const int a0 = blockIdx.y * kGqTile, b0 = blockIdx.x * kGqTile;
+    const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+    float acc[4][4] = {};
+    for (int n0 = 0; n0 < N; n0 += 16) {
+        for (int e = threadIdx.x; e < 16 * kGqTile; e += 256) {
+            const int r = e / kGqTile, c = e % kGqTile, n = n0 + r;
+            const int ca = a0 + c, cb = b0 + c;
+            xa[r][c] = n < N && ca < d_in ? bf16_to_f32(x[n * ldx + ca]) : 0.0f;
+            xb[r][c] = n < N && cb < d_in ? bf16_to_f32(x[n * ldx + cb]) : 0.0f;
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int r = 0; r < 16; ++r) {
+            float va[4], vb[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                va[i] = xa[r][ty + 16 * i];
+                vb[i] = xb[r][tx + 16 * i];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(va[i], vb[j], acc[i][j]);
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int a = a0 + ty + 16 * i, b = b0 + tx + 16 * j;
+            if (a < d_in && b < d_in) h[(int64_t)a * d_in + b] = scale * acc[i][j];
+        }
+}
+
+// Dead columns and damping, one block: dead[i] = (H_ii == 0); H_ii = 1 there; then
+// H_ii += alpha mean(diag H).
+__global__ void __launch_bounds__(1024) gptq_prepare_kernel(float *__restrict__ h, int n,
+                                                            float alpha,
+                                                            uint8_t *__restrict__ dead) {
+    __shared__ float part[1024];
+    float s = 0.0f;
+    for (int i = threadIdx.x; i < n; i += 1024) {
+        float d = h[(int64_t)i * n + i];
+        const bool z = d == 0.0f;
+        if (z) d = 1.0f;
+        dead[i] = z ? 1 : 0;
+        h[(int64_t)i * n + i] = d;
+        s += d;
+    }
+    part[threadIdx.x] = s;
+    __syncthreads();
+    for (int o = 512; o > 0; o >>= 1) {
+        if (threadIdx.x < o) part[threadIdx.x] += part[threadIdx.x + o];
+        __syncthreads();
+    }
+    const float lam = alpha * (part[0] / static_cast<float>(n));
+    for (int i = threadIdx.x; i < n; i += 1024) h[(int64_t)i * n + i] += lam;
+}
+
+// Reverse Cholesky step k, on the lower triangle of H (the only part updated): V[i][k] =
+// H[k][i] / sqrt(H[k][k]) for i <= k, and for j <= i < k H[i][j] -= H[k][i] H[k][j] / H[k][k].
+// Row k of H is read, never written, in this step.
+__global__ void __launch_bounds__(256) gptq_chol_step_kernel(float *__restrict__ h, int n, int k,
+                                                             float *__restrict__ v) {
+    const float hkk = h[(int64_t)k * n + k];
+    const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (e <= k) v[e * n + k] = h[(int64_t)k * n + e] / sqrtf(hkk);
+    // lower-triangle element e of the k x k block: row i, column j <= i
+    const int64_t total = static_cast<int64_t>(k) * (k + 1) / 2;
+    if (e >= total) return;
+    int i = static_cast<int>((sqrtf(8.0f * static_cast<float>(e) + 1.0f) - 1.0f) * 0.5f);
+    while (static_cast<int64_t>(i) * (i + 1) / 2 > e) --i;
+    while (static_cast<int64_t>(i + 1) * (i + 2) / 2 <= e) ++i;
+    const int j = static_cast<int>(e - static_cast<int64_t>(i) * (i + 1) / 2);
+    const float u = h[(int64_t)k * n + i] * (h[(int64_t)k * n + j] / hkk);
+    h[(int64_t)i * n + j] -= u;
+}
+
+// Back substitution step k of V U = I (U kept with row m scaled by V[m][m], i.e. R = diag(V) U):
+// for i < k and j >= k, R[i][j] -= V[i][k] R[k][j] / V[k][k]. Row k is read, never written.
+__global__ void __launch_bounds__(256) gptq_inv_step_kernel(const float *__restrict__ v, int n,
+                                                            int k, float *__restrict__ r) {
+    const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    const int cols = n - k;
+    if (e >= static_cast<int64_t>(k) * cols) return;
+    const int i = static_cast<int>(e / cols), j = k + static_cast<int>(e % cols);
+    const float f = v[(int64_t)i * n + k] / v[(int64_t)k * n + k];
+    r[(int64_t)i * n + j] -= f * r[(int64_t)k * n + j];
+}
+
+// R = I (upper part used), and the final U = diag(V)^-1 R (rows scaled), zeros below the diagonal.
+__global__ void __launch_bounds__(256) gptq_identity_kernel(float *__restrict__ r, int n) {
+    const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (e >= static_cast<int64_t>(n) * n) return;
+    r[e] = (e / n == e % n) ? 1.0f : 0.0f;
+}
+
+__global__ void __launch_bounds__(256) gptq_scale_rows_kernel(const float *__restrict__ v, int n,
+                                                              float *__restrict__ u) {
+    const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (e >= static_cast<int64_t>(n) * n) return;
+    const int i = static_cast<int>(e / n), j = static_cast<int>(e % n);
+    u[e] = j < i ? 0.0f : u[e] / v[(int64_t)i * n + i];
+}
+
+// w4_pack's statistics of one group of the current weights (pads are zeros of the group), and
+// the code of one value; the same fp32 operations as the packing kernel's rule.
+struct GroupQ {
+    float s, z;
+};
+
+__device__ GroupQ group_stats(const float *__restrict__ row, int k0, int g, int d_in, int mode) {
+    float amax = 0.0f, mx = 0.0f, mn = 0.0f;
+    for (int t = 0; t < g; ++t) {
+        const int k = k0 + t;
+        const float r = k < d_in ? row[k] : 0.0f;
+        const float a = fabsf(r);
+        if (t == 0) {
+            amax = a;
+            mx = r;
+            mn = r;
+        } else {
+            amax = a > amax ? a : amax;
+            mx = r > mx ? r : mx;
+            mn = r < mn ? r : mn;
+        }
+    }
+    GroupQ q;
+    if (mode == 0) {
+        q.s = bf16_to_f32(f32_to_bf16(amax / 7.0f + 0.0f));
+        q.z = 8.0f;
+    } else {
+        q.s = bf16_to_f32(f32_to_bf16((mx - mn) / 15.0f + 0.0f));
+        float zf = 0.0f;
+        if (q.s != 0.0f) zf = rintf(-mn / q.s) + 0.0f;
+        q.z = bf16_to_f32(f32_to_bf16(zf));
+    }
+    return q;
+}
+
+__device__ __forceinline__ float code_of(float r, GroupQ q) {
+    if (q.s == 0.0f) return q.z;
+    return fminf(fmaxf(rintf(r / q.s + q.z), 0.0f), 15.0f);
+}
+
+// One block of 32 columns, one thread per row: group statistics at group starts (from the
+// current row, read from memory), codes, the errors and the in-block updates; E[j][c] receives
+// e for the trailing update, the codes go to qweight (pads of the last group too).
+__global__ void __launch_bounds__(256) gptq_block_kernel(
+    float *__restrict__ w, int d_out, int d_in, int64_t ldw, const float *__restrict__ u, int n,
+    int b0, int g, int mode, uint8_t *__restrict__ qweight, int64_t row_bytes,
+    uint16_t *__restrict__ scales, uint16_t *__restrict__ zeros, int n_groups,
+    float *__restrict__ ebuf, float *__restrict__ row_loss) {
+    __shared__ float ub[kGqBlock][kGqBlock + 1];
+    const int cols = max(0, min(kGqBlock, d_in - b0));  // 0: a block of the last group's pads
+    for (int e = threadIdx.x; e < kGqBlock * kGqBlock; e += 256) {
+        const int i = e / kGqBlock, c = e % kGqBlock;
+        ub[i][c] = i < cols && c < cols ? u[(int64_t)(b0 + i) * n + b0 + c] : 0.0f;
+    }
+    __syncthreads();
+    const int j = blockIdx.x * 256 + threadIdx.x;
+    if (j >= d_out) return;
+    float *row = w + (int64_t)j * ldw;
+    float wv[kGqBlock];
+#pragma unroll
+    for (int c = 0; c < kGqBlock; ++c) wv[c] = c < cols ? row[b0 + c] : 0.0f;
+    GroupQ q{0.0f, 8.0f};
+    const int G0 = b0 / g;
+    if (b0 % g != 0) {  // the block continues a group: its statistics are stored
+        q.s = bf16_to_f32(scales[(int64_t)j * n_groups + G0]);
+        q.z = mode == 0 ? 8.0f : bf16_to_f32(zeros[(int64_t)j * n_groups + G0]);
+    }
+    float loss = 0.0f;
+    uint32_t packed[kGqBlock / 8] = {};
+#pragma unroll
+    for (int c = 0; c < kGqBlock; ++c) {
+        if (c < cols) {
+            const int k = b0 + c;
+            if (k % g == 0) {  // a group starts here: statistics of the current weights
+                // (the block's own columns are the up-to-date values in registers)
+#pragma unroll
+                for (int t = 0; t < kGqBlock; ++t)
+                    if (t >= c && t < cols) row[b0 + t] = wv[t];
+                q = group_stats(row, k, g, d_in, mode);
+                scales[(int64_t)j * n_groups + k / g] = static_cast<uint16_t>(f32_to_bf16(q.s));
+                if (mode != 0) zeros[(int64_t)j * n_groups + k / g] = static_cast<uint16_t>(f32_to_bf16(q.z));
+            }
+            const float code = code_of(wv[c], q);
+            const float qv = q.s * (code - q.z);
+            const float err = wv[c] - qv;
+            const float d = ub[c][c];
+            loss += 0.5f * (err * err) / (d * d);
+            const float e = err / d;
+            ebuf[(int64_t)j * kGqBlock + c] = e;
+#pragma unroll
+            for (int t = 0; t < kGqBlock; ++t)
+                if (t > c) wv[t] -= e * ub[c][t];
+            wv[c] = qv;
+            packed[c / 8] |= static_cast<uint32_t>(code) << (4 * (c % 8));
+        } else {
+            ebuf[(int64_t)j * kGqBlock + c] = 0.0f;
+            packed[c / 8] |= static_cast<uint32_t>(code_of(0.0f, q)) << (4 * (c % 8));
+        }
+    }
+#pragma unroll
+    for (int c = 0; c < kGqBlock / 8; ++c)
+        *reinterpret_cast<uint32_t *>(qweight + (int64_t)j * row_bytes + b0 / 2 + 4 * c) = packed[c];
+    if (row_loss) row_loss[j] = (b0 == 0 ? 0.0f : row_loss[j]) + loss;
+}
+
+// Trailing update: W[:, c0:] -= E U[b0:b0+32, c0:], 64 x 64 tiles of W (rows x columns).
+__global__ void __launch_bounds__(256) gptq_trail_kernel(float *__restrict__ w, int d_out,
+                                                         int d_in, int64_t ldw,
+                                                         const float *__restrict__ u, int n,
+                                                         int b0, const float *__restrict__ ebuf) {
+    __shared__ float es[kGqTile][kGqBlock + 1], us[kGqBlock][kGqTile + 1];
+    const int c0 = b0 + kGqBlock + blockIdx.x * kGqTile, r0 = blockIdx.y * kGqTile;
+    for (int e = threadIdx.x; e < kGqTile * kGqBlock; e += 256) {
+        const int r = e / kGqBlock, c = e % kGqBlock;
+        es[r][c] = r0 + r < d_out ? ebuf[(int64_t)(r0 + r) * kGqBlock + c] : 0.0f;
+        const int i = e / kGqTile, cc = e % kGqTile;
+        us[i][cc] = c0 + cc < d_in && b0 + i < d_in ? u[(int64_t)(b0 + i) * n + c0 + cc] : 0.0f;
+    }
+    __syncthreads();
+    const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+    float acc[4][4] = {};
+#pragma unroll 8
+    for (int i = 0; i < kGqBlock; ++i) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) acc[a][b] = fmaf(es[ty + 16 * a][i], us[i][tx + 16 * b], acc[a][b]);
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int r = r0 + ty + 16 * a, c = c0 + tx + 16 * b;
+            if (r < d_out && c < d_in) w[(int64_t)r * ldw + c] -= acc[a][b];
+        }
+}
+
+__global__ void __launch_bounds__(256) gptq_dead_kernel(float *__restrict__ w, int d_out, int d_in,
+                                                        int64_t ldw,
+                                                        const uint8_t *__restrict__ dead) {
+    const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (e >= static_cast<int64_t>(d_out) * d_in) return;
+    const int c = static_cast<int>(e % d_in);
+    if (dead[c]) w[(e / d_in) * ldw + c] = 0.0f;
+}
+
+unsigned blocks_for(int64_t n) { return static_cast<unsigned>((n + 255) / 256); }
+
+}  // namespace
+
+hipError_t launch_gptq_hessian(const uint16_t *x, int64_t N, int64_t d_in, int64_t ldx, float *h,
+                               hipStream_t stream) {
+    const unsigned t = static_cast<unsigned>((d_in + kGqTile - 1) / kGqTile);
+    hipLaunchKernelGGL(gptq_hessian_kernel, dim3(t, t), dim3(256), 0, stream, x,
+                       static_cast<int>(N), static_cast<int>(d_in), ldx,
+                       2.0f / static_cast<float>(N), h);
+    return hipGetLastError();
+}
+
+hipError_t launch_gptq_factor(float *h, int64_t d_in, float alpha, float *u, float *v,
+                              uint8_t *dead, hipStream_t stream) {
+    const int n = static_cast<int>(d_in);
+    hipLaunchKernelGGL(gptq_prepare_kernel, dim3(1), dim3(1024), 0, stream, h, n, alpha, dead);
+    for (int k = n - 1; k >= 0; --k) {
+        const int64_t work = std::max<int64_t>(static_cast<int64_t>(k) * (k + 1) / 2, k + 1);
+        hipLaunchKernelGGL(gptq_chol_step_kernel, dim3(blocks_for(work)), dim3(256), 0, stream,
+                           h, n, k, v);
+    }
+    hipLaunchKernelGGL(gptq_identity_kernel, dim3(blocks_for((int64_t)n * n)), dim3(256), 0,
+                       stream, u, n);
+    for (int k = n - 1; k >= 1; --k) {
+        const int64_t work = static_cast<int64_t>(k) * (n - k);
+        hipLaunchKernelGGL(gptq_inv_step_kernel, dim3(blocks_for(work)), dim3(256), 0, stream, v,
+                           n, k, u);
+    }
+    hipLaunchKernelGGL(gptq_scale_rows_kernel, dim3(blocks_for((int64_t)n * n)), dim3(256), 0,
+                       stream, v, n, u);
+    return hipGetLastError();
+}
+
+hipError_t launch_gptq_quantize(float *w, int64_t d_out, int64_t d_in, int64_t ldw,
+                                const float *u, const uint8_t *dead, int64_t span, int mode,
+                                uint8_t *qweight, uint16_t *scales, uint16_t *zeros,
+                                int64_t n_groups, int64_t k_pad, float *ebuf, float *row_loss,
+                                hipStream_t stream) {
+    const int n = static_cast<int>(d_in);
+    if (dead)
+        hipLaunchKernelGGL(gptq_dead_kernel, dim3(blocks_for(d_out * d_in)), dim3(256), 0, stream,
+                           w, static_cast<int>(d_out), n, ldw, dead);
+    for (int b0 = 0; b0 < k_pad; b0 += kGqBlock) {  // (blocks past d_in write pad codes)
+        hipLaunchKernelGGL(gptq_block_kernel, dim3(blocks_for(d_out)), dim3(256), 0, stream, w,
+                           static_cast<int>(d_out), n, ldw, u, n, b0, static_cast<int>(span), mode,
+                           qweight, k_pad / 2, scales, zeros, static_cast<int>(n_groups), ebuf,
+                           row_loss);
+        const int rest = n - b0 - kGqBlock;
+        if (rest > 0)
+            hipLaunchKernelGGL(gptq_trail_kernel,
+                               dim3(static_cast<unsigned>((rest + kGqTile - 1) / kGqTile),
+                                    static_cast<unsigned>((d_out + kGqTile - 1) / kGqTile)),
+                               dim3(256), 0, stream, w, static_cast<int>(d_out), n, ldw, u, n, b0,
+                               ebuf);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace w4

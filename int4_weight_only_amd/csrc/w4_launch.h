@@ -32,6 +32,17 @@ hipError_t launch_w4a8_linear(const uint16_t *x, int64_t M, int64_t ldx, const u
                               int64_t d_in, int64_t k_pad, void *y, int64_t ldy, bool out_f32,
                               float *s_x, int32_t *acc, hipStream_t stream);
 
+// GPTQ (gptq.hip): Hessian, factorization of its damped inverse, column loop.
+hipError_t launch_gptq_hessian(const uint16_t *x, int64_t N, int64_t d_in, int64_t ldx, float *h,
+                               hipStream_t stream);
+hipError_t launch_gptq_factor(float *h, int64_t d_in, float alpha, float *u, float *v,
+                              uint8_t *dead, hipStream_t stream);
+hipError_t launch_gptq_quantize(float *w, int64_t d_out, int64_t d_in, int64_t ldw,
+                                const float *u, const uint8_t *dead, int64_t span, int mode,
+                                uint8_t *qweight, uint16_t *scales, uint16_t *zeros,
+                                int64_t n_groups, int64_t k_pad, float *ebuf, float *row_loss,
+                                hipStream_t stream);
+
 // Repack of bf16 weights on the 4-bit grid into the g32 symmetric format (qat_repack.hip).
 bool qat_repack_supported(int64_t d_out, int64_t n_groups);
 hipError_t launch_qat_repack(const uint16_t *w, int64_t d_out, int64_t d_in, int64_t ldw,

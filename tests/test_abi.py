@@ -32,6 +32,9 @@ def lib():
                                    ctypes.POINTER(ctypes.c_size_t)]
     L.w4_pack.argtypes = [p, i64, i64, i64, i32, i32, p, p, p, p]
     L.w4_qat_repack.argtypes = [p, i64, i64, i64, p, p, p, p]
+    L.w4_gptq_hessian.argtypes = [p, i64, i64, i64, p, p]
+    L.w4_gptq_factor.argtypes = [p, i64, ctypes.c_float, p, p, p, p]
+    L.w4_gptq_quantize.argtypes = [p, i64, i64, i64, p, p, i32, i32, p, p, p, p, p, p]
     lin = [p, i64, i64, p, p, p, p, i64, i64, i32, p, i64, i32]
     L.w4_gemv.argtypes = lin + [p]
     L.w4_gemv_glu.argtypes = lin + [p]
@@ -48,7 +51,8 @@ def lib():
 def test_header_declares_the_five_entry_points():
     names = declared_functions()
     for n in ("w4_pack", "w4_gemv", "w4_gemv_glu", "w4_gemm", "act_quant_int8", "w4a8_gemv",
-              "w4a8_gemm", "w4a8_linear", "w4_qat_repack",
+              "w4a8_gemm", "w4a8_linear", "w4_qat_repack", "w4_gptq_hessian", "w4_gptq_factor",
+              "w4_gptq_quantize",
               "w4_packed_layout", "w4_status_string",
               "w4_last_hip_error"):
         assert n in names
@@ -181,6 +185,44 @@ def test_w4a8_rejects_bad_arguments(lib):
     assert call(acc=E + 2) == W4_ERR_ALIGN
     big = (1 << 20) + 16
     assert call(d_in=big, ldq=big) == W4_ERR_RANGE
+
+
+def test_gptq_rejects_bad_arguments(lib):
+    h = lib.w4_gptq_hessian
+    assert h(None, 8, 64, 64, B, None) == W4_ERR_NULL
+    assert h(A, 8, 64, 64, None, None) == W4_ERR_NULL
+    assert h(A, 0, 64, 64, B, None) == W4_ERR_SHAPE
+    assert h(A, 8, 64, 32, B, None) == W4_ERR_SHAPE
+    assert h(A + 1, 8, 64, 64, B, None) == W4_ERR_ALIGN
+    assert h(A, 8, 8193, 8200, B, None) == W4_ERR_RANGE
+    f = lib.w4_gptq_factor
+    assert f(None, 64, 0.01, B, C, D, None) == W4_ERR_NULL
+    assert f(A, 64, 0.01, B, C, None, None) == W4_ERR_NULL
+    assert f(A, 0, 0.01, B, C, D, None) == W4_ERR_SHAPE
+    assert f(A, 8193, 0.01, B, C, D, None) == W4_ERR_RANGE
+    assert f(A, 64, -1.0, B, C, D, None) == W4_ERR_RANGE
+    assert f(A, 64, float("nan"), B, C, D, None) == W4_ERR_RANGE
+    assert f(A + 2, 64, 0.01, B, C, D, None) == W4_ERR_ALIGN
+    q = lib.w4_gptq_quantize
+
+    def call(**kw):
+        a = dict(w=A, d_out=16, d_in=64, ldw=64, u=B, dead=None, g=32, mode=0, qw=C, sc=D, zr=None,
+                 work=E, loss=None)
+        a.update(kw)
+        return q(a["w"], a["d_out"], a["d_in"], a["ldw"], a["u"], a["dead"], a["g"], a["mode"],
+                 a["qw"], a["sc"], a["zr"], a["work"], a["loss"], None)
+
+    assert call(w=None) == W4_ERR_NULL
+    assert call(work=None) == W4_ERR_NULL
+    assert call(mode=1) == W4_ERR_NULL  # asymmetric without zeros
+    assert call(zr=E) == W4_ERR_NULL    # symmetric with zeros
+    assert call(mode=2) == W4_ERR_UNSUPPORTED
+    assert call(d_out=0) == W4_ERR_SHAPE
+    assert call(ldw=32) == W4_ERR_SHAPE
+    assert call(g=48) == W4_ERR_GROUP
+    assert call(d_in=8193, ldw=8193) == W4_ERR_RANGE
+    assert call(w=A + 2) == W4_ERR_ALIGN
+    assert call(loss=E + 2) == W4_ERR_ALIGN
 
 
 def test_qat_repack_rejects_bad_arguments(lib):

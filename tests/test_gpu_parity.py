@@ -117,6 +117,131 @@ def test_pack_configs_full_size():
 
 
 # ------------------------------------------------------------------------------------------
+# GPTQ (fp32 on the GPU) against O9 (fp64): the Hessian elementwise, the factor by its identity
+# and elementwise, the column loop by its codes, its loss identity and the layer objective
+# ------------------------------------------------------------------------------------------
+import oracle.gptq as gq  # noqa: E402
+
+
+def _gptq_calib(seed, N, d_in, dead=()):
+    """bf16 calibration activations with correlated channels (latent factors plus noise), the
+    listed columns zero in every row (the tests' own generator)."""
+    rng = np.random.default_rng(seed)
+    lat = rng.normal(size=(N, max(1, d_in // 4)))
+    x = lat @ (rng.normal(size=(lat.shape[1], d_in)) / 2.0) + 0.3 * rng.normal(size=(N, d_in))
+    x[:, list(dead)] = 0.0
+    return workloads.to_bf16_bits(x.astype(np.float32))
+
+
+def _deq(codes, sc_bits, zr_bits, d_in, span):
+    G = np.arange(d_in) // span
+    s = oracle.bf16_to_f32(sc_bits)[:, G].astype(np.float64)
+    z = oracle.bf16_to_f32(zr_bits)[:, G].astype(np.float64) if zr_bits is not None else 8.0
+    return s * (codes[:, :d_in].astype(np.float64) - z)
+
+
+@pytest.mark.parametrize("N,d_in", [(1, 1), (37, 100), (256, 300), (2048, 3584)])
+def test_gptq_hessian(N, d_in):
+    _announce("gptq_hessian", N, d_in)
+    xb = _gptq_calib(70 + N, N, d_in)
+    ldx = d_in + 8 - d_in % 8 if d_in % 8 else d_in + 8
+    xp = np.full((N, ldx), 0x7FC0, dtype=np.uint16)  # NaN past d_in: never read
+    xp[:, :d_in] = xb
+    h = host(w4.gptq_hessian(dev_bf16(xp), d_in))
+    ref = gq.hessian(xb)
+    x = np.abs(oracle.bf16_to_f32(xb).astype(np.float64))
+    bound = 2.0 / N * (x.T @ x) * 1e-5 + 1e-30
+    assert np.all(np.abs(h - ref) <= bound)
+
+
+@pytest.mark.parametrize("d_in,dead", [(1, ()), (64, (3,)), (300, (0, 299)), (1024, (7, 500))])
+def test_gptq_factor(d_in, dead):
+    """U from the GPU factorization against O9's (fp64 inverse and Cholesky of the same damped
+    matrix), and the identity U^T U (H + lambda I) = I."""
+    _announce("gptq_factor", d_in, dead)
+    N = 2 * d_in + 8
+    xb = _gptq_calib(71 + d_in, N, d_in, dead)
+    href = gq.hessian(xb)
+    hd, _, lam, dref = gq.prepare(href, np.zeros((1, d_in)), 0.01)
+    uref = gq.inverse_factor(hd)
+    h = torch.from_numpy(href.astype(np.float32)).cuda()
+    u, deadg = w4.gptq_factor(h, 0.01)
+    torch.cuda.synchronize()
+    u = host(u).astype(np.float64)
+    assert np.array_equal(host(deadg).astype(bool), dref)
+    assert np.all(np.tril(u, -1) == 0.0)
+    assert np.max(np.abs(u - uref)) <= 2e-3 * np.max(np.abs(uref))
+    eye = u.T @ u @ hd
+    assert np.max(np.abs(eye - np.eye(d_in))) <= 2e-3
+
+
+@pytest.mark.parametrize("g,mode", [(32, SYM), (128, ASYM), (0, SYM), (64, ASYM)])
+def test_gptq_quantize_against_oracle(g, mode):
+    """The column loop on the oracle's U: codes as O9's except where fp32 and fp64 error
+    propagation round a value apart (at most 2%), the loss identity of the GPU's own result,
+    and the layer objective within 1% of O9's."""
+    d_out, d_in, N = 256, 1000, 512
+    _announce("gptq_quantize", d_out, d_in, g, mode)
+    w = workloads.weight(72, g + mode, d_out, d_in)
+    xb = _gptq_calib(72 + g, N, d_in, dead=(17,))
+    r = gq.gptq(w, xb, g, mode)
+    u = torch.from_numpy(np.ascontiguousarray(r["U"], dtype=np.float32)).cuda()
+    dead = torch.from_numpy(r["dead"].astype(np.uint8)).cuda()
+    qw, sc, zr, row_loss = w4.gptq_quantize(torch.from_numpy(w.copy()).cuda(), u, dead, g, mode)
+    torch.cuda.synchronize()
+    qw, sc = host(qw), host_bits(sc)
+    zr = host_bits(zr) if zr is not None else None
+    codes = oracle.unpack(qw)
+    kp = oracle.k_pad(d_in, g)
+    span = kp // oracle.n_groups(d_in, g)
+    assert np.mean(codes[:, :d_in] == r["codes"][:, :d_in]) >= 0.98
+    x = oracle.bf16_to_f32(xb).astype(np.float64)
+    w0 = r["w"]
+    q = _deq(codes, sc, zr, d_in, span)
+    assert np.all(q[:, 17] == 0.0)  # the dead column
+    qp = _deq(codes, sc, zr, kp, span)  # pads decode to 0
+    assert np.all(qp[:, d_in:] == 0.0)
+    d = w0 - q
+    obj = np.sum((x @ d.T) ** 2) / N + 0.5 * r["lam"] * np.sum(d * d)
+    assert float(np.sum(host(row_loss).astype(np.float64))) == pytest.approx(obj, rel=2e-3)
+    d_ref = w0 - _deq(r["codes"], r["scales"], r["zeros"], d_in, span)
+    e_gpu, e_ref = np.sum((x @ d.T) ** 2), np.sum((x @ d_ref.T) ** 2)
+    assert abs(e_gpu - e_ref) <= 0.01 * e_ref
+    # every code decodes within the grid of its group's stored scale and zero
+    assert codes.max() <= 15
+
+
+def test_gptq_end_to_end_c4_qkv():
+    """The whole path on the GPU at the C4 q/k/v shape (4608 x 3584, g32 SYM, 2048 calibration
+    tokens): GPTQ's layer objective is below RTN's, and its loss identity holds."""
+    cfg = workloads.C4
+    lin = cfg.linears[0]
+    _announce("gptq end to end", lin.d_out, lin.d_in)
+    w = workloads.linear_weight(cfg, 0)
+    xb = _gptq_calib(73, 2048, lin.d_in)
+    wd = torch.from_numpy(w).cuda()
+    qw, sc, _, row_loss = w4.gptq(wd, dev_bf16(xb), 32, SYM)
+    qr, sr, _ = w4.w4_pack(wd, 32, SYM)
+    torch.cuda.synchronize()
+    x = torch.from_numpy(oracle.bf16_to_f32(xb)).cuda().double()
+    wt = wd.double()
+
+    def deq(qwt, sct):
+        c = oracle.unpack(host(qwt))[:, :lin.d_in].astype(np.float64)
+        s = np.repeat(oracle.bf16_to_f32(host_bits(sct)).astype(np.float64), 32, axis=1)
+        return torch.from_numpy(s[:, :lin.d_in] * (c - 8.0)).cuda()
+
+    d_g, d_r = wt - deq(qw, sc), wt - deq(qr, sr)
+    e_g = float(((x @ d_g.T) ** 2).sum())
+    e_r = float(((x @ d_r.T) ** 2).sum())
+    assert e_g < 0.8 * e_r, (e_g, e_r)
+    diag = 2.0 / 2048 * (x * x).sum(dim=0)
+    lam = 0.01 * float(diag.mean())
+    obj = e_g / 2048 + 0.5 * lam * float((d_g * d_g).sum())
+    assert float(row_loss.double().sum()) == pytest.approx(obj, rel=5e-3)
+
+
+# ------------------------------------------------------------------------------------------
 # w4_qat_repack
 # ------------------------------------------------------------------------------------------
 def check_qat(w_bits, d_in, what):
