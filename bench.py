@@ -354,6 +354,43 @@ def bench_qat(torch, w4, workloads, iters):
                 groups_on_grid=round(on_grid, 4))
 
 
+def bench_gptq(torch, w4, workloads, iters):
+    """GPTQ on the C4 q/k/v shape (4608 x 3584, g32 symmetric) with 2048 calibration tokens:
+    the three calls timed separately (HIP events). Inputs are generated on the GPU with a seeded
+    torch generator: N(0, 0.02^2) weights, activations with correlated channels (timing only;
+    parity of the path is in the GPU tests)."""
+    lin = workloads.C4.linears[0]
+    dev = torch.device("cuda", 0)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(workloads.C4.seed)
+    N = 2048
+    w = torch.randn((lin.d_out, lin.d_in), generator=gen, device=dev) * 0.02
+    lat = torch.randn((N, lin.d_in // 4), generator=gen, device=dev)
+    mix = torch.randn((lin.d_in // 4, lin.d_in), generator=gen, device=dev) / 2
+    x = (lat @ mix + 0.3 * torch.randn((N, lin.d_in), generator=gen, device=dev))
+    x = x.to(torch.bfloat16).contiguous()
+    del lat, mix
+    timer = Timer(torch)
+    for it in range(iters + 1):
+        key = "warm" if it == 0 else ""
+        timer.start("h" + key)
+        h = w4.gptq_hessian(x, lin.d_in)
+        timer.stop("h" + key)
+        timer.start("f" + key)
+        u, dead = w4.gptq_factor(h, 0.01)
+        timer.stop("f" + key)
+        wc = w.clone()
+        timer.start("q" + key)
+        w4.gptq_quantize(wc, u, dead, 32, w4.W4_SYM)
+        timer.stop("q" + key)
+    torch.cuda.synchronize()
+    h_ms, f_ms, q_ms = timer.mean_ms("h"), timer.mean_ms("f"), timer.mean_ms("q")
+    flop_h = 2.0 * N * lin.d_in * lin.d_in
+    return dict(shape=f"{lin.d_out}x{lin.d_in}", calib_tokens=N, hessian_ms=round(h_ms, 3),
+                hessian_tflops=round(flop_h / h_ms / 1e9, 1), factor_ms=round(f_ms, 3),
+                quantize_ms=round(q_ms, 3), total_ms=round(h_ms + f_ms + q_ms, 3))
+
+
 def bench_c3(torch, w4, workloads, iters):
     """28 layers x {qkv, o, gate/up, down}, asymmetric g128, weights generated on the GPU with a
     seeded torch generator (timing only; parity of these shapes is in the GPU tests)."""
@@ -425,7 +462,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
-    ap.add_argument("--only", choices=["c2", "c3", "c4", "c5", "qat"], default=None,
+    ap.add_argument("--only", choices=["c2", "c3", "c4", "c5", "qat", "gptq"], default=None,
                     help="time one workload only (for profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -455,6 +492,8 @@ def main():
             secondary["C5_w4a8"] = bench_c5(torch, w4, workloads, 100)
         elif args.only == "qat":
             secondary["qat_repack"] = bench_qat(torch, w4, workloads, 10)
+        elif args.only == "gptq":
+            secondary["gptq"] = bench_gptq(torch, w4, workloads, 3)
         if args.only != "c2":
             print(json.dumps(secondary), flush=True)
             return
@@ -467,6 +506,8 @@ def main():
         secondary["C3_decoder_step"] = bench_c3(torch, w4, workloads, 5)
         log("QAT repack")
         secondary["qat_repack"] = bench_qat(torch, w4, workloads, 10)
+        log("GPTQ")
+        secondary["gptq"] = bench_gptq(torch, w4, workloads, 3)
 
     secondary["C2_gate_up_silu_mul"] = dict(
         us=round(r["glu_ms"] * 1e3, 3), gbs=round(r["b_glu"] / r["glu_ms"] / 1e6, 1),
