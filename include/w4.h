@@ -108,7 +108,8 @@ int w4_pack(const float *w, int64_t d_out, int64_t d_in, int64_t ldw, int group_
  *
  * w4_gptq_factor -- dead columns, damping, and U with (H + lambda I)^-1 = U^T U.
  *   h     fp32 [d_in][d_in], in: the Hessian; destroyed (its lower triangle is worked in place)
- *   alpha the damping factor (the reference uses 0.01), >= 0
+ *   alpha the damping factor (the reference uses 0.01), >= 0; with alpha = 0 the Hessian must be
+ *         positive definite (N >= d_in calibration rows in general position), else U holds NaN
  *   u     fp32 [d_in][d_in], out: U (zeros below the diagonal)
  *   work  fp32 [d_in][d_in], scratch (the reverse Cholesky factor V, H = V V^T, U = V^-1)
  *   dead  uint8 [d_in], out: 1 for dead columns
