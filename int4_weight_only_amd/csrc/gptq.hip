@@ -10,11 +10,12 @@
 //
 // Steps (each a plain kernel; the host sequences them):
 //   * hessian: H = (2/N) X^T X, 64 x 64 output tiles, the tokens staged through LDS in fp32;
-//   * factor: dead columns and damping; the reverse Cholesky H = V V^T (V upper triangular, from
-//     the last column back, one launch per column updating the leading block); U = V^-1 by
-//     back substitution (one launch per row of V, updating the rows above it); then
-//     U^T U = V^-T V^-1 = H^-1. The per-column launches keep every step race-free and simple; the
-//     factorization is an offline step (tens of milliseconds at d_in = 3584);
+//   * factor: dead columns and damping; the reverse Cholesky H = V V^T (V upper triangular),
+//     then U = V^-1 by back substitution, so that U^T U = V^-T V^-1 = H^-1. Both run by panels of
+//     64 columns from the last panel back: the panel's diagonal block in LDS (one workgroup), a
+//     triangular solve for the rows above it (one thread per row) and a GEMM update of the
+//     leading block (the Cholesky), or the substitution inside the panel (one thread per column)
+//     and a GEMM for the rows above it (the inverse);
 //   * quantize: blocks of 32 columns. One thread per output row runs the block's columns in
 //     order (the group's scale and zero by w4_pack's rule from the current weights at the group's
 //     first column, the code, e_i, the updates inside the block, the row's loss), then a GEMM
@@ -96,35 +97,167 @@ __global__ void __launch_bounds__(1024) gptq_prepare_kernel(float *__restrict__ 
     for (int i = threadIdx.x; i < n; i += 1024) h[(int64_t)i * n + i] += lam;
 }
 
-// Reverse Cholesky step k, on the lower triangle of H (the only part updated): V[i][k] =
-// H[k][i] / sqrt(H[k][k]) for i <= k, and for j <= i < k H[i][j] -= H[k][i] H[k][j] / H[k][k].
-// Row k of H is read, never written, in this step.
-__global__ void __launch_bounds__(256) gptq_chol_step_kernel(float *__restrict__ h, int n, int k,
+// ---- blocked factorization: panels of kGqPanel columns, from the last panel back ----
+constexpr int kGqPanel = 64;
+
+// Reverse Cholesky of the panel's diagonal block (its lower triangle, already updated by every
+// later panel) in LDS: V[P][P] (upper), one workgroup.
+__global__ void __launch_bounds__(256) gptq_chol_diag_kernel(const float *__restrict__ h, int n,
+                                                             int p0, int nb,
                                                              float *__restrict__ v) {
-    const float hkk = h[(int64_t)k * n + k];
-    const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    if (e <= k) v[e * n + k] = h[(int64_t)k * n + e] / sqrtf(hkk);
-    // lower-triangle element e of the k x k block: row i, column j <= i
-    const int64_t total = static_cast<int64_t>(k) * (k + 1) / 2;
-    if (e >= total) return;
-    int i = static_cast<int>((sqrtf(8.0f * static_cast<float>(e) + 1.0f) - 1.0f) * 0.5f);
-    while (static_cast<int64_t>(i) * (i + 1) / 2 > e) --i;
-    while (static_cast<int64_t>(i + 1) * (i + 2) / 2 <= e) ++i;
-    const int j = static_cast<int>(e - static_cast<int64_t>(i) * (i + 1) / 2);
-    const float u = h[(int64_t)k * n + i] * (h[(int64_t)k * n + j] / hkk);
-    h[(int64_t)i * n + j] -= u;
+    __shared__ float a[kGqPanel][kGqPanel + 1];
+    for (int e = threadIdx.x; e < kGqPanel * kGqPanel; e += 256) {
+        const int i = e / kGqPanel, j = e % kGqPanel;
+        a[i][j] = i < nb && j <= i ? h[(int64_t)(p0 + i) * n + p0 + j] : 0.0f;
+    }
+    __syncthreads();
+    for (int k = nb - 1; k >= 0; --k) {
+        const float d = a[k][k];
+        const float rs = 1.0f / sqrtf(d);
+        // column k of V: V[i][k] = a[k][i] / sqrt(d), i <= k (a[k][k] / sqrt(d) = sqrt(d))
+        for (int i = threadIdx.x; i <= k; i += 256)
+            v[(int64_t)(p0 + i) * n + p0 + k] = a[k][i] * rs;
+        // the leading k x k block: a[i][j] -= a[k][i] a[k][j] / d, j <= i < k
+        const int tot = k * (k + 1) / 2;
+        float upd[8];
+        int idx[8];
+        int cnt = 0;
+        for (int e = threadIdx.x; e < tot; e += 256) {
+            int i = static_cast<int>((sqrtf(8.0f * static_cast<float>(e) + 1.0f) - 1.0f) * 0.5f);
+            while (i * (i + 1) / 2 > e) --i;
+            while ((i + 1) * (i + 2) / 2 <= e) ++i;
+            const int j = e - i * (i + 1) / 2;
+            upd[cnt] = a[k][i] * (a[k][j] / d);
+            idx[cnt] = i * (kGqPanel + 1) + j;
+            ++cnt;
+        }
+        __syncthreads();  // every read of row k and of the block is done before the writes
+        for (int c = 0; c < cnt; ++c) (&a[0][0])[idx[c]] -= upd[c];
+        __syncthreads();
+    }
 }
 
-// Back substitution step k of V U = I (U kept with row m scaled by V[m][m], i.e. R = diag(V) U):
-// for i < k and j >= k, R[i][j] -= V[i][k] R[k][j] / V[k][k]. Row k is read, never written.
-__global__ void __launch_bounds__(256) gptq_inv_step_kernel(const float *__restrict__ v, int n,
-                                                            int k, float *__restrict__ r) {
-    const int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-    const int cols = n - k;
-    if (e >= static_cast<int64_t>(k) * cols) return;
-    const int i = static_cast<int>(e / cols), j = k + static_cast<int>(e % cols);
-    const float f = v[(int64_t)i * n + k] / v[(int64_t)k * n + k];
-    r[(int64_t)i * n + j] -= f * r[(int64_t)k * n + j];
+// V[i][P] for the rows above the panel: h'[j] = H[p0 + j][i] (updated by the later panels)
+// = sum_{m >= j} V[i][p0 + m] V[p0 + j][p0 + m], solved from the last j back; one thread a row.
+__global__ void __launch_bounds__(256) gptq_chol_trsm_kernel(const float *__restrict__ h, int n,
+                                                             int p0, int nb,
+                                                             float *__restrict__ v) {
+    __shared__ float vp[kGqPanel][kGqPanel + 1];
+    for (int e = threadIdx.x; e < kGqPanel * kGqPanel; e += 256) {
+        const int j = e / kGqPanel, m = e % kGqPanel;
+        vp[j][m] = j < nb && m < nb && m >= j ? v[(int64_t)(p0 + j) * n + p0 + m] : 0.0f;
+    }
+    __syncthreads();
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i >= p0) return;
+    float x[kGqPanel];
+#pragma unroll
+    for (int j = 0; j < kGqPanel; ++j) x[j] = j < nb ? h[(int64_t)(p0 + j) * n + i] : 0.0f;
+#pragma unroll
+    for (int j = kGqPanel - 1; j >= 0; --j) {
+        if (j < nb) {
+            float t = x[j];
+#pragma unroll
+            for (int m = j + 1; m < kGqPanel; ++m) t -= x[m] * vp[j][m];
+            x[j] = t / vp[j][j];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < kGqPanel; ++j)
+        if (j < nb) v[(int64_t)i * n + p0 + j] = x[j];
+}
+
+// H[i][j] -= sum_m V[i][p0 + m] V[j][p0 + m] on the lower-triangle 64 x 64 tiles of [0, p0)^2.
+__global__ void __launch_bounds__(256) gptq_chol_syrk_kernel(float *__restrict__ h, int n, int p0,
+                                                             int nb,
+                                                             const float *__restrict__ v) {
+    __shared__ float vi[kGqPanel][kGqPanel + 1], vj[kGqPanel][kGqPanel + 1];
+    const int e = blockIdx.x;
+    int ti = static_cast<int>((sqrtf(8.0f * static_cast<float>(e) + 1.0f) - 1.0f) * 0.5f);
+    while (ti * (ti + 1) / 2 > e) --ti;
+    while ((ti + 1) * (ti + 2) / 2 <= e) ++ti;
+    const int tj = e - ti * (ti + 1) / 2;
+    const int r0 = ti * kGqTile, c0 = tj * kGqTile;
+    for (int q = threadIdx.x; q < kGqTile * kGqPanel; q += 256) {
+        const int r = q / kGqPanel, m = q % kGqPanel;
+        vi[r][m] = m < nb ? v[(int64_t)(r0 + r) * n + p0 + m] : 0.0f;
+        vj[r][m] = m < nb ? v[(int64_t)(c0 + r) * n + p0 + m] : 0.0f;
+    }
+    __syncthreads();
+    const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+    float acc[4][4] = {};
+#pragma unroll 8
+    for (int m = 0; m < kGqPanel; ++m) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) acc[a][b] = fmaf(vi[ty + 16 * a][m], vj[tx + 16 * b][m], acc[a][b]);
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) h[(int64_t)(r0 + ty + 16 * a) * n + c0 + tx + 16 * b] -= acc[a][b];
+}
+
+// Back substitution inside the panel, one thread per column j >= p0: for k from the panel's last
+// row back, R[i][j] -= V[i][k] / V[k][k] R[k][j] for the panel's rows i < k.
+__global__ void __launch_bounds__(256) gptq_inv_panel_kernel(const float *__restrict__ v, int n,
+                                                             int p0, int nb,
+                                                             float *__restrict__ r) {
+    __shared__ float f[kGqPanel][kGqPanel + 1];  // f[i][k] = V[p0 + i][p0 + k] / V[p0 + k][p0 + k]
+    for (int e = threadIdx.x; e < kGqPanel * kGqPanel; e += 256) {
+        const int i = e / kGqPanel, k = e % kGqPanel;
+        f[i][k] = i < nb && k < nb && i < k
+                      ? v[(int64_t)(p0 + i) * n + p0 + k] / v[(int64_t)(p0 + k) * n + p0 + k]
+                      : 0.0f;
+    }
+    __syncthreads();
+    const int j = p0 + blockIdx.x * 256 + threadIdx.x;
+    if (j >= n) return;
+    float x[kGqPanel];
+#pragma unroll
+    for (int i = 0; i < kGqPanel; ++i) x[i] = i < nb ? r[(int64_t)(p0 + i) * n + j] : 0.0f;
+#pragma unroll
+    for (int k = kGqPanel - 1; k >= 1; --k)
+#pragma unroll
+        for (int i = 0; i < k; ++i) x[i] -= f[i][k] * x[k];
+#pragma unroll
+    for (int i = 0; i < kGqPanel; ++i)
+        if (i < nb) r[(int64_t)(p0 + i) * n + j] = x[i];
+}
+
+// Rows above the panel: R[i][j] -= sum_k V[i][p0 + k] / V[p0 + k][p0 + k] R[p0 + k][j],
+// i < p0, j >= p0, 64 x 64 tiles.
+__global__ void __launch_bounds__(256) gptq_inv_gemm_kernel(const float *__restrict__ v, int n,
+                                                            int p0, int nb,
+                                                            float *__restrict__ r) {
+    __shared__ float fa[kGqTile][kGqPanel + 1], rb[kGqPanel][kGqTile + 1];
+    const int r0 = blockIdx.y * kGqTile, c0 = p0 + blockIdx.x * kGqTile;
+    for (int q = threadIdx.x; q < kGqTile * kGqPanel; q += 256) {
+        const int i = q / kGqPanel, k = q % kGqPanel;
+        fa[i][k] = r0 + i < p0 && k < nb
+                       ? v[(int64_t)(r0 + i) * n + p0 + k] / v[(int64_t)(p0 + k) * n + p0 + k]
+                       : 0.0f;
+        const int kk = q / kGqTile, c = q % kGqTile;
+        rb[kk][c] = kk < nb && c0 + c < n ? r[(int64_t)(p0 + kk) * n + c0 + c] : 0.0f;
+    }
+    __syncthreads();
+    const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+    float acc[4][4] = {};
+#pragma unroll 8
+    for (int k = 0; k < kGqPanel; ++k) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a)
+#pragma unroll
+            for (int b = 0; b < 4; ++b) acc[a][b] = fmaf(fa[ty + 16 * a][k], rb[k][tx + 16 * b], acc[a][b]);
+    }
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            const int i = r0 + ty + 16 * a, j = c0 + tx + 16 * b;
+            if (i < p0 && j < n) r[(int64_t)i * n + j] -= acc[a][b];
+        }
 }
 
 // R = I (upper part used), and the final U = diag(V)^-1 R (rows scaled), zeros below the diagonal.
@@ -305,17 +438,32 @@ hipError_t launch_gptq_factor(float *h, int64_t d_in, float alpha, float *u, flo
                               uint8_t *dead, hipStream_t stream) {
     const int n = static_cast<int>(d_in);
     hipLaunchKernelGGL(gptq_prepare_kernel, dim3(1), dim3(1024), 0, stream, h, n, alpha, dead);
-    for (int k = n - 1; k >= 0; --k) {
-        const int64_t work = std::max<int64_t>(static_cast<int64_t>(k) * (k + 1) / 2, k + 1);
-        hipLaunchKernelGGL(gptq_chol_step_kernel, dim3(blocks_for(work)), dim3(256), 0, stream,
-                           h, n, k, v);
+    const int last = (n - 1) / kGqPanel * kGqPanel;
+    // reverse Cholesky H = V V^T, panel by panel from the last
+    for (int p0 = last; p0 >= 0; p0 -= kGqPanel) {
+        const int nb = std::min(kGqPanel, n - p0);
+        hipLaunchKernelGGL(gptq_chol_diag_kernel, dim3(1), dim3(256), 0, stream, h, n, p0, nb, v);
+        if (p0 > 0) {
+            hipLaunchKernelGGL(gptq_chol_trsm_kernel, dim3(blocks_for(p0)), dim3(256), 0, stream,
+                               h, n, p0, nb, v);
+            const int t = p0 / kGqTile;
+            hipLaunchKernelGGL(gptq_chol_syrk_kernel, dim3(static_cast<unsigned>(t * (t + 1) / 2)),
+                               dim3(256), 0, stream, h, n, p0, nb, v);
+        }
     }
+    // U = V^-1: R = diag(V) U by block back substitution from the last panel, then the rows
+    // scaled
     hipLaunchKernelGGL(gptq_identity_kernel, dim3(blocks_for((int64_t)n * n)), dim3(256), 0,
                        stream, u, n);
-    for (int k = n - 1; k >= 1; --k) {
-        const int64_t work = static_cast<int64_t>(k) * (n - k);
-        hipLaunchKernelGGL(gptq_inv_step_kernel, dim3(blocks_for(work)), dim3(256), 0, stream, v,
-                           n, k, u);
+    for (int p0 = last; p0 >= 0; p0 -= kGqPanel) {
+        const int nb = std::min(kGqPanel, n - p0);
+        hipLaunchKernelGGL(gptq_inv_panel_kernel, dim3(blocks_for(n - p0)), dim3(256), 0, stream,
+                           v, n, p0, nb, u);
+        if (p0 > 0)
+            hipLaunchKernelGGL(gptq_inv_gemm_kernel,
+                               dim3(static_cast<unsigned>((n - p0 + kGqTile - 1) / kGqTile),
+                                    static_cast<unsigned>((p0 + kGqTile - 1) / kGqTile)),
+                               dim3(256), 0, stream, v, n, p0, nb, u);
     }
     hipLaunchKernelGGL(gptq_scale_rows_kernel, dim3(blocks_for((int64_t)n * n)), dim3(256), 0,
                        stream, v, n, u);
