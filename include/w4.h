@@ -14,8 +14,9 @@
  * Conventions shared by every entry point
  *   - Array arguments are DEVICE pointers owned by the caller.  The library never allocates,
  *     frees or retains device memory and keeps no state between calls (thread-safe; calls on one
- *     stream are ordered by that stream).  No entry point needs scratch memory: partial sums
- *     meet in LDS.
+ *     stream are ordered by that stream).  The linear layers and the codecs need no scratch
+ *     memory (partial sums meet in LDS); GPTQ's factor and column loop take caller-owned work
+ *     buffers.
  *   - bf16 values travel as uint16_t bit patterns.  `stream` is a hipStream_t passed as void*
  *     (NULL = the default stream).  Calls enqueue kernels and return without synchronizing.
  *   - Arguments are validated on the host before anything is enqueued.  A failed check returns
