@@ -92,14 +92,15 @@ __global__ void __launch_bounds__(256) pack_kernel(const float *__restrict__ w, 
     }
 }
 
-// One workgroup of kAqThreads threads per token row.  [Orin 从 FP 线性层到 INT4 DP4A 的数学推导],
+// One workgroup of T threads per token row.  [Orin 从 FP 线性层到 INT4 DP4A 的数学推导],
 // [Infra 2.2 量化的基本概念]:  s = max|x|/127,  q = clamp(rint(x/s), -127, 127).
-// A thread owns the 8-column chunks tid, tid + kAqThreads, ...; the first kAqCache of them stay in
-// registers between the max pass and the quantization pass, so a row of up to
-// kAqThreads * kAqCache * 8 columns is read from memory once.  Loads are 16 bytes (ldx % 8 == 0
-// keeps every chunk that starts before K inside the row); columns >= K are masked.
-constexpr int kAqThreads = 1024;
-constexpr int kAqCache = 4;
+// A thread owns the 8-column chunks tid, tid + T, ...; the first kAqCache of them stay in
+// registers between the max pass and the quantization pass, so a row of up to T * kAqCache * 8
+// columns is read from memory once.  Rows of up to 8192 columns run 256 threads caching 4 chunks
+// (more workgroups in flight per CU, and most threads hold work), as do rows of up to 20480
+// columns caching 10 when there are many rows; other rows run 1024 threads caching 4 (and
+// re-reading what does not fit).  Loads are 16 bytes (ldx % 8 == 0 keeps
+// every chunk that starts before K inside the row); columns >= K are masked.
 
 __device__ __forceinline__ float chunk_absmax(const uint4 &v, int64_t col, int64_t K) {
     const uint32_t u[4] = {v.x, v.y, v.z, v.w};
@@ -142,6 +143,7 @@ __device__ __forceinline__ int chunk_quantize(const uint4 &v, int64_t col, int64
     return sum;
 }
 
+template <int kAqThreads, int kAqCache>
 __global__ void __launch_bounds__(kAqThreads) act_quant_kernel(const uint16_t *__restrict__ x,
                                                                int64_t K, int64_t ldx,
                                                                int8_t *__restrict__ q, int64_t ldq,
@@ -219,8 +221,16 @@ hipError_t launch_pack(const float *w, int64_t d_out, int64_t d_in, int64_t ldw,
 
 hipError_t launch_act_quant(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int8_t *q,
                             int64_t ldq, float *s_x, int32_t *q_sum, hipStream_t stream) {
-    hipLaunchKernelGGL(act_quant_kernel, dim3(static_cast<unsigned>(M)), dim3(kAqThreads), 0,
-                       stream, x, K, ldx, q, ldq, s_x, q_sum);
+    const dim3 grid(static_cast<unsigned>(M));
+    if (K <= 256 * 8 * 4)
+        hipLaunchKernelGGL((act_quant_kernel<256, 4>), grid, dim3(256), 0, stream, x, K, ldx, q,
+                           ldq, s_x, q_sum);
+    else if (K <= 256 * 8 * 10 && M >= 256)  // (a few long rows: more threads per row)
+        hipLaunchKernelGGL((act_quant_kernel<256, 10>), grid, dim3(256), 0, stream, x, K, ldx, q,
+                           ldq, s_x, q_sum);
+    else
+        hipLaunchKernelGGL((act_quant_kernel<1024, 4>), grid, dim3(1024), 0, stream, x, K, ldx,
+                           q, ldq, s_x, q_sum);
     return hipGetLastError();
 }
 

@@ -335,6 +335,18 @@ def test_act_quant_configs():
     check_act_quant(x, "64 tokens, ragged K, one zero token")
 
 
+@pytest.mark.parametrize("M,K", [(2048, 3584), (300, 8192), (256, 8200), (260, 18944),
+                                 (256, 20480), (300, 20490), (255, 10001)])
+def test_act_quant_many_tokens(M, K):
+    """The row widths and token counts around each workgroup shape of the kernel (256 threads
+    caching 4 or 10 chunks, 1024 threads), the prefill sizes among them; ragged K."""
+    x = workloads.activations(24, M + K, M, K, 0.01, 20.0)
+    x[M // 2] = 0
+    xp = np.full((M, (K + 7) // 8 * 8), 0x7FC0, dtype=np.uint16)  # NaN past K: never read
+    xp[:, :K] = x
+    check_act_quant(xp, f"M={M} K={K}", K)
+
+
 def test_act_quant_all_bf16_patterns():
     """Every finite bf16 value, quantized against several fixed maxima."""
     allbits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
