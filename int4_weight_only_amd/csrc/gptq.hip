@@ -12,7 +12,7 @@
 //   * hessian: H = (2/N) X^T X, 64 x 64 output tiles, the tokens staged through LDS in fp32;
 //   * factor: dead columns and damping; the reverse Cholesky H = V V^T (V upper triangular),
 //     then U = V^-1 by back substitution, so that U^T U = V^-T V^-1 = H^-1. Both run by panels of
-//     64 columns from the last panel back: the panel's diagonal block in LDS (one workgroup), a
+//     64 columns from the last panel back: the panel's diagonal block in LDS (one wave), a
 //     triangular solve for the rows above it (one thread per row) and a GEMM update of the
 //     leading block (the Cholesky), or the substitution inside the panel (one thread per column)
 //     and a GEMM for the rows above it (the inverse);
@@ -101,39 +101,34 @@ __global__ void __launch_bounds__(1024) gptq_prepare_kernel(float *__restrict__ 
 constexpr int kGqPanel = 64;
 
 // Reverse Cholesky of the panel's diagonal block (its lower triangle, already updated by every
-// later panel) in LDS: V[P][P] (upper), one workgroup.
-__global__ void __launch_bounds__(256) gptq_chol_diag_kernel(const float *__restrict__ h, int n,
-                                                             int p0, int nb,
-                                                             float *__restrict__ v) {
-    __shared__ float a[kGqPanel][kGqPanel + 1];
-    for (int e = threadIdx.x; e < kGqPanel * kGqPanel; e += 256) {
-        const int i = e / kGqPanel, j = e % kGqPanel;
-        a[i][j] = i < nb && j <= i ? h[(int64_t)(p0 + i) * n + p0 + j] : 0.0f;
-    }
-    __syncthreads();
+// later panel): V[P][P] (upper), one wave; lane i holds row i of the block in registers, and at
+// step k lane k publishes its row through LDS.
+__global__ void __launch_bounds__(kGqPanel) gptq_chol_diag_kernel(const float *__restrict__ h,
+                                                                  int n, int p0, int nb,
+                                                                  float *__restrict__ v) {
+    __shared__ float rowk[kGqPanel];
+    const int i = threadIdx.x;
+    float r[kGqPanel];
+#pragma unroll
+    for (int j = 0; j < kGqPanel; ++j)
+        r[j] = i < nb && j <= i ? h[(int64_t)(p0 + i) * n + p0 + j] : 0.0f;
     for (int k = nb - 1; k >= 0; --k) {
-        const float d = a[k][k];
-        const float rs = 1.0f / sqrtf(d);
-        // column k of V: V[i][k] = a[k][i] / sqrt(d), i <= k (a[k][k] / sqrt(d) = sqrt(d))
-        for (int i = threadIdx.x; i <= k; i += 256)
-            v[(int64_t)(p0 + i) * n + p0 + k] = a[k][i] * rs;
-        // the leading k x k block: a[i][j] -= a[k][i] a[k][j] / d, j <= i < k
-        const int tot = k * (k + 1) / 2;
-        float upd[8];
-        int idx[8];
-        int cnt = 0;
-        for (int e = threadIdx.x; e < tot; e += 256) {
-            int i = static_cast<int>((sqrtf(8.0f * static_cast<float>(e) + 1.0f) - 1.0f) * 0.5f);
-            while (i * (i + 1) / 2 > e) --i;
-            while ((i + 1) * (i + 2) / 2 <= e) ++i;
-            const int j = e - i * (i + 1) / 2;
-            upd[cnt] = a[k][i] * (a[k][j] / d);
-            idx[cnt] = i * (kGqPanel + 1) + j;
-            ++cnt;
+        if (i == k) {
+#pragma unroll
+            for (int j = 0; j < kGqPanel; ++j) rowk[j] = r[j];
         }
-        __syncthreads();  // every read of row k and of the block is done before the writes
-        for (int c = 0; c < cnt; ++c) (&a[0][0])[idx[c]] -= upd[c];
         __syncthreads();
+        const float d = rowk[k];
+        // column k of V: V[i][k] = a[k][i] / sqrt(d) for i <= k
+        if (i <= k) v[(int64_t)(p0 + i) * n + p0 + k] = rowk[i] / sqrtf(d);
+        // row i of the leading k x k block: a[i][j] -= a[k][i] a[k][j] / d, j <= i < k
+        if (i < k) {
+            const float f = rowk[i] / d;
+#pragma unroll
+            for (int j = 0; j < kGqPanel; ++j)
+                if (j <= i) r[j] -= f * rowk[j];
+        }
+        __syncthreads();  // every lane has read row k before the next one is published
     }
 }
 
@@ -442,7 +437,8 @@ hipError_t launch_gptq_factor(float *h, int64_t d_in, float alpha, float *u, flo
     // reverse Cholesky H = V V^T, panel by panel from the last
     for (int p0 = last; p0 >= 0; p0 -= kGqPanel) {
         const int nb = std::min(kGqPanel, n - p0);
-        hipLaunchKernelGGL(gptq_chol_diag_kernel, dim3(1), dim3(256), 0, stream, h, n, p0, nb, v);
+        hipLaunchKernelGGL(gptq_chol_diag_kernel, dim3(1), dim3(kGqPanel), 0, stream, h, n, p0,
+                           nb, v);
         if (p0 > 0) {
             hipLaunchKernelGGL(gptq_chol_trsm_kernel, dim3(blocks_for(p0)), dim3(256), 0, stream,
                                h, n, p0, nb, v);
