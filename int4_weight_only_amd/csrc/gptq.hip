@@ -305,6 +305,30 @@ __device__ GroupQ group_stats(const float *__restrict__ row, int k0, int g, int 
     return q;
 }
 
+// The same statistics for a group of kGqBlock columns held in registers (columns past d_in are
+// zeros there, as pads are).
+__device__ GroupQ group_stats_regs(const float (&wv)[kGqBlock], int mode) {
+    float amax = fabsf(wv[0]), mx = wv[0], mn = wv[0];
+#pragma unroll
+    for (int t = 1; t < kGqBlock; ++t) {
+        const float r = wv[t], a = fabsf(r);
+        amax = a > amax ? a : amax;
+        mx = r > mx ? r : mx;
+        mn = r < mn ? r : mn;
+    }
+    GroupQ q;
+    if (mode == 0) {
+        q.s = bf16_to_f32(f32_to_bf16(amax / 7.0f + 0.0f));
+        q.z = 8.0f;
+    } else {
+        q.s = bf16_to_f32(f32_to_bf16((mx - mn) / 15.0f + 0.0f));
+        float zf = 0.0f;
+        if (q.s != 0.0f) zf = rintf(-mn / q.s) + 0.0f;
+        q.z = bf16_to_f32(f32_to_bf16(zf));
+    }
+    return q;
+}
+
 __device__ __forceinline__ float code_of(float r, GroupQ q) {
     if (q.s == 0.0f) return q.z;
     return fminf(fmaxf(rintf(r / q.s + q.z), 0.0f), 15.0f);
@@ -344,11 +368,14 @@ __global__ void __launch_bounds__(256) gptq_block_kernel(
         if (c < cols) {
             const int k = b0 + c;
             if (k % g == 0) {  // a group starts here: statistics of the current weights
-                // (the block's own columns are the up-to-date values in registers)
+                if (g == kGqBlock) {  // the group is this block (c == 0): its registers
+                    q = group_stats_regs(wv, mode);
+                } else {  // (the block's own columns are the up-to-date values in registers)
 #pragma unroll
-                for (int t = 0; t < kGqBlock; ++t)
-                    if (t >= c && t < cols) row[b0 + t] = wv[t];
-                q = group_stats(row, k, g, d_in, mode);
+                    for (int t = 0; t < kGqBlock; ++t)
+                        if (t >= c && t < cols) row[b0 + t] = wv[t];
+                    q = group_stats(row, k, g, d_in, mode);
+                }
                 scales[(int64_t)j * n_groups + k / g] = static_cast<uint16_t>(f32_to_bf16(q.s));
                 if (mode != 0) zeros[(int64_t)j * n_groups + k / g] = static_cast<uint16_t>(f32_to_bf16(q.z));
             }
