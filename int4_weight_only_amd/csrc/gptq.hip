@@ -16,7 +16,7 @@
 //     triangular solve for the rows above it (one thread per row) and a GEMM update of the
 //     leading block (the Cholesky), or the substitution inside the panel (one thread per column)
 //     and a GEMM for the rows above it (the inverse);
-//   * quantize: blocks of 32 columns. One thread per output row runs the block's columns in
+//   * quantize: blocks of 32 columns. Four lanes per output row run the block's columns in
 //     order (the group's scale and zero by w4_pack's rule from the current weights at the group's
 //     first column, the code, e_i, the updates inside the block, the row's loss), then a GEMM
 //     applies the block's errors to the columns after it: W[:, b+32:] -= E U[b:b+32, b+32:].
@@ -305,38 +305,17 @@ __device__ GroupQ group_stats(const float *__restrict__ row, int k0, int g, int 
     return q;
 }
 
-// The same statistics for a group of kGqBlock columns held in registers (columns past d_in are
-// zeros there, as pads are).
-__device__ GroupQ group_stats_regs(const float (&wv)[kGqBlock], int mode) {
-    float amax = fabsf(wv[0]), mx = wv[0], mn = wv[0];
-#pragma unroll
-    for (int t = 1; t < kGqBlock; ++t) {
-        const float r = wv[t], a = fabsf(r);
-        amax = a > amax ? a : amax;
-        mx = r > mx ? r : mx;
-        mn = r < mn ? r : mn;
-    }
-    GroupQ q;
-    if (mode == 0) {
-        q.s = bf16_to_f32(f32_to_bf16(amax / 7.0f + 0.0f));
-        q.z = 8.0f;
-    } else {
-        q.s = bf16_to_f32(f32_to_bf16((mx - mn) / 15.0f + 0.0f));
-        float zf = 0.0f;
-        if (q.s != 0.0f) zf = rintf(-mn / q.s) + 0.0f;
-        q.z = bf16_to_f32(f32_to_bf16(zf));
-    }
-    return q;
-}
-
 __device__ __forceinline__ float code_of(float r, GroupQ q) {
     if (q.s == 0.0f) return q.z;
     return fminf(fmaxf(rintf(r / q.s + q.z), 0.0f), 15.0f);
 }
 
-// One block of 32 columns, one thread per row: group statistics at group starts (from the
-// current row, read from memory), codes, the errors and the in-block updates; E[j][c] receives
-// e for the trailing update, the codes go to qweight (pads of the last group too).
+// One block of 32 columns, four lanes per output row (lane part p holds columns 8p .. 8p + 7 in
+// registers): group statistics at group starts (group starts fall on block starts, since groups
+// are multiples of 32 columns), then the columns in order -- the owning lane takes the code, the
+// error and e = err / U_cc, the row's four lanes share e and update their later columns.
+// E[j][c] receives e for the trailing update; the codes go to qweight (pads of the last group
+// too).
 __global__ void __launch_bounds__(256) gptq_block_kernel(
     float *__restrict__ w, int d_out, int d_in, int64_t ldw, const float *__restrict__ u, int n,
     int b0, int g, int mode, uint8_t *__restrict__ qweight, int64_t row_bytes,
@@ -349,57 +328,81 @@ __global__ void __launch_bounds__(256) gptq_block_kernel(
         ub[i][c] = i < cols && c < cols ? u[(int64_t)(b0 + i) * n + b0 + c] : 0.0f;
     }
     __syncthreads();
-    const int j = blockIdx.x * 256 + threadIdx.x;
-    if (j >= d_out) return;
+    const int j = blockIdx.x * 64 + static_cast<int>(threadIdx.x >> 2);
+    const int p = threadIdx.x & 3;
+    if (j >= d_out) return;  // (a row's four lanes leave together)
+    const int lane = threadIdx.x & (kWave - 1), base = lane & ~3;
     float *row = w + (int64_t)j * ldw;
-    float wv[kGqBlock];
+    float wv[8];
 #pragma unroll
-    for (int c = 0; c < kGqBlock; ++c) wv[c] = c < cols ? row[b0 + c] : 0.0f;
+    for (int t = 0; t < 8; ++t) wv[t] = 8 * p + t < cols ? row[b0 + 8 * p + t] : 0.0f;
     GroupQ q{0.0f, 8.0f};
     const int G0 = b0 / g;
     if (b0 % g != 0) {  // the block continues a group: its statistics are stored
         q.s = bf16_to_f32(scales[(int64_t)j * n_groups + G0]);
         q.z = mode == 0 ? 8.0f : bf16_to_f32(zeros[(int64_t)j * n_groups + G0]);
-    }
-    float loss = 0.0f;
-    uint32_t packed[kGqBlock / 8] = {};
+    } else {  // a group starts here: statistics of the current weights
+        if (g == kGqBlock) {  // the group is this block, in the registers of the four lanes
+            float amax = fabsf(wv[0]), mx = wv[0], mn = wv[0];
 #pragma unroll
-    for (int c = 0; c < kGqBlock; ++c) {
-        if (c < cols) {
-            const int k = b0 + c;
-            if (k % g == 0) {  // a group starts here: statistics of the current weights
-                if (g == kGqBlock) {  // the group is this block (c == 0): its registers
-                    q = group_stats_regs(wv, mode);
-                } else {  // (the block's own columns are the up-to-date values in registers)
-#pragma unroll
-                    for (int t = 0; t < kGqBlock; ++t)
-                        if (t >= c && t < cols) row[b0 + t] = wv[t];
-                    q = group_stats(row, k, g, d_in, mode);
-                }
-                scales[(int64_t)j * n_groups + k / g] = static_cast<uint16_t>(f32_to_bf16(q.s));
-                if (mode != 0) zeros[(int64_t)j * n_groups + k / g] = static_cast<uint16_t>(f32_to_bf16(q.z));
+            for (int t = 1; t < 8; ++t) {
+                amax = fmaxf(amax, fabsf(wv[t]));
+                mx = fmaxf(mx, wv[t]);
+                mn = fminf(mn, wv[t]);
             }
-            const float code = code_of(wv[c], q);
-            const float qv = q.s * (code - q.z);
-            const float err = wv[c] - qv;
-            const float d = ub[c][c];
-            loss += 0.5f * (err * err) / (d * d);
-            const float e = err / d;
-            ebuf[(int64_t)j * kGqBlock + c] = e;
 #pragma unroll
-            for (int t = 0; t < kGqBlock; ++t)
-                if (t > c) wv[t] -= e * ub[c][t];
-            wv[c] = qv;
-            packed[c / 8] |= static_cast<uint32_t>(code) << (4 * (c % 8));
-        } else {
-            ebuf[(int64_t)j * kGqBlock + c] = 0.0f;
-            packed[c / 8] |= static_cast<uint32_t>(code_of(0.0f, q)) << (4 * (c % 8));
+            for (int o = 1; o < 4; o <<= 1) {
+                amax = fmaxf(amax, __shfl_xor(amax, o, kWave));
+                mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+                mn = fminf(mn, __shfl_xor(mn, o, kWave));
+            }
+            if (mode == 0) {
+                q.s = bf16_to_f32(f32_to_bf16(amax / 7.0f + 0.0f));
+                q.z = 8.0f;
+            } else {
+                q.s = bf16_to_f32(f32_to_bf16((mx - mn) / 15.0f + 0.0f));
+                float zf = 0.0f;
+                if (q.s != 0.0f) zf = rintf(-mn / q.s) + 0.0f;
+                q.z = bf16_to_f32(f32_to_bf16(zf));
+            }
+        } else {  // the group reaches past the block: its columns in memory are current
+            q = group_stats(row, b0, g, d_in, mode);
+        }
+        if (p == 0) {
+            scales[(int64_t)j * n_groups + G0] = static_cast<uint16_t>(f32_to_bf16(q.s));
+            if (mode != 0) zeros[(int64_t)j * n_groups + G0] = static_cast<uint16_t>(f32_to_bf16(q.z));
         }
     }
+    float loss = 0.0f;
+    uint32_t packed = 0u;
 #pragma unroll
-    for (int c = 0; c < kGqBlock / 8; ++c)
-        *reinterpret_cast<uint32_t *>(qweight + (int64_t)j * row_bytes + b0 / 2 + 4 * c) = packed[c];
-    if (row_loss) row_loss[j] = (b0 == 0 ? 0.0f : row_loss[j]) + loss;
+    for (int c = 0; c < kGqBlock; ++c) {
+        const int owner = c >> 3, t = c & 7;
+        float e = 0.0f;
+        if (p == owner) {
+            if (c < cols) {
+                const float code = code_of(wv[t], q);
+                const float qv = q.s * (code - q.z);
+                const float err = wv[t] - qv;
+                const float d = ub[c][c];
+                loss += 0.5f * (err * err) / (d * d);
+                e = err / d;
+                ebuf[(int64_t)j * kGqBlock + c] = e;
+                packed |= static_cast<uint32_t>(code) << (4 * t);
+            } else {
+                ebuf[(int64_t)j * kGqBlock + c] = 0.0f;
+                packed |= static_cast<uint32_t>(code_of(0.0f, q)) << (4 * t);
+            }
+        }
+        e = __shfl(e, base + owner, kWave);
+#pragma unroll
+        for (int tt = 0; tt < 8; ++tt)
+            if (8 * p + tt > c) wv[tt] -= e * ub[c][8 * p + tt];
+    }
+    *reinterpret_cast<uint32_t *>(qweight + (int64_t)j * row_bytes + b0 / 2 + 4 * p) = packed;
+#pragma unroll
+    for (int o = 1; o < 4; o <<= 1) loss += __shfl_xor(loss, o, kWave);
+    if (row_loss && p == 0) row_loss[j] = (b0 == 0 ? 0.0f : row_loss[j]) + loss;
 }
 
 // Trailing update: W[:, c0:] -= E U[b0:b0+32, c0:], 64 x 64 tiles of W (rows x columns).
@@ -503,7 +506,8 @@ hipError_t launch_gptq_quantize(float *w, int64_t d_out, int64_t d_in, int64_t l
         hipLaunchKernelGGL(gptq_dead_kernel, dim3(blocks_for(d_out * d_in)), dim3(256), 0, stream,
                            w, static_cast<int>(d_out), n, ldw, dead);
     for (int b0 = 0; b0 < k_pad; b0 += kGqBlock) {  // (blocks past d_in write pad codes)
-        hipLaunchKernelGGL(gptq_block_kernel, dim3(blocks_for(d_out)), dim3(256), 0, stream, w,
+        hipLaunchKernelGGL(gptq_block_kernel, dim3(static_cast<unsigned>((d_out + 63) / 64)),
+                           dim3(256), 0, stream, w,
                            static_cast<int>(d_out), n, ldw, u, n, b0, static_cast<int>(span), mode,
                            qweight, k_pad / 2, scales, zeros, static_cast<int>(n_groups), ebuf,
                            row_loss);
