@@ -211,6 +211,26 @@ def test_gptq_quantize_against_oracle(g, mode):
     assert codes.max() <= 15
 
 
+def test_gptq_strided_weights_without_dead_flags():
+    """A weight with a row stride past d_in (junk there, never read or used) and no dead-column
+    flags: the same codes and scales as the dense call."""
+    d_out, d_in, ldw, N = 100, 200, 232, 160
+    w = workloads.weight(74, 0, d_out, d_in)
+    xb = _gptq_calib(74, N, d_in)
+    h = w4.gptq_hessian(dev_bf16(xb))
+    u, dead = w4.gptq_factor(h, 0.01)
+    torch.cuda.synchronize()
+    assert int(dead.sum()) == 0
+    wp = np.full((d_out, ldw), 1e30, dtype=np.float32)
+    wp[:, :d_in] = w
+    a = w4.gptq_quantize(torch.from_numpy(wp).cuda(), u, None, 64, ASYM, d_in)
+    b = w4.gptq_quantize(torch.from_numpy(w.copy()).cuda(), u, dead, 64, ASYM)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert np.array_equal(host(x.view(torch.int16) if x.dtype == torch.bfloat16 else x),
+                              host(y.view(torch.int16) if y.dtype == torch.bfloat16 else y))
+
+
 def test_gptq_end_to_end_c4_qkv():
     """The whole path on the GPU at the C4 q/k/v shape (4608 x 3584, g32 SYM, 2048 calibration
     tokens): GPTQ's layer objective is below RTN's, and its loss identity holds."""
