@@ -311,8 +311,9 @@ def test_qat_repack_ragged_and_edges():
 
 
 def test_qat_repack_c4_full_size():
-    """The C4 q/k/v and down shapes (g32), 1% of the groups off the grid."""
-    for li in (0, 2):
+    """The C4 q/k/v, gate/up (the benchmarked shape) and down shapes (g32), 1% of the groups off
+    the grid."""
+    for li in (0, 1, 2):
         lin = workloads.C4.linears[li]
         w = workloads.qat_grid_weight(workloads.C4.seed, li, lin.d_out, lin.d_in, 0.01)
         _, _, m = check_qat(w, lin.d_in, f"C4/{lin.name}")
