@@ -9,7 +9,7 @@ distinct copies totalling more than twice the 256 MB Infinity Cache, so they str
 Also reported (in "secondary"): the prefill GEMM at M = 2048 (TFLOP/s and MFMA-peak fraction),
 the W4A8 decode path, and the 28-layer asymmetric decoder-step linear set at M = 1, 8, 16.
 
-Prints ONE JSON line.  Only --gpus 1 is supported (this build targets one GPU).
+Prints ONE JSON line.  Only --gpus 1 is supported (the library runs on one GPU).
 """
 import argparse
 import hashlib
@@ -467,7 +467,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              "(this build has no multi-GPU path).", file=sys.stderr)
+              "(the library has no multi-GPU path).", file=sys.stderr)
         sys.exit(2)
 
     import torch

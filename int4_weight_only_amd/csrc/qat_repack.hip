@@ -118,7 +118,7 @@ __global__ void __launch_bounds__(kQatThreads) qat_repack_kernel(
             const float s_m = amax / static_cast<float>(m);
             // v = r / s_m decides. r (1 / s_m) is within 2^-19 of it: unless some value's
             // estimate lies within 2^-14 of the 1/16 threshold (or the reciprocal is not finite),
-            // the estimates give the same levels and the same verdict (near a half-integer the two
+            // the estimates give the same levels and the same decision (near a half-integer the two
             // may round apart, but both are then rejected); otherwise the group is tested again
             // with the division.
             const float rcp = 1.0f / s_m;
