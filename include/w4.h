@@ -65,6 +65,7 @@ enum { W4_OUT_BF16 = 0, W4_OUT_F32 = 1 }; /* element type of y                  
 #define W4_MAX_DIM ((int64_t)1 << 24)  /* d_out, d_in, M, K                      */
 #define W4_MAX_W4A8_D_IN ((int64_t)1 << 20) /* keeps sum(code * q) within int32: 2^20*15*127 < 2^31 */
 #define W4_GEMV_MAX_M 64
+#define W4_DECODE_MAX_D_IN ((int64_t)1 << 16) /* d_in of the decode (M <= 64) entry points     */
 #define W4_MAX_GPTQ_D_IN 8192 /* the GPTQ factorization holds d_in x d_in fp32 matrices      */
 
 /*
@@ -163,7 +164,8 @@ int w4_qat_repack(const uint16_t *w, int64_t d_out, int64_t d_in, int64_t ldw, u
  *   y        [M][ldy], ldy >= d_out, element type out_dtype (W4_OUT_BF16 / W4_OUT_F32),
  *            naturally aligned.  Accumulation is fp32; the bf16 output is the round-to-nearest-
  *            even image of the fp32 result of the same call.
- * M > 64 returns W4_ERR_UNSUPPORTED (use w4_gemm); d_in <= 65536 (else W4_ERR_RANGE).
+ * M > 64 returns W4_ERR_UNSUPPORTED (use w4_gemm); d_in <= W4_DECODE_MAX_D_IN = 65536 (else
+ * W4_ERR_RANGE; w4_gemm serves any d_in up to W4_MAX_DIM).
  */
 int w4_gemv(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
             const uint16_t *scales, const uint16_t *zeros, const uint16_t *bias, int64_t d_out,
@@ -183,6 +185,7 @@ int w4_gemv(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
  * Served by the int8 matrix-core decode kernel: 1 <= M <= 4 tokens, group_size 128 or 256, or
  * 0 with k_pad a multiple of 128, and k_pad <= 32768 / M (its activation stage); other arguments
  * return W4_ERR_UNSUPPORTED (use w4_gemv on the fused weight and apply the gate separately).
+ * d_in <= W4_DECODE_MAX_D_IN (W4_ERR_RANGE beyond).
  */
 int w4_gemv_glu(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
                 const uint16_t *scales, const uint16_t *zeros, const uint16_t *bias, int64_t d_ff,
@@ -220,7 +223,9 @@ int act_quant_int8(const uint16_t *x, int64_t M, int64_t K, int64_t ldx, int8_t 
  *   acc[m][j] = sum_{k < d_in} (code[j][k] - 8) * q[m][k]          (exact, int32)
  *   y[m][j]   = s_w[j] * s_x[m] * acc[m][j] + b[j]                  (fp32)
  * Weights are a per-row symmetric pack (w4_pack with group_size = 0, W4_SYM); s_w is that pack's
- * scales array.  1 <= M <= 64 and d_in <= W4_MAX_W4A8_D_IN, so every partial sum fits in int32.
+ * scales array.  1 <= M <= 64 (W4_ERR_UNSUPPORTED beyond: use w4a8_gemm) and
+ * d_in <= W4_DECODE_MAX_D_IN = 65536, the decode kernels' limit (W4_ERR_RANGE beyond: w4a8_gemm
+ * serves d_in up to W4_MAX_W4A8_D_IN = 2^20, the bound that keeps every partial sum in int32).
  *   q        int8 [M][ldq], ldq >= d_in, ldq % 16 == 0, 16-byte aligned (from act_quant_int8)
  *   s_x      fp32 [M]
  *   qweight  uint8 [d_out][k_pad/2], k_pad = ceil(d_in/32)*32, 16-byte aligned
@@ -242,6 +247,7 @@ int w4a8_gemv(const int8_t *q, const float *s_x, int64_t M, int64_t ldq, const u
  *   qweight, s_w, bias, y, out_dtype, acc: as for w4a8_gemv
  *   s_x      fp32 [M] or NULL: receives the token scales
  * The codes, s_x and acc are bit-identical to those of act_quant_int8 + w4a8_gemv on the same x.
+ * Limits: those of w4a8_gemv (1 <= M <= 64, d_in <= W4_DECODE_MAX_D_IN, W4_ERR_RANGE beyond).
  * Every workgroup quantizes the whole activation row it needs; rows longer than the kernel's
  * activation stage (k_pad > 32768) return W4_ERR_UNSUPPORTED: use the two calls.
  */

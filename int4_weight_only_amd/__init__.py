@@ -36,12 +36,12 @@ class W4Error(RuntimeError):
         self.status = status
 
 
-def _load():
-    if not os.path.exists(_LIB_PATH):
-        raise ImportError(f"libw4.so not found at {_LIB_PATH}; build it with "
+def _load(path):
+    if not os.path.exists(path):
+        raise ImportError(f"{os.path.basename(path)} not found at {path}; build it with "
                           "`python -c 'import __graft_entry__ as g; g.build()'` or "
                           "`python int4_weight_only_amd/build.py`")
-    lib = ctypes.CDLL(_LIB_PATH)
+    lib = ctypes.CDLL(path)
     i64, p, i32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int
     lib.w4_packed_layout.argtypes = [i64, i64, i32, ctypes.POINTER(i64), ctypes.POINTER(i64),
                                      ctypes.POINTER(ctypes.c_size_t)]
@@ -69,11 +69,21 @@ def _load():
     return lib
 
 
-_lib = _load()
+_lib = _load(_LIB_PATH)
 
 
 def library_path():
     return _LIB_PATH
+
+
+def _select_library(path):
+    """Bind every entry point of this module to another build of the library (the tests use the
+    build with the kernel-choice hook, libw4_hooks.so); returns the path bound before."""
+    global _lib, _LIB_PATH
+    prev = _LIB_PATH
+    _lib = _load(path)
+    _LIB_PATH = path
+    return prev
 
 
 def _check(fn, status):
@@ -105,6 +115,23 @@ def _need(t, name, dtype, device=None, dim=None):
         raise ValueError(f"{name} must have {dim} dims, got {t.dim()}")
     if t.dim() > 0 and t.stride(-1) != 1:
         raise ValueError(f"{name} must be contiguous along its last dim")
+
+
+def _check_out_shape(out, rows, cols, name="out"):
+    """A caller-supplied output must hold `rows` x `cols` elements at its own row stride: the
+    kernels write rows 0 .. rows-1, columns 0 .. cols-1, with ldy = out.stride(0)."""
+    if out.shape[0] < rows or out.shape[1] < cols:
+        raise ValueError(f"{name} has shape {tuple(out.shape)}, needs at least ({rows}, {cols})")
+    if rows > 1 and out.stride(0) < cols:
+        raise ValueError(f"{name} rows overlap: stride {out.stride(0)} < {cols} columns")
+
+
+def _out(out, rows, cols, tdtype, dev):
+    if out is None:
+        return torch.empty((rows, cols), dtype=tdtype, device=dev)
+    _need(out, "out", tdtype, dev, 2)
+    _check_out_shape(out, rows, cols)
+    return out
 
 
 def packed_layout(d_out, d_in, group_size):
@@ -229,10 +256,7 @@ def _linear(fn_name, x, qweight, scales, zeros, bias, d_in, group_size, out_dtyp
     if x.shape[1] < d_in:
         raise ValueError(f"x has {x.shape[1]} columns, fewer than d_in={d_in}")
     tdtype = torch.float32 if out_dtype == W4_OUT_F32 else torch.bfloat16
-    if out is None:
-        out = torch.empty((M, d_out), dtype=tdtype, device=dev)
-    else:
-        _need(out, "out", tdtype, dev, 2)
+    out = _out(out, M, d_out, tdtype, dev)
     fn = getattr(_lib, fn_name)
     args = [_ptr(x), M, x.stride(0), _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(bias),
             d_out, d_in, group_size, _ptr(out), out.stride(0), out_dtype]
@@ -273,10 +297,7 @@ def w4_gemv_glu(x, qweight, scales, zeros, bias, d_in, group_size, out_dtype=W4_
     if x.shape[1] < d_in:
         raise ValueError(f"x has {x.shape[1]} columns, fewer than d_in={d_in}")
     tdtype = torch.float32 if out_dtype == W4_OUT_F32 else torch.bfloat16
-    if out is None:
-        out = torch.empty((M, d_ff), dtype=tdtype, device=dev)
-    else:
-        _need(out, "out", tdtype, dev, 2)
+    out = _out(out, M, d_ff, tdtype, dev)
     _check("w4_gemv_glu", _lib.w4_gemv_glu(_ptr(x), M, x.stride(0), _ptr(qweight), _ptr(scales),
                                            _ptr(zeros), _ptr(bias), d_ff, d_in, group_size,
                                            _ptr(out), out.stride(0), out_dtype, _stream(dev)))
@@ -352,10 +373,7 @@ def _w4a8(name, q, s_x, qweight, s_w, bias, d_in, out_dtype, want_acc, out):
     if s_x.shape[0] != M or q.shape[1] < d_in:
         raise ValueError("q must be [M][>= d_in] and s_x [M]")
     tdtype = torch.float32 if out_dtype == W4_OUT_F32 else torch.bfloat16
-    if out is None:
-        out = torch.empty((M, d_out), dtype=tdtype, device=dev)
-    else:
-        _need(out, "out", tdtype, dev, 2)
+    out = _out(out, M, d_out, tdtype, dev)
     acc = torch.empty((M, d_out), dtype=torch.int32, device=dev) if want_acc else None
     _check(name, getattr(_lib, name)(_ptr(q), _ptr(s_x), M, q.stride(0), _ptr(qweight),
                                      _ptr(s_w), _ptr(bias), d_out, d_in, _ptr(out),
@@ -385,10 +403,7 @@ def w4a8_linear(x, qweight, s_w, bias, d_in, out_dtype=W4_OUT_BF16, want_acc=Fal
     if x.shape[1] < d_in:
         raise ValueError(f"x has {x.shape[1]} columns, fewer than d_in={d_in}")
     tdtype = torch.float32 if out_dtype == W4_OUT_F32 else torch.bfloat16
-    if out is None:
-        out = torch.empty((M, d_out), dtype=tdtype, device=dev)
-    else:
-        _need(out, "out", tdtype, dev, 2)
+    out = _out(out, M, d_out, tdtype, dev)
     acc = torch.empty((M, d_out), dtype=torch.int32, device=dev) if want_acc else None
     s_x = torch.empty(M, dtype=torch.float32, device=dev) if want_scales else None
     _check("w4a8_linear", _lib.w4a8_linear(_ptr(x), M, x.stride(0), _ptr(qweight), _ptr(s_w),

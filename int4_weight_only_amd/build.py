@@ -29,9 +29,17 @@ FLAGS = [
 EXTRA = {"gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
+# The test library: the same sources, with the kernel-choice hook of decode_i8.hip compiled in
+# (W4_TEST_HOOKS). Only the tests load it; the product library has no such entry point.
+HOOKS_LIB = os.path.join(HERE, "libw4_hooks.so")
+HOOKED = {"decode_i8.hip"}
+
+
+def _compile(src: str, verbose: bool, hooks: bool = False) -> str:
+    stem = os.path.splitext(src)[0] + ("_hooks" if hooks else "")
+    obj = os.path.join(BUILD, stem + ".o")
+    defs = ["-DW4_TEST_HOOKS"] if hooks else []
+    cmd = [HIPCC, *FLAGS, *EXTRA.get(src, []), *defs, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -40,16 +48,24 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str, verbose: bool) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = [(s, False) for s in SOURCES] + [(s, True) for s in sorted(HOOKED)]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        objs = list(ex.map(lambda j: _compile(j[0], verbose, j[1]), jobs))
+    plain = objs[:len(SOURCES)]
+    hooked = {s: o for (s, h), o in zip(jobs, objs) if h}
+    _link(plain, LIB, verbose)
+    _link([hooked.get(s, o) for s, o in zip(SOURCES, plain)], HOOKS_LIB, verbose)
     return LIB
 
 

@@ -37,8 +37,8 @@ Layout layout_of(int64_t d_in, int group_size) {
 }
 
 // The decode kernels keep one row's columns spread over at most 16 waves x 64 lanes x a few
-// 32-column steps; this bounds d_in for the decode entry points.
-constexpr int64_t kDecodeMaxDin = 65536;
+// 32-column steps; this bounds d_in for the decode entry points (w4.h: W4_DECODE_MAX_D_IN).
+constexpr int64_t kDecodeMaxDin = W4_DECODE_MAX_D_IN;
 
 int check_dims(int64_t d_out, int64_t d_in) {
     if (d_out < 1 || d_in < 1) return W4_ERR_SHAPE;

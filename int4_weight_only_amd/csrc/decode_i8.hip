@@ -8,21 +8,22 @@
 // 瓶颈": decode time is the weight stream).
 //
 // The dot products of a group run on v_mfma_i32_16x16x64_i8 with the raw codes as one operand:
-//   * activations: per token and 128-column group, x is scaled by 2^S with max |x| 2^S in
-//     [2^19, 2^20) and rounded to an integer X (exact for every |x| >= 2^-12 max, as bf16 carries
-//     8 significant bits; smaller values are off by at most 2^-21 max). X is written with three
-//     7-bit digits, X = b0 + 128 b1 + 16384 (b2 - 64) with b0 = X mod 128, b1 = floor(X / 128)
-//     mod 128, b2 = floor(X / 16384) + 64, all in [0, 127]. The digits of token t are rows
-//     4t .. 4t+2 of the MFMA's A operand and row 4t+3 is all ones, so one MFMA gives, for up to
-//     four tokens, sum c b0, sum c b1, sum c b2 and sum c of each of 16 rows;
+//   * activations: per token and 128-column group, X = rint(x 2^S) with max|x| 2^S in
+//     [2^29, 2^30). X is exact for every |x| >= 2^-22 max|x| (bf16 carries 8 significant bits) and
+//     off by at most 2^-30 max|x| otherwise, so an outlier channel in a group costs the other
+//     columns of the group nothing measurable ([Infra] section 2.4: activation outliers sit in a
+//     few channels). X is written as four signed base-256 digits: the bytes of
+//     (X + 0x80808080) ^ 0x80808080 are d0..d3 in [-128, 127] with X = sum_p d_p 256^p. The
+//     digits of token t are rows 4t .. 4t+3 of the MFMA's A operand, so one MFMA serves up to
+//     four tokens;
 //   * weights: a lane's 16 bytes (32 codes) of one row become two int8 operands, the low nibbles
 //     (w & 0x0F0F0F0F) and the high nibbles ((w >> 4) & 0x0F0F0F0F) -- three VALU operations per
 //     8 codes instead of a dequantization;
-//   * the integer sums are exact; the zero point and the digit offset are removed in int32,
-//     sum (c - z) X = [sum c (b0 + 128 b1) - z B01] + 16384 [sum c b2 - 64 sum c - z B2] with
-//     the group's digit sums B01 = sum (b0 + 128 b1) and B2 = sum (b2 - 64), so padding columns
-//     (c = z) add exactly nothing whatever x holds there;
-//   * the two integer parts are added once in fp32 and scaled by s 2^-S.
+//   * two MFMAs per (16 rows x 128 columns) unit give sum c d_p of every digit plane p; the zero
+//     point is removed per plane in int32 with the group's digit sums D_p:
+//     T_p = sum (c - z) d_p = sum c d_p - z D_p, exactly, so padding columns (c = z) add exactly
+//     nothing whatever x holds there; then sum (c - z) X = (T0 + 256 T1) + 65536 (T2 + 256 T3),
+//     one fp32 rounding, scaled by s 2^-S.
 // Zero points that are not integers of magnitude <= 256 (w4_pack never makes one) split into
 // such an integer and a residual applied through the group's sum of X.
 //
@@ -55,7 +56,7 @@ constexpr int kI8MaxTokens = 4;
 constexpr uint32_t kI8LdsLimit = 160 * 1024;
 
 // LDS layout (bytes). a: the digit operands, [group][lo/hi][k-block q][row 0 .. 4M-1] x 16 B;
-// stats: [token][group] x {B01, B2, 2^-S, sum X}; sct / zct: the slice's scales / zeros,
+// stats: [token][group] x {D0, D1, D2, D3, 2^-S, sum X, -, -}; sct / zct: the slice's scales / zeros,
 // [16 T rows][n_groups] x 2 B (rows past the slice are never written: only lanes whose results
 // are dropped read them); red: [wave][tile][lane] fp32 partial sums.
 struct I8Lds {
@@ -68,12 +69,26 @@ __host__ __device__ inline I8Lds i8_lds(int M, int n128, int n_groups, int T, bo
     I8Lds L;
     L.a = 0;
     L.stats = static_cast<uint32_t>(n128) * 2u * 4u * 4u * M * 16u;
-    L.sct = L.stats + static_cast<uint32_t>(M) * n128 * 16u;
+    L.sct = L.stats + static_cast<uint32_t>(M) * n128 * 32u;
     const uint32_t table = align16(16u * T * n_groups * 2u);
     L.zct = L.sct + table;
     L.red = L.zct + (zp ? table : 0u);
     L.total = L.red + static_cast<uint32_t>(kI8Waves) * T * kWave * 4u;
     return L;
+}
+
+// 4x4 byte transpose: out[p] = byte p of w0, w1, w2, w3 (in that order, low to high).
+__device__ __forceinline__ void transpose4(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3,
+                                           uint32_t out[4]) {
+    // t0 = (w0.0, w1.0, w0.2, w1.2), t1 = (w0.1, w1.1, w0.3, w1.3), likewise t2, t3 of w2, w3
+    const uint32_t t0 = __builtin_amdgcn_perm(w1, w0, 0x06020400u);
+    const uint32_t t1 = __builtin_amdgcn_perm(w1, w0, 0x07030501u);
+    const uint32_t t2 = __builtin_amdgcn_perm(w3, w2, 0x06020400u);
+    const uint32_t t3 = __builtin_amdgcn_perm(w3, w2, 0x07030501u);
+    out[0] = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
+    out[1] = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
+    out[2] = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
+    out[3] = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
 }
 
 // GLU: the gate of the MLP fused into the epilogue ([Lab5 基础]: FFN(x) = W_down [SiLU(W_gate x)
@@ -259,35 +274,32 @@ __global__ void __launch_bounds__(kI8Threads) gemv_i8_kernel(
                 am = max(am, static_cast<uint32_t>(__shfl_xor(static_cast<int>(am), o, kWave)));
             const float amax = __uint_as_float(am << 16);
             const bool finite = am < 0x7F80u;
-            const int S = finite && amax > 0.0f ? 19 - ilogbf(amax) : 0;  // max|x| 2^S < 2^20
-            // digits of the columns 8j + e. v = x 2^S + 13631488 (= 2^23 + 2^22 + 2^20) lies in
-            // [2^23, 2^24), so the fp32 add rounds x 2^S to the nearest integer X (ties to
-            // even) and the low 23 bits of v hold X + 2^22 + 2^20: bits 0..6 are b0 = X mod 128,
-            // bits 7..13 are b1 = floor(X / 128) mod 128, bits 14..20 are b2 =
-            // floor(X / 16384) + 64. (Non-finite groups give junk digits; their scale 2^-S is
-            // NaN, so their rows come out NaN.) The lo operand bytes are the columns
-            // 8j + {0,2,4,6}, the hi ones 8j + {1,3,5,7}.
-            uint32_t dlo[3] = {0u, 0u, 0u}, dhi[3] = {0u, 0u, 0u};
+            const int S = finite && amax > 0.0f ? 29 - ilogbf(amax) : 0;  // max|x| 2^S < 2^30
+            // X_e = rint(x_e 2^S) (|X_e| < 2^30); its digits are the bytes of
+            // (X_e + 0x80808080) ^ 0x80808080. (A non-finite group gives junk digits; its scale
+            // 2^-S is NaN, so its rows come out NaN.)
+            uint32_t D[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const uint32_t bits = (e & 1) ? (u[e >> 1] & 0xFFFF0000u) : (u[e >> 1] << 16);
-                const uint32_t v =
-                    __float_as_uint(ldexpf(__uint_as_float(bits), S) + 13631488.0f);
-                const int sh = 8 * (e >> 1);
-                uint32_t *dd = (e & 1) ? dhi : dlo;
-                dd[0] |= (v & 127u) << sh;
-                dd[1] |= ((v >> 7) & 127u) << sh;
-                dd[2] |= ((v >> 14) & 127u) << sh;
+                const int X = static_cast<int>(__builtin_rintf(ldexpf(__uint_as_float(bits), S)));
+                D[e] = (static_cast<uint32_t>(X) + 0x80808080u) ^ 0x80808080u;
             }
-            const uint32_t ones = 0x01010101u;
-            int b01 = static_cast<int>(__builtin_amdgcn_udot4(dlo[0], ones, __builtin_amdgcn_udot4(dhi[0], ones, 0u, false), false)) +
-                      128 * static_cast<int>(__builtin_amdgcn_udot4(dlo[1], ones, __builtin_amdgcn_udot4(dhi[1], ones, 0u, false), false));
-            int b2 = static_cast<int>(__builtin_amdgcn_udot4(dlo[2], ones, __builtin_amdgcn_udot4(dhi[2], ones, 0u, false), false)) - 8 * 64;
+            // the lo operand bytes are the columns 8j + {0,2,4,6}, the hi ones 8j + {1,3,5,7}
+            uint32_t dlo[4], dhi[4];
+            transpose4(D[0], D[2], D[4], D[6], dlo);
+            transpose4(D[1], D[3], D[5], D[7], dhi);
+            const int ones = 0x01010101;
+            int ds[4];
 #pragma unroll
-            for (int o = 1; o < 16; o <<= 1) {
-                b01 += __shfl_xor(b01, o, kWave);
-                b2 += __shfl_xor(b2, o, kWave);
-            }
+            for (int pl = 0; pl < 4; ++pl)
+                ds[pl] = __builtin_amdgcn_sdot4(
+                    static_cast<int>(dlo[pl]), ones,
+                    __builtin_amdgcn_sdot4(static_cast<int>(dhi[pl]), ones, 0, false), false);
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1)
+#pragma unroll
+                for (int pl = 0; pl < 4; ++pl) ds[pl] += __shfl_xor(ds[pl], o, kWave);
             // lane (n, q) of B holds columns 32q .. 32q+31 of the group, bytes 4i .. 4i+3 of an
             // operand being columns 32q + 8i + 2b (+1): here q = j / 4, i = j % 4
             const int kq = j >> 2, ki = j & 3;
@@ -295,31 +307,32 @@ __global__ void __launch_bounds__(kI8Threads) gemv_i8_kernel(
             const int lo0 = (((G * 2 + 0) * 4 + kq) * 4 * M + 4 * t) * 4 + ki;  // in dwords
             const int hi0 = (((G * 2 + 1) * 4 + kq) * 4 * M + 4 * t) * 4 + ki;
 #pragma unroll
-            for (int d = 0; d < 3; ++d) {
-                ab[lo0 + 4 * d] = dlo[d];
-                ab[hi0 + 4 * d] = dhi[d];
+            for (int pl = 0; pl < 4; ++pl) {
+                ab[lo0 + 4 * pl] = dlo[pl];
+                ab[hi0 + 4 * pl] = dhi[pl];
             }
-            ab[lo0 + 12] = ones;
-            ab[hi0 + 12] = ones;
             if (j == 0) {
                 const float gsc = finite ? ldexpf(1.0f, -S) : __builtin_nanf("");
-                const float sx = static_cast<float>(b01) + 16384.0f * static_cast<float>(b2);
-                i32x4_t st = {b01, b2, __float_as_int(gsc), __float_as_int(sx)};
-                *reinterpret_cast<i32x4_t *>(lds + L.stats + (t * n128 + G) * 16) = st;
+                const float sx = static_cast<float>(ds[0]) + 256.0f * static_cast<float>(ds[1]) +
+                                 65536.0f * static_cast<float>(ds[2]) +
+                                 16777216.0f * static_cast<float>(ds[3]);
+                i32x4_t *sp = reinterpret_cast<i32x4_t *>(lds + L.stats + (t * n128 + G) * 32);
+                sp[0] = i32x4_t{ds[0], ds[1], ds[2], ds[3]};
+                sp[1] = i32x4_t{__float_as_int(gsc), __float_as_int(sx), 0, 0};
             }
         }
     }
     __syncthreads();
 
     // ---- the units ----
-    // Lane (n, q) of the result holds D rows 4q .. 4q+3 of column n: token q's digit sums and
-    // code sum of row n. A rows >= 4M feed only D rows that are never read, so their lanes read
-    // any row (their own row modulo 4M), and lanes of tokens >= M read token 0's statistics
-    // (their results are never stored).
+    // Lane (n, q) of the result holds D rows 4q .. 4q+3 of column n: token q's four digit-plane
+    // sums of row n. A rows >= 4M feed only D rows that are never read, so their lanes read any
+    // row (their own row modulo 4M), and lanes of tokens >= M read token 0's statistics (their
+    // results are never stored).
     const uint32_t a_group = 2u * 4u * 4u * M * 16u;
     const uint32_t a_hi = 4u * 4u * M * 16u;
     const uint32_t a_lane = L.a + (static_cast<uint32_t>(q) * 4u * M + n % (4 * M)) * 16u;
-    const uint32_t s_lane = L.stats + static_cast<uint32_t>(q < M ? q : 0) * n128 * 16u;
+    const uint32_t s_lane = L.stats + static_cast<uint32_t>(q < M ? q : 0) * n128 * 32u;
     const uint32_t c_lane = static_cast<uint32_t>(n) * n_groups;  // table index of row n
     const i32x4_t zero4 = {0, 0, 0, 0};
     float acc = 0.0f;
@@ -328,8 +341,10 @@ __global__ void __launch_bounds__(kI8Threads) gemv_i8_kernel(
         const uint32_t ao = a_lane + static_cast<uint32_t>(G) * a_group;
         const i32x4_t alo = *reinterpret_cast<const i32x4_t *>(lds + ao);
         const i32x4_t ahi = *reinterpret_cast<const i32x4_t *>(lds + ao + a_hi);
+        const i32x4_t dsum =
+            *reinterpret_cast<const i32x4_t *>(lds + s_lane + static_cast<uint32_t>(G) * 32u);
         const i32x4_t st =
-            *reinterpret_cast<const i32x4_t *>(lds + s_lane + static_cast<uint32_t>(G) * 16u);
+            *reinterpret_cast<const i32x4_t *>(lds + s_lane + static_cast<uint32_t>(G) * 32u + 16u);
         const uint32_t ci = c_lane + static_cast<uint32_t>(16 * t * n_groups) +
                             (static_cast<uint32_t>(G) >> gshift);
         const uint32_t sbits = sct[ci];
@@ -349,11 +364,12 @@ __global__ void __launch_bounds__(kI8Threads) gemv_i8_kernel(
             zi = static_cast<int>(zf);
             zr = z - zf;
         }
-        const int i01 = d[0] + (d[1] << 7) - zi * st[0];
-        const int i2 = d[2] - (d[3] << 6) - zi * st[1];
-        float f = fmaf(16384.0f, static_cast<float>(i2), static_cast<float>(i01));
-        if (ZP) f = fmaf(-zr, __int_as_float(st[3]), f);
-        const float sc = bf16_to_f32(sbits) * __int_as_float(st[2]);
+        const int t0 = d[0] - zi * dsum[0], t1 = d[1] - zi * dsum[1];
+        const int t2 = d[2] - zi * dsum[2], t3 = d[3] - zi * dsum[3];
+        const int lo = t0 + (t1 << 8), hi = t2 + (t3 << 8);  // |T_p| <= 15 * 128 * 128: exact
+        float f = fmaf(65536.0f, static_cast<float>(hi), static_cast<float>(lo));
+        if (ZP) f = fmaf(-zr, __int_as_float(st[1]), f);
+        const float sc = bf16_to_f32(sbits) * __int_as_float(st[0]);
         acc = t != at ? 0.0f : acc;
         at = t;
         acc = fmaf(sc, f, acc);
@@ -420,15 +436,8 @@ __global__ void __launch_bounds__(kI8Threads) gemv_i8_kernel(
 }
 
 // Workgroups per CU: two for short rows; one for long rows, whose per-block activation
-// preparation grows with the row (W4_I8_BLOCKS_PER_CU, read once, overrides it for tuning).
-int i8_blocks_per_cu(int64_t n128) {
-    static const int forced = [] {
-        const char *e = getenv("W4_I8_BLOCKS_PER_CU");
-        return e ? atoi(e) : 0;
-    }();
-    if (forced > 0) return forced;
-    return n128 <= 32 ? 2 : 1;
-}
+// preparation grows with the row.
+int i8_blocks_per_cu(int64_t n128) { return n128 <= 32 ? 2 : 1; }
 
 struct I8Plan {
     int blocks, rows_per_block, T;
@@ -475,17 +484,20 @@ hipError_t launch_i8_t(const uint16_t *x, int64_t ldx, const uint8_t *qweight,
 
 }  // namespace
 
-// Which decode kernel serves a call: W4_GEMV_PATH, read on every call, is "i8" (the int8
-// matrix-core kernel wherever it applies), "stream" (never it) or unset (automatic: the int8
-// kernel for one token on shapes where it measured faster, at least 32 rows per compute unit
-// and rows of at most 32 groups of 128 columns).
-int gemv_path_override() {
-    const char *e = getenv("W4_GEMV_PATH");
-    if (!e) return 0;
-    if (e[0] == 'i') return 1;
-    if (e[0] == 's') return -1;
-    return 0;
-}
+// Which decode kernel serves a call. The library chooses by shape: the int8 kernel for one
+// token on shapes where it measured faster -- at least 32 rows per compute unit and rows of at
+// most 32 groups of 128 columns. A build with W4_TEST_HOOKS defined (the test library, never the
+// product one) also exports w4_test_force_decode_path, so that the tests can run each kernel on
+// shapes the choice gives to another: 1 = the int8 kernel wherever it applies, 2 = never it,
+// 0 = the library's choice.
+#ifdef W4_TEST_HOOKS
+namespace {
+int g_forced_path = 0;
+}  // namespace
+int gemv_path_override() { return g_forced_path == 1 ? 1 : (g_forced_path == 2 ? -1 : 0); }
+#else
+int gemv_path_override() { return 0; }
+#endif
 
 bool gemv_i8_preferred(int64_t M, int64_t d_out, int64_t k_pad) {
     const int path = gemv_path_override();
@@ -553,3 +565,11 @@ hipError_t launch_gemv_i8(const uint16_t *x, int64_t M, int64_t ldx, const uint8
 }
 
 }  // namespace w4
+
+#ifdef W4_TEST_HOOKS
+extern "C" int w4_test_force_decode_path(int path) {
+    if (path < 0 || path > 2) return 5;  // W4_ERR_RANGE
+    w4::g_forced_path = path;
+    return 0;
+}
+#endif

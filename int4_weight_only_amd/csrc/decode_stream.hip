@@ -778,14 +778,8 @@ int pick_steps(int64_t cpr) {
     return 0;
 }
 
-// Workgroups per CU of the persistent grid (measured defaults; W4_STREAM_BLOCKS_PER_CU, read once,
-// overrides them for tuning on other parts).
+// Workgroups per CU of the persistent grid (measured on MI355X).
 int stream_blocks_per_cu(int T, int seg, int64_t d_out) {
-    static const int forced = [] {
-        const char *e = getenv("W4_STREAM_BLOCKS_PER_CU");
-        return e ? atoi(e) : 0;
-    }();
-    if (forced > 0) return forced;
     if (seg > 1) return 1;
     if (T > 2) return 2;
     return d_out >= 32 * (int64_t)device_cu_count() ? 4 : 3;  // fewer rows: fewer workgroups

@@ -1,9 +1,15 @@
 """Helpers shared by the GPU parity tests: host <-> device conversion of bf16 bit patterns and
 the parity bar.  No quantization arithmetic lives here."""
+import contextlib
+import os
+
 import numpy as np
 import torch
 
+import int4_weight_only_amd as w4
 import oracle
+
+HOOKS_LIB = os.path.join(os.path.dirname(w4.__file__), "libw4_hooks.so")
 
 REL_TOL = 2e-3  # |y - y_ref| <= REL_TOL * (1 + |y_ref|) on fp32 outputs
 
@@ -48,3 +54,18 @@ def assert_bf16_is_rne_of_f32(y_bf16, y_f32, what=""):
     want = oracle.f32_to_bf16(np.asarray(y_f32, dtype=np.float32))
     got = host_bits(y_bf16)
     assert np.array_equal(got, want), f"{what}: bf16 output is not RNE(fp32 output)"
+
+
+@contextlib.contextmanager
+def forced_decode_path(path):
+    """Run the library's test build (libw4_hooks.so: the same kernels, plus a hook on the decode
+    kernel choice) with the choice forced: "i8" = the int8 matrix-core kernel wherever it applies,
+    "stream" = never it, None = the library's own choice."""
+    code = {None: 0, "i8": 1, "stream": 2}[path]
+    prev = w4._select_library(HOOKS_LIB)
+    try:
+        assert w4._lib.w4_test_force_decode_path(code) == 0
+        yield
+    finally:
+        w4._lib.w4_test_force_decode_path(0)
+        w4._select_library(prev)

@@ -63,6 +63,26 @@ def test_every_declared_symbol_is_exported(lib):
         assert hasattr(lib, name), name
 
 
+def test_test_hook_only_in_the_test_build(lib):
+    """The kernel-choice hook exists only in libw4_hooks.so (the tests' build); the product
+    library has no runtime switch of any kind."""
+    assert not hasattr(lib, "w4_test_force_decode_path")
+    hooks = os.path.join(ROOT, "int4_weight_only_amd", "libw4_hooks.so")
+    h = ctypes.CDLL(hooks)
+    assert hasattr(h, "w4_test_force_decode_path")
+    for name in declared_functions():
+        assert hasattr(h, name), name
+    h.w4_test_force_decode_path.argtypes = [ctypes.c_int]
+    assert h.w4_test_force_decode_path(3) == W4_ERR_RANGE
+    assert h.w4_test_force_decode_path(0) == W4_OK
+
+
+def test_library_sources_read_no_environment():
+    csrc = os.path.join(ROOT, "int4_weight_only_amd", "csrc")
+    for f in os.listdir(csrc):
+        assert "getenv" not in open(os.path.join(csrc, f)).read(), f
+
+
 def test_status_strings(lib):
     for s in range(8):
         assert lib.w4_status_string(s)
@@ -185,6 +205,18 @@ def test_w4a8_rejects_bad_arguments(lib):
     assert call(acc=E + 2) == W4_ERR_ALIGN
     big = (1 << 20) + 16
     assert call(d_in=big, ldq=big) == W4_ERR_RANGE
+    # the decode kernels' limit: d_in <= W4_DECODE_MAX_D_IN = 65536 (w4a8_gemm serves up to 2^20)
+    assert call(d_in=65552, ldq=65552) == W4_ERR_RANGE
+    assert call(d_in=65536, ldq=65536, q=None) == W4_ERR_NULL  # in range: fails only on the NULL
+
+
+def test_header_states_the_decode_limit():
+    text = open(HEADER).read()
+    assert re.search(r"#define W4_DECODE_MAX_D_IN \(\(int64_t\)1 << 16\)", text)
+    for fn in ("w4_gemv", "w4a8_gemv", "w4a8_linear", "w4_gemv_glu"):
+        block = text[text.index(f" * {fn} --"):]
+        block = block[:block.index("void *stream);")]
+        assert "W4_DECODE_MAX_D_IN" in block, fn
 
 
 def test_gptq_rejects_bad_arguments(lib):
@@ -312,6 +344,7 @@ def test_w4a8_linear_rejects_bad_arguments(lib):
     assert call(out=2) == W4_ERR_UNSUPPORTED
     big = (1 << 20) + 16
     assert call(d_in=big, ldx=big) == W4_ERR_RANGE
+    assert call(d_in=65552, ldx=65552) == W4_ERR_RANGE  # W4_DECODE_MAX_D_IN
     # rows longer than the fused kernel's activation stage: the two-call path serves them
     assert call(d_in=60000, ldx=60000) == W4_ERR_UNSUPPORTED
 
