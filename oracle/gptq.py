@@ -59,22 +59,45 @@ def inverse_factor(h):
 
 def _code(w_col, s_bits, z_bits, mode):
     """O1's code decision for one column, in fp32 operations (a zero scale gives the zero code,
-    which O1 stores as 8 for symmetric and 0 for asymmetric groups)."""
+    which O1 stores as 8 for symmetric and 0 for asymmetric groups). Also returns the value
+    before rounding, v = w / s + z (fp32), whose distance to the nearest half-integer says how
+    close the decision was."""
     s = bf16_to_f32(s_bits)
     z = bf16_to_f32(z_bits) if mode == ASYM else np.full(s.shape, 8.0, np.float32)
     v = np.asarray(w_col).astype(np.float32)
     nz = s != 0.0
     t = np.divide(v, s, out=np.zeros_like(v), where=nz)
     t = t + z
+    pre = t.copy()
     t = np.clip(np.rint(t), 0.0, 15.0)
     code = np.where(nz, t, z).astype(np.uint8)
-    return code, s.astype(np.float64), z.astype(np.float64)
+    return code, s.astype(np.float64), z.astype(np.float64), pre
+
+
+def _group_stats(block, span, s_bits, mode):
+    """The fp32 values that O1's scale and zero decisions round (the same fp32 operations, on the
+    group padded with zeros): symmetric max|w| / 7; asymmetric (max - min) / 15 and -min / s with
+    the stored bf16 s. Diagnostics only: they say how close each decision was to a rounding tie."""
+    blk = np.zeros((block.shape[0], span), dtype=np.float32)
+    blk[:, :block.shape[1]] = block
+    if mode == SYM:
+        s32 = np.max(np.abs(blk), axis=1).astype(np.float32) / np.float32(7.0)
+        return s32, np.zeros_like(s32)
+    mx = np.max(blk, axis=1).astype(np.float32)
+    mn = np.min(blk, axis=1).astype(np.float32)
+    s32 = (mx - mn) / np.float32(15.0)
+    s = bf16_to_f32(s_bits)
+    zp = np.divide(-mn, s, out=np.zeros_like(mn), where=s != 0.0)
+    return s32.astype(np.float32), zp.astype(np.float32)
 
 
 def gptq(w, x_bits, group_size, mode, alpha=0.01, d_in=None):
     """GPTQ of an fp32 weight [d_out][d_in] with bf16 calibration activations [N][>= d_in].
     Returns dict(qweight, scales, zeros (None for SYM), L_pred, H (damped), U, lam, dead,
-    w (the weight after the dead-column step), codes [d_out][k_pad])."""
+    w (the weight after the dead-column step), codes [d_out][k_pad], v [d_out][d_in]: each
+    column's value w / s + z before rounding, fp32; s_pre, z_pre [d_out][n_groups]: each group's
+    fp32 scale before its bf16 rounding and (asymmetric) -min / s before its rounding to an
+    integer -- O1's statistics of the updated weights at the group's first column)."""
     w = np.asarray(w, dtype=np.float32)
     d_out = w.shape[0]
     d_in = w.shape[1] if d_in is None else d_in
@@ -84,6 +107,9 @@ def gptq(w, x_bits, group_size, mode, alpha=0.01, d_in=None):
     kp, ng = k_pad(d_in, group_size), n_groups(d_in, group_size)
     span = kp // ng
     codes = np.zeros((d_out, kp), dtype=np.uint8)
+    vpre = np.zeros((d_out, d_in), dtype=np.float32)
+    s_pre = np.zeros((d_out, ng), dtype=np.float32)
+    z_pre = np.zeros((d_out, ng), dtype=np.float32)
     scales = np.zeros((d_out, ng), dtype=np.uint16)
     zeros = np.zeros((d_out, ng), dtype=np.uint16) if mode == ASYM else None
     L = 0.0
@@ -98,7 +124,8 @@ def gptq(w, x_bits, group_size, mode, alpha=0.01, d_in=None):
             scales[:, G] = s_bits
             if mode == ASYM:
                 zeros[:, G] = z_bits
-        code, s, z = _code(W[:, i], s_bits, z_bits, mode)
+            s_pre[:, G], z_pre[:, G] = _group_stats(block, span, s_bits, mode)
+        code, s, z, vpre[:, i] = _code(W[:, i], s_bits, z_bits, mode)
         q = s * (code.astype(np.float64) - z)
         codes[:, i] = code
         err = W[:, i] - q
@@ -109,12 +136,12 @@ def gptq(w, x_bits, group_size, mode, alpha=0.01, d_in=None):
     for G in range(ng):
         lo, hi = max(G * span, d_in), (G + 1) * span
         if lo < hi:
-            zc, _, _ = _code(np.zeros(d_out), scales[:, G], zeros[:, G] if mode == ASYM else None,
-                             mode)
+            zc, _, _, _ = _code(np.zeros(d_out), scales[:, G],
+                                zeros[:, G] if mode == ASYM else None, mode)
             codes[:, lo:hi] = zc[:, None]
     qweight = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
     return dict(qweight=qweight, scales=scales, zeros=zeros, L_pred=L, H=h, U=U, lam=lam,
-                dead=dead, w=W0, codes=codes)
+                dead=dead, w=W0, codes=codes, v=vpre, s_pre=s_pre, z_pre=z_pre)
 
 
 __all__ = ["hessian", "prepare", "inverse_factor", "gptq", "SYM", "ASYM"]

@@ -751,3 +751,24 @@ def test_gptq_dead_column():
     d = w0 - q
     obj = np.sum((x @ d.T) ** 2) / N + 0.5 * lam * np.sum(d * d) + 0.5 * np.sum(d[:, [5, 40]] ** 2)
     assert r["L_pred"] == pytest.approx(obj, rel=1e-8)
+
+
+@pytest.mark.parametrize("g,mode", [(32, SYM), (128, ASYM), (0, SYM), (64, ASYM)])
+def test_gptq_exported_decision_values_round_to_its_result(g, mode):
+    """O9's diagnostic exports are the values its decisions round: every code is
+    clip(rint(v), 0, 15) of the exported pre-rounding value (nonzero scales), every stored scale
+    is the bf16 rounding of the exported fp32 scale, every stored zero point the integer nearest
+    the exported -min / s. A ragged last group (136 columns) is included."""
+    d_out, d_in = 48, 136
+    w = workloads.weight(77, g + mode, d_out, d_in)
+    xb = _calib(9, 96, d_in)
+    r = gq.gptq(w, xb, g, mode)
+    kp = oracle.k_pad(d_in, g)
+    span = kp // oracle.n_groups(d_in, g)
+    s = oracle.bf16_to_f32(r["scales"])[:, np.arange(d_in) // span]
+    nz = s != 0.0
+    dec = np.clip(np.rint(r["v"]), 0, 15)
+    assert np.array_equal(dec[nz], r["codes"][:, :d_in][nz])
+    assert np.array_equal(oracle.f32_to_bf16(r["s_pre"]), r["scales"])
+    if mode == ASYM:
+        assert np.array_equal(np.rint(r["z_pre"]), oracle.bf16_to_f32(r["zeros"]))
