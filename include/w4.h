@@ -16,7 +16,8 @@
  *     frees or retains device memory and keeps no state between calls (thread-safe; calls on one
  *     stream are ordered by that stream).  The linear layers and the codecs need no scratch
  *     memory (partial sums meet in LDS); GPTQ's factor and column loop take caller-owned work
- *     buffers.
+ *     buffers.  The one exception is w4_gptq_quantize_noalloc, for callers that cannot
+ *     allocate: it keeps its work buffer in a device array of the library (see there).
  *   - bf16 values travel as uint16_t bit patterns.  `stream` is a hipStream_t passed as void*
  *     (NULL = the default stream).  Calls enqueue kernels and return without synchronizing.
  *   - Arguments are validated on the host before anything is enqueued.  A failed check returns
@@ -133,6 +134,21 @@ int w4_gptq_quantize(float *w, int64_t d_out, int64_t d_in, int64_t ldw, const f
                      const uint8_t *dead, int group_size, int mode, uint8_t *qweight,
                      uint16_t *scales, uint16_t *zeros, float *work, float *row_loss,
                      void *stream);
+
+/*
+ * w4_gptq_quantize_noalloc -- w4_gptq_quantize without the `work` argument, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). The block errors live in a device array of the library,
+ * W4_GPTQ_NOALLOC_MAX_ROWS rows of 32 floats (8 MiB), which each GPU holds from the first call on
+ * it until the process ends. Every call on one GPU shares that array: calls that overlap on one
+ * GPU (other streams, other host threads) race and give unspecified results; serialize them.
+ * The call allocates nothing. d_out > W4_GPTQ_NOALLOC_MAX_ROWS returns W4_ERR_RANGE; every other
+ * argument and result is that of w4_gptq_quantize.
+ */
+#define W4_GPTQ_NOALLOC_MAX_ROWS ((int64_t)1 << 16)
+int w4_gptq_quantize_noalloc(float *w, int64_t d_out, int64_t d_in, int64_t ldw, const float *u,
+                             const uint8_t *dead, int group_size, int mode, uint8_t *qweight,
+                             uint16_t *scales, uint16_t *zeros, float *row_loss, void *stream);
 
 /*
  * w4_qat_repack -- pack a weight trained on the 4-bit grid (a QAT export stored in bf16) without

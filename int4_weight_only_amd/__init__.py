@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "W4_SYM", "W4_ASYM", "W4_OUT_BF16", "W4_OUT_F32", "W4Error", "packed_layout", "w4_pack",
     "w4_gemv", "w4_gemv_glu", "w4_gemm", "act_quant_int8", "w4a8_gemv", "w4a8_gemm", "w4a8_linear",
-    "w4_qat_repack", "gptq_hessian", "gptq_factor", "gptq_quantize", "gptq",
+    "w4_qat_repack", "gptq_hessian", "gptq_factor", "gptq_quantize", "gptq_quantize_noalloc",
+    "gptq",
     "w4_linear",
     "library_path",
 ]
@@ -50,6 +51,7 @@ def _load(path):
     lib.w4_gptq_hessian.argtypes = [p, i64, i64, i64, p, p]
     lib.w4_gptq_factor.argtypes = [p, i64, ctypes.c_float, p, p, p, p]
     lib.w4_gptq_quantize.argtypes = [p, i64, i64, i64, p, p, i32, i32, p, p, p, p, p, p]
+    lib.w4_gptq_quantize_noalloc.argtypes = [p, i64, i64, i64, p, p, i32, i32, p, p, p, p, p]
     lin = [p, i64, i64, p, p, p, p, i64, i64, i32, p, i64, i32]
     lib.w4_gemv.argtypes = lin + [p]
     lib.w4_gemv_glu.argtypes = lin + [p]
@@ -59,7 +61,7 @@ def _load(path):
     lib.w4a8_gemm.argtypes = lib.w4a8_gemv.argtypes
     lib.w4a8_linear.argtypes = [p, i64, i64, p, p, p, i64, i64, p, i64, i32, p, p, p]
     for f in ("w4_packed_layout", "w4_pack", "w4_qat_repack", "w4_gptq_hessian", "w4_gptq_factor",
-              "w4_gptq_quantize", "w4_gemv", "w4_gemv_glu", "w4_gemm",
+              "w4_gptq_quantize", "w4_gptq_quantize_noalloc", "w4_gemv", "w4_gemv_glu", "w4_gemm",
               "act_quant_int8", "w4a8_gemv", "w4a8_gemm", "w4a8_linear"):
         getattr(lib, f).restype = i32
     lib.w4_status_string.argtypes = [i32]
@@ -222,6 +224,44 @@ def gptq_quantize(w, u, dead, group_size, mode, d_in=None):
     _check("w4_gptq_quantize", _lib.w4_gptq_quantize(
         _ptr(w), d_out, d_in, w.stride(0), _ptr(u), _ptr(dead), group_size, mode, _ptr(qweight),
         _ptr(scales), _ptr(zeros), _ptr(work), _ptr(row_loss), _stream(dev)))
+    return qweight, scales, zeros, row_loss
+
+
+def gptq_quantize_noalloc(w, u, dead, group_size, mode, d_in=None, row_loss=None, out=None):
+    """gptq_quantize for callers that cannot allocate: the block errors live in the library's own
+    device array (calls that overlap on one GPU race), and the outputs are the caller's
+    out=(qweight, scales, zeros or None) and row_loss (nothing is allocated here either when
+    they are given).  Returns (qweight, scales, zeros or None, row_loss or None)."""
+    _need(w, "w", torch.float32, dim=2)
+    dev = w.device
+    _need(u, "u", torch.float32, dev, 2)
+    if dead is not None:
+        _need(dead, "dead", torch.uint8, dev, 1)
+    d_out, ldw = w.shape
+    d_in = ldw if d_in is None else d_in
+    if tuple(u.shape) != (d_in, d_in) or not u.is_contiguous():
+        raise ValueError(f"u must be contiguous [{d_in}][{d_in}]")
+    k_pad, n_groups, _ = packed_layout(d_out, d_in, group_size)
+    if out is None:
+        qweight = torch.empty((d_out, k_pad // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((d_out, n_groups), dtype=torch.bfloat16, device=dev)
+        zeros = torch.empty_like(scales) if mode == W4_ASYM else None
+    else:
+        qweight, scales, zeros = out
+        _need(qweight, "qweight", torch.uint8, dev, 2)
+        _need(scales, "scales", torch.bfloat16, dev, 2)
+        if tuple(qweight.shape) != (d_out, k_pad // 2) or not qweight.is_contiguous():
+            raise ValueError(f"qweight must be contiguous [{d_out}][{k_pad // 2}]")
+        for name, t in (("scales", scales), ("zeros", zeros)):
+            if t is not None and (tuple(t.shape) != (d_out, n_groups) or not t.is_contiguous()):
+                raise ValueError(f"{name} must be contiguous [{d_out}][{n_groups}]")
+    if row_loss is not None:
+        _need(row_loss, "row_loss", torch.float32, dev, 1)
+        if row_loss.shape[0] < d_out:
+            raise ValueError(f"row_loss must hold {d_out} values")
+    _check("w4_gptq_quantize_noalloc", _lib.w4_gptq_quantize_noalloc(
+        _ptr(w), d_out, d_in, w.stride(0), _ptr(u), _ptr(dead), group_size, mode, _ptr(qweight),
+        _ptr(scales), _ptr(zeros), _ptr(row_loss), _stream(dev)))
     return qweight, scales, zeros, row_loss
 
 

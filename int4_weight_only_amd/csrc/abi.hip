@@ -157,6 +157,31 @@ int w4_gptq_quantize(float *w, int64_t d_out, int64_t d_in, int64_t ldw, const f
     return err == hipSuccess ? W4_OK : hip_fail(err);
 }
 
+int w4_gptq_quantize_noalloc(float *w, int64_t d_out, int64_t d_in, int64_t ldw, const float *u,
+                             const uint8_t *dead, int group_size, int mode, uint8_t *qweight,
+                             uint16_t *scales, uint16_t *zeros, float *row_loss, void *stream) {
+    if (!w || !u || !qweight || !scales) return W4_ERR_NULL;
+    if (mode != W4_SYM && mode != W4_ASYM) return W4_ERR_UNSUPPORTED;
+    if ((mode == W4_ASYM) != (zeros != nullptr)) return W4_ERR_NULL;
+    if (int st = check_dims(d_out, d_in)) return st;
+    if (ldw < d_in) return W4_ERR_SHAPE;
+    if (d_in > W4_MAX_GPTQ_D_IN || ldw > W4_MAX_DIM || d_out > W4_GPTQ_NOALLOC_MAX_ROWS)
+        return W4_ERR_RANGE;
+    if (!valid_group(group_size)) return W4_ERR_GROUP;
+    if (!aligned(w, 4) || !aligned(u, 4) || !aligned(qweight, 4) || !aligned(scales, 2) ||
+        (zeros && !aligned(zeros, 2)) || (row_loss && !aligned(row_loss, 4)))
+        return W4_ERR_ALIGN;
+    static_assert(W4_GPTQ_NOALLOC_MAX_ROWS == w4::kGqScratchRows, "the scratch array's rows");
+    float *ebuf = nullptr;
+    hipError_t err = w4::gptq_scratch(&ebuf);
+    if (err != hipSuccess) return hip_fail(err);
+    const Layout L = layout_of(d_in, group_size);
+    err = w4::launch_gptq_quantize(w, d_out, d_in, ldw, u, dead, L.span, mode, qweight, scales,
+                                   zeros, L.n_groups, L.k_pad, ebuf, row_loss,
+                                   static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? W4_OK : hip_fail(err);
+}
+
 int w4_qat_repack(const uint16_t *w, int64_t d_out, int64_t d_in, int64_t ldw, uint8_t *qweight,
                   uint16_t *scales, uint8_t *m_out, void *stream) {
     if (!w || !qweight || !scales) return W4_ERR_NULL;

@@ -24,8 +24,37 @@
 #include "w4_launch.h"
 
 #include <algorithm>
+#include <mutex>
+#include <vector>
 
 namespace w4 {
+
+// The column loop's block errors for callers that cannot allocate (w4_gptq_quantize_noalloc):
+// a file-scope device array, kGqScratchRows rows of 32 floats (8 MiB). Each GPU the library
+// runs on holds its own copy until the process ends; every call on one GPU shares it, so calls
+// that overlap on one GPU race. Nothing in it needs clearing: the block kernel writes every entry
+// of the rows in use before the trailing update reads it. Host code never passes the array's
+// name to a kernel (that is a host-side stand-in): it passes the device address from
+// hipGetSymbolAddress, looked up once per device.
+static __device__ __align__(256) float scratch[kGqScratchRows * 32];
+
+hipError_t gptq_scratch(float **ptr) {
+    static std::mutex mu;
+    static std::vector<float *> by_device;
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess) return err;
+    std::lock_guard<std::mutex> lock(mu);
+    if (dev >= static_cast<int>(by_device.size())) by_device.resize(dev + 1, nullptr);
+    if (by_device[dev] == nullptr) {
+        void *p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (err != hipSuccess) return err;
+        by_device[dev] = static_cast<float *>(p);
+    }
+    *ptr = by_device[dev];
+    return hipSuccess;
+}
 
 namespace {
 

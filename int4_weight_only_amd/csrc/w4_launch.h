@@ -37,6 +37,10 @@ hipError_t launch_gptq_hessian(const uint16_t *x, int64_t N, int64_t d_in, int64
                                hipStream_t stream);
 hipError_t launch_gptq_factor(float *h, int64_t d_in, float alpha, float *u, float *v,
                               uint8_t *dead, hipStream_t stream);
+// The device address of this GPU's block-error array for w4_gptq_quantize_noalloc
+// (kGqScratchRows rows of 32 floats).
+constexpr int64_t kGqScratchRows = int64_t(1) << 16;
+hipError_t gptq_scratch(float **ptr);
 hipError_t launch_gptq_quantize(float *w, int64_t d_out, int64_t d_in, int64_t ldw,
                                 const float *u, const uint8_t *dead, int64_t span, int mode,
                                 uint8_t *qweight, uint16_t *scales, uint16_t *zeros,
