@@ -17,15 +17,26 @@
 // (A zero point that is not an integer of magnitude <= 240 -- never produced by w4_pack -- makes w
 // a rounded fp32 value and the split keeps its top 16 significant bits.)
 //
-// Tiling: 256 threads (4 waves, 2 x 2); block tile BM tokens x 128 output channels; K step 32
-// (one MFMA deep; every 32-column step lies in one group).  Each wave owns (BM/2) x 64 outputs,
-// with the accumulators in VGPRs; two blocks share a compute unit.  Activations go from memory
-// straight into a ring of three LDS stages (buffer_load ... lds), two steps ahead of the matrix
-// work; packed weights go to registers, also two steps ahead, and are dequantized into one of
-// two LDS stages while the current step multiplies.  One barrier per step, without a memory
-// fence, so that loads stay in flight across it.  Blocks are numbered so that each XCD (blocks
-// are dealt to the 8 XCDs round-robin) works on consecutive output-channel tiles and shares
+// Tiling: 512 threads (8 waves, 2 x 4), one block per compute unit; block tile BM tokens x 256
+// output channels; K step 32 (one MFMA deep; every 32-column step lies in one group).  Each wave
+// owns (BM/2) x 64 outputs, with the accumulators in VGPRs.
+//
+// Everything a step reads from memory arrives by direct global->LDS loads (buffer_load ... lds),
+// so that no wave ever waits for a load in its registers:
+//   * activations: a ring of three stages, two steps ahead;
+//   * packed weights and their scales (and zero points): chunks of four steps (64 bytes of every
+//     weight row, four scales per row), double-buffered, one chunk ahead.
+// The cost that bounds such a kernel on this part is the number of distinct cache lines its loads
+// touch per step, not their bytes: a 256-row weight step touches 256 lines whichever way it is
+// loaded, a four-step chunk touches the same lines once for four steps, and the 256-channel tile
+// halves the activation lines per matrix instruction against a 128-channel tile.
+// Each step dequantizes the next step's weights from the chunk into one of two LDS stages of
+// exact hi/lo halves while the matrix cores work on the current one.  One barrier per step,
+// without a memory fence, so that loads stay in flight across it.  Blocks are numbered so that
+// each XCD (blocks are dealt to the 8 XCDs round-robin) works on consecutive tiles and shares
 // their weights in its L2.
+#include <type_traits>
+
 #include "w4_device.h"
 #include "w4_launch.h"
 
@@ -36,45 +47,50 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
-constexpr int BN = 128, BK = 32;
-constexpr int kThreads = 256;
+constexpr int BN = 256, BK = 32;
+constexpr int KC = 4;          // steps per weight chunk
+constexpr int kThreads = 512;  // 8 waves
 constexpr int kXcds = 8;
+constexpr int kPeriod = 24;    // lcm of the stage rings: 3 activation, 2 weight, 2 chunk (x 4 steps)
 
-// LDS rows are BK = 32 bf16 (64 bytes, four 16-byte chunks) with no padding; chunk c of row r is
-// stored at chunk position c ^ ((r >> 2) & 3).  The 16 rows read by one 16-lane phase of a
-// fragment load, and the 8 rows x 2 halves written by one phase of the tile stores, then fall
-// into 16 different 16-byte bank groups.
+// LDS layout of a [rows][BK = 32] bf16 tile: blocks of 16 rows (1 KiB), and inside a block the
+// 16-byte chunk c (columns 8c .. 8c + 7) of row r at slot 16 c + r, chunk-major.  The matrix-core
+// operand fragment of 16 rows x 32 columns (lane l: row l % 16, chunk l / 16) is then one
+// contiguous 1 KiB read, lane l at byte 16 l, which the LDS serves at its full rate; a row-major
+// tile (rows of 64 bytes), swizzled or not, serves the same fragment at half that rate.
 __device__ __forceinline__ int lds_at(int row, int chunk) {
-    return row * BK + ((chunk ^ ((row >> 2) & 3)) << 3);
+    return (row >> 4) * (16 * BK) + chunk * 128 + (row & 15) * 8;
 }
 
-// One direct global->LDS load: 16 bytes per lane from `off` within the descriptor (0 when out of
-// range) into LDS at `lds` + 16 * lane.
-__device__ __forceinline__ void load_lds16(rsrc_t r, uint16_t *lds, uint32_t off) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void *)lds, 16,
-                                             off, 0, 0, 0);
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+// Direct global->LDS loads: `bytes` (16: the 16 bytes at `off`; 2: the 16-bit value at `off`,
+// zero-extended to a dword) per lane from the descriptor (zeros when out of range) into LDS at
+// `lds` + bytes_per_slot * lane (16 or 4).
+__device__ __forceinline__ void load_lds16(rsrc_t r, void *lds, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, off, 0, 0, 0);
+}
+__device__ __forceinline__ void load_lds2(rsrc_t r, void *lds, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 2, off, 0, 0, 0);
 }
 
-// Block barrier without a memory fence.  The direct global->LDS loads of later steps stay in
-// flight across it (a fenced barrier would drain them); the caller's own LDS stores are
-// completed first (lgkmcnt(0)), and the loads of the stage read after the barrier have landed
-// because the vector-memory counter is in order: they were issued before the weight loads that
-// the caller has already waited for.  The empty asm statements keep the compiler from moving
-// memory accesses across the barrier.
+// s_waitcnt with lgkmcnt(0), expcnt(7) and vmcnt(N) (gfx9 encoding: vmcnt bits 3:0 and 15:14).
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4));
+}
+
+// Block barrier without a memory fence, after this wave's LDS stores (lgkmcnt(0)) and all but
+// its N most recent direct loads (vmcnt(N)) have completed.  The empty asm statements keep the
+// compiler from moving memory accesses across it.
+template <int N>
 __device__ __forceinline__ void stage_barrier() {
     asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited for
+    wait_vm_lgkm0<N>();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
-
-// Registers of one step's weight loads (one row x 16 codes per thread, with that row's raw
-// scale and zero point, converted only when stored so that nothing uses a load early), two steps
-// ahead.
-struct WLoad {
-    uint2 w;
-    uint16_t s_bits, z_bits;
-};
 
 // The fp32 weights s * (c - z) of the 4 codes held as bytes in `b`, split into bf16 hi and lo
 // halves; hi2/lo2 receive 2 dwords each (columns in byte order).
@@ -99,33 +115,44 @@ __device__ __forceinline__ void split4(uint32_t b, float s, float zs, uint32_t *
 }
 
 template <int BM, bool ZP>
-__global__ void __launch_bounds__(kThreads, 2) gemm_w4a16_kernel(
+__global__ void __launch_bounds__(kThreads, 1) gemm_w4a16_kernel(
     const uint16_t *__restrict__ x, int M, int64_t ldx, const uint8_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
     const uint16_t *__restrict__ bias, int d_out, int d_in, int64_t row_bytes,
     int steps_per_group, int n_groups, int n_steps, int tiles_m, int tiles_n,
     void *__restrict__ y, int64_t ldy, int out_f32) {
-    constexpr int WM = BM / 2;   // rows of a wave tile
-    constexpr int TM = WM / 16;  // 16-row MFMA tiles per wave
-    constexpr int XR = BM / 128; // x rows loaded per thread
-    // Shared memory: a ring of three activation stages (filled two steps ahead by direct
-    // global->LDS loads) and two stages of dequantized weight halves.  Every stage is an array of
-    // its own and the step loop is unrolled so that each access names its array: the compiler
-    // then sees that a direct load in flight does not touch the stage being read or written (it
-    // would otherwise wait for the load before every such access).
+    constexpr int WM = BM / 2;    // rows of a wave tile
+    constexpr int TM = WM / 16;   // 16-row MFMA tiles per wave
+    constexpr int XI = BM / 128;  // activation loads per wave per step (16 rows each)
+    constexpr int CI = ZP ? 6 : 4;  // chunk loads per wave per chunk (codes, scales, zeros: 2 each)
+    // Shared memory, every stage an array of its own: the step loop is unrolled over the period
+    // of all rings so that each access names its array, and the compiler then sees that a direct
+    // load in flight does not touch the stage being read or written (it would otherwise wait for
+    // the load before every such access).
     __shared__ __attribute__((aligned(16))) uint16_t sx0[BM * BK];
     __shared__ __attribute__((aligned(16))) uint16_t sx1[BM * BK];
     __shared__ __attribute__((aligned(16))) uint16_t sx2[BM * BK];
-    __shared__ __attribute__((aligned(16))) uint16_t shi[2][BN * BK];
-    __shared__ __attribute__((aligned(16))) uint16_t slo[2][BN * BK];
+    __shared__ __attribute__((aligned(16))) uint16_t shi0[BN * BK];
+    __shared__ __attribute__((aligned(16))) uint16_t shi1[BN * BK];
+    __shared__ __attribute__((aligned(16))) uint16_t slo0[BN * BK];
+    __shared__ __attribute__((aligned(16))) uint16_t slo1[BN * BK];
+    // weight chunk: 16 blocks of 16 rows; in block b the 16 bytes of row 16 b + r for step k of the
+    // chunk at byte 1024 b + 256 k + 16 r
+    __shared__ __attribute__((aligned(16))) uint8_t sq0[BN * KC * 16];
+    __shared__ __attribute__((aligned(16))) uint8_t sq1[BN * KC * 16];
+    // scale (zero point) bits of row 16 b + r for step k of the chunk in dword 64 b + 16 k + r
+    __shared__ __attribute__((aligned(16))) uint32_t ss0[BN * KC];
+    __shared__ __attribute__((aligned(16))) uint32_t ss1[BN * KC];
+    __shared__ __attribute__((aligned(16))) uint32_t sz0[ZP ? BN * KC : 1];
+    __shared__ __attribute__((aligned(16))) uint32_t sz1[ZP ? BN * KC : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int wm = wid >> 1, wn = wid & 1;
+    const int wm = wid >> 2, wn = wid & 3;
 
     // XCD-aware tile order: hardware block b runs on XCD b % 8; renumber so that the blocks of
-    // one XCD are consecutive tiles, M fastest (the tokens tiles of one weight tile together).
+    // one XCD are consecutive tiles, M fastest (the token tiles of one weight tile together).
     const int nblocks = tiles_m * tiles_n;
     const int b = static_cast<int>(blockIdx.x);
     int t = b;
@@ -133,20 +160,18 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_w4a16_kernel(
     const int tile_m = t % tiles_m, tile_n = t / tiles_m;
     const int m0 = tile_m * BM, n0 = tile_n * BN;
 
-    // Activations: direct global->LDS loads (buffer_load ... lds).  One instruction moves 16 rows
-    // x 64 bytes of a step: lane l lands in LDS slot l (row l / 4, chunk position l % 4), so it
-    // fetches the chunk that the swizzled layout keeps there.  Wave w owns rows
-    // [w * BM / 4, (w + 1) * BM / 4) of the tile, XS slabs of 16 rows, each with a descriptor that
-    // covers only the slab's rows below M: a row >= M, or a chunk starting at or beyond d_in, gets
-    // an offset outside it and lands as zeros.  (Rows >= M only feed outputs that are never
-    // stored; a chunk that straddles d_in is trimmed after it lands.)
-    constexpr int XS = BM / 64;
-    const int x_chunk = (lane & 3) ^ (lane >> 4);
-    const uint32_t x_row_off = static_cast<uint32_t>(lane >> 2) * static_cast<uint32_t>(ldx) * 2u;
-    rsrc_t x_rsrc[XS];
+    // Activations: one instruction moves 16 rows x 64 bytes of a step; lane l lands in LDS slot l
+    // of a 16-row block, so it fetches row l % 16, chunk l / 16.  Wave w owns rows
+    // [w * BM / 8, (w + 1) * BM / 8) of the tile, XI blocks of 16 rows, each with a descriptor
+    // that covers only the block's rows below M: a row >= M, or a chunk starting at or beyond
+    // d_in, gets an offset outside it and lands as zeros.  (Rows >= M only feed outputs that are
+    // never stored; a chunk that straddles d_in is trimmed after it lands.)
+    const int x_chunk = lane >> 4;
+    const uint32_t x_row_off = static_cast<uint32_t>(lane & 15) * static_cast<uint32_t>(ldx) * 2u;
+    rsrc_t x_rsrc[XI];
 #pragma unroll
-    for (int q = 0; q < XS; ++q) {
-        const int grow0 = m0 + wid * (BM / 4) + q * 16;
+    for (int q = 0; q < XI; ++q) {
+        const int grow0 = m0 + wid * (BM / 8) + q * 16;
         const int rows = grow0 < M ? (M - grow0 < 16 ? M - grow0 : 16) : 0;
         x_rsrc[q] = make_rsrc(rows > 0 ? x + static_cast<int64_t>(grow0) * ldx : x,
                               static_cast<uint32_t>(rows) * static_cast<uint32_t>(ldx) * 2u);
@@ -155,8 +180,8 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_w4a16_kernel(
         const int col = step * BK + 8 * x_chunk;
         const uint32_t off = col < d_in ? x_row_off + 2u * static_cast<uint32_t>(col) : kOutOfRange;
 #pragma unroll
-        for (int q = 0; q < XS; ++q)
-            load_lds16(x_rsrc[q], &stage[(wid * (BM / 4) + q * 16) * BK], off);
+        for (int q = 0; q < XI; ++q)
+            load_lds16(x_rsrc[q], &stage[(wid * (BM / 8) + q * 16) * BK], off);
     };
     // Zero the columns >= d_in of the chunk that straddles d_in (only when d_in % 8 != 0, in the
     // one step that holds it), after this wave's loads of that stage have landed.
@@ -170,8 +195,8 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_w4a16_kernel(
                 for (int e = 0; e < 4; ++e)
                     m[e] = 2 * e + 2 <= keep ? 0xFFFFFFFFu : (2 * e + 1 == keep ? 0x0000FFFFu : 0u);
 #pragma unroll
-                for (int q = 0; q < XS; ++q) {
-                    uint4 *p = reinterpret_cast<uint4 *>(&stage[(wid * (BM / 4) + q * 16) * BK + 8 * lane]);
+                for (int q = 0; q < XI; ++q) {
+                    uint4 *p = reinterpret_cast<uint4 *>(&stage[(wid * (BM / 8) + q * 16) * BK + 8 * lane]);
                     uint4 v = *p;
                     v.x &= m[0];
                     v.y &= m[1];
@@ -183,35 +208,61 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_w4a16_kernel(
         }
     };
 
-    // loader roles for the weights: thread -> (row, 16-column half of the 32-column step)
-    const int ld_row = tid >> 1;
-    const int ld_half = tid & 1;
-    const int wrow = n0 + ld_row;
-    const bool wrow_ok = wrow < d_out;
-
-    // Weight loads are unconditional (the row is clamped into the matrix and masked when
-    // stored): a load behind a branch would make the compiler's memory-counter waits drain the
-    // loads that run ahead.
-    auto load_w = [&](int step, WLoad &L) {
-        const int k0 = step * BK + 16 * ld_half;
-        const int G = step / steps_per_group;
-        const int wr = wrow_ok ? wrow : d_out - 1;
-        L.w = *reinterpret_cast<const uint2 *>(qweight + static_cast<int64_t>(wr) * row_bytes +
-                                               k0 / 2);
-        const int64_t gi = static_cast<int64_t>(wr) * n_groups + G;
-        L.s_bits = scales[gi];
-        if (ZP) L.z_bits = zeros[gi];
+    // Weight chunks: wave w loads row blocks 2w and 2w + 1 (16 rows each) of the tile, each with
+    // a descriptor that covers only its rows below d_out (rows beyond load zeros: zero codes and
+    // a zero scale, so zero weights).  Codes: lane l fetches the 16 bytes of row l % 16 for step
+    // l / 16 of the chunk (offsets past the row's end only occur in chunks beyond the last step,
+    // whose contents are never used).  Scales and zero points: lane l fetches the 16-bit value of
+    // row l % 16 for step l / 16, i.e. of group min(step / steps_per_group, n_groups - 1).
+    rsrc_t q_rsrc[2], s_rsrc[2], z_rsrc[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int r0 = n0 + (2 * wid + h) * 16;
+        const int rows = r0 < d_out ? (d_out - r0 < 16 ? d_out - r0 : 16) : 0;
+        q_rsrc[h] = make_rsrc(rows > 0 ? qweight + static_cast<int64_t>(r0) * row_bytes : qweight,
+                              static_cast<uint32_t>(rows * row_bytes));
+        s_rsrc[h] = make_rsrc(rows > 0 ? scales + static_cast<int64_t>(r0) * n_groups : scales,
+                              static_cast<uint32_t>(rows * n_groups * 2));
+        if (ZP)
+            z_rsrc[h] = make_rsrc(rows > 0 ? zeros + static_cast<int64_t>(r0) * n_groups : zeros,
+                                  static_cast<uint32_t>(rows * n_groups * 2));
+    }
+    const uint32_t q_lane_off = static_cast<uint32_t>((lane & 15) * row_bytes + 16 * (lane >> 4));
+    const uint32_t s_lane_row = static_cast<uint32_t>((lane & 15) * n_groups);
+    auto dma_chunk = [&](int chunk, uint8_t *sq, uint32_t *ss, uint32_t *sz) {
+        const int k0 = chunk * KC;
+        const uint32_t qoff = q_lane_off + static_cast<uint32_t>(k0) * 16u;
+        int g = (k0 + (lane >> 4)) / steps_per_group;
+        g = g < n_groups ? g : n_groups - 1;
+        const uint32_t soff = 2u * (s_lane_row + static_cast<uint32_t>(g));
+#pragma unroll
+        for (int h = 0; h < 2; ++h) load_lds16(q_rsrc[h], &sq[(2 * wid + h) * 1024], qoff);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) load_lds2(s_rsrc[h], &ss[(2 * wid + h) * 64], soff);
+        if (ZP) {
+#pragma unroll
+            for (int h = 0; h < 2; ++h) load_lds2(z_rsrc[h], &sz[(2 * wid + h) * 64], soff);
+        }
     };
 
-    // Weights of a loaded step -> exact hi/lo bf16 halves in a stage (straight-line vector code
-    // that the scheduler can interleave with the matrix instructions of the current step).
-    auto store_w = [&](const WLoad &L, int stage) {
-        const float sv = wrow_ok ? bf16_to_f32(L.s_bits) : 0.0f;
-        const float zv = ZP ? bf16_to_f32(L.z_bits) : 8.0f;
+    // Dequantizer roles: thread -> (row, 16-column half of the 32-column step); the 16 lanes of a
+    // quarter wave take 16 consecutive rows and one half, so that their chunk reads and each of
+    // their stage stores are contiguous in LDS.
+    const int ld_row = (tid & 15) + 16 * (tid >> 5);
+    const int ld_half = (tid >> 4) & 1;
+    const int q_read = (ld_row >> 4) * 1024 + (ld_row & 15) * 16 + 8 * ld_half;
+    const int s_read = (ld_row >> 4) * 64 + (ld_row & 15);
+
+    // Step k of a chunk -> exact hi/lo bf16 halves in a weight stage.
+    auto dequant = [&](int k, const uint8_t *sq, const uint32_t *ss, const uint32_t *sz,
+                       uint16_t *shi, uint16_t *slo) {
+        const uint2 wq = *reinterpret_cast<const uint2 *>(&sq[q_read + 256 * k]);
+        const float sv = bf16_to_f32(ss[s_read + 16 * k]);
+        const float zv = ZP ? bf16_to_f32(sz[s_read + 16 * k]) : 8.0f;
         const float zs = -(zv * sv);
         // 16 codes = two 16-byte chunks of the stage (8 columns per packed dword); per dword the
         // bytes of the even columns (w & 0x0F0F0F0F) and odd columns ((w >> 4) & 0x0F0F0F0F)
-        const uint32_t wv[2] = {L.w.x, L.w.y};
+        const uint32_t wv[2] = {wq.x, wq.y};
 #pragma unroll
         for (int d = 0; d < 2; ++d) {
             const uint32_t ev = wv[d] & 0x0F0F0F0Fu;
@@ -223,8 +274,8 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_w4a16_kernel(
             split4(c03, sv, zs, &hi[0], &lo[0]);
             split4(c47, sv, zs, &hi[2], &lo[2]);
             const int c = lds_at(ld_row, 2 * ld_half + d);
-            *reinterpret_cast<uint4 *>(&shi[stage][c]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-            *reinterpret_cast<uint4 *>(&slo[stage][c]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+            *reinterpret_cast<uint4 *>(&shi[c]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+            *reinterpret_cast<uint4 *>(&slo[c]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
         }
     };
 
@@ -236,8 +287,8 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_w4a16_kernel(
 
     // A lane reads row frag_row (+ multiples of 16) at k-chunk lane / 16 of every fragment.
     const int frag_row = lane & 15;
-    const int frag_off = lds_at(frag_row, lane >> 4);
-    auto compute = [&](const uint16_t *xstage, int wstage) {
+    const int frag_off = lds_at(frag_row, lane >> 4);  // = 8 * lane
+    auto compute = [&](const uint16_t *xstage, const uint16_t *shi, const uint16_t *slo) {
         bf16x8_t a[TM];
 #pragma unroll
         for (int i = 0; i < TM; ++i)
@@ -246,8 +297,8 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_w4a16_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int wr = (wn * 64 + j * 16) * BK + frag_off;
-            const bf16x8_t bh = *reinterpret_cast<const bf16x8_t *>(&shi[wstage][wr]);
-            const bf16x8_t bl = *reinterpret_cast<const bf16x8_t *>(&slo[wstage][wr]);
+            const bf16x8_t bh = *reinterpret_cast<const bf16x8_t *>(&shi[wr]);
+            const bf16x8_t bl = *reinterpret_cast<const bf16x8_t *>(&slo[wr]);
 #pragma unroll
             for (int i = 0; i < TM; ++i)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], bh, acc[i][j], 0, 0, 0);
@@ -257,52 +308,59 @@ __global__ void __launch_bounds__(kThreads, 2) gemm_w4a16_kernel(
         }
     };
 
-    // One step: start the activations of step + 2 into the free activation stage and the
-    // weights of step + 2 into the free register set (the last steps reload the final step,
-    // unconditionally), multiply from the current stages, and dequantize the weights of step + 1
-    // into the other weight stage (last read before the previous barrier; after the final step
-    // this writes a stage nobody reads).  Waiting for the weights of step + 1 also covers the
-    // activations of step + 1, which were issued before them.
-    const int last = n_steps - 1;
-    auto run_step = [&](int step, uint16_t *xcur, uint16_t *xnext, uint16_t *xfree,
-                        WLoad &free_set, const WLoad &next_set, int ws) {
-        dma_x(step + 2 < n_steps ? step + 2 : last, xfree);
-        load_w(step + 2 < n_steps ? step + 2 : last, free_set);
-        // keep the loads ahead of the vector work on the previous set: a wait for that set placed
-        // before them would have to drain every load in flight
+    uint16_t *const sx[3] = {sx0, sx1, sx2};
+    uint16_t *const shi[2] = {shi0, shi1};
+    uint16_t *const slo[2] = {slo0, slo1};
+    uint8_t *const sq[2] = {sq0, sq1};
+    uint32_t *const ss[2] = {ss0, ss1};
+    uint32_t *const sz[2] = {sz0, sz1};
+
+    // Step s (P = s % kPeriod, known at compile time): start the activations of step s + 2 and,
+    // at the first step of a chunk, the next chunk; multiply from the current stages; dequantize
+    // step s + 1 from its chunk into the other weight stage (last read before the previous
+    // barrier); then wait for what the next step reads and pass the barrier.
+    //   vector-memory issue order: ... X(s+1) [CH(c+1) if s-1 opens chunk c] X(s+2) [CH if s opens]
+    //   the next step reads X(s+1), and step 4c + 3 dequantizes from chunk c + 1; both are covered
+    //   by waiting until only the loads issued after X(s+1) are in flight.
+    // After the final step the loads run past the matrix (zeros or unused bytes) into stages
+    // nobody reads.
+    auto run_step = [&](int step, auto PP) {
+        constexpr int P = decltype(PP)::value;
+        constexpr int K = P % KC;
+        constexpr int CB = (P / KC) % 2;  // chunk buffer of this step
+        constexpr int CN = ((P + 1) / KC) % 2;  // chunk buffer of step s + 1
+        dma_x(step + 2, sx[(P + 2) % 3]);
+        if constexpr (K == 0) dma_chunk(step / KC + 1, sq[CB ^ 1], ss[CB ^ 1], sz[CB ^ 1]);
         __builtin_amdgcn_sched_barrier(0);
-        compute(xcur, ws);
-        store_w(next_set, ws ^ 1);
-        trim_x(step + 1, xnext);
-        stage_barrier();
+        compute(sx[P % 3], shi[P % 2], slo[P % 2]);
+        dequant((P + 1) % KC, sq[CN], ss[CN], sz[CN], shi[(P + 1) % 2], slo[(P + 1) % 2]);
+        trim_x(step + 1, sx[(P + 1) % 3]);
+        constexpr int N = XI + ((K == 0 || K == 1) ? CI : 0);
+        stage_barrier<N>();
     };
 
-    WLoad W0, W1;
+    // prologue: X(0), CH(0), X(1); step 0's weights into stage 0
     dma_x(0, sx0);
-    load_w(0, W0);
-    dma_x(n_steps > 1 ? 1 : 0, sx1);
-    load_w(n_steps > 1 ? 1 : 0, W1);
-    store_w(W0, 0);
+    dma_chunk(0, sq0, ss0, sz0);
+    dma_x(1, sx1);
+    wait_vm_lgkm0<XI>();
+    __syncthreads();
+    dequant(0, sq0, ss0, sz0, shi0, slo0);
     trim_x(0, sx0);
     __syncthreads();
 
-    // steps 6i .. 6i + 5: activation stages rotate with period 3, weight sets with period 2
-    int step = 0;
-    for (; step + 5 < n_steps; step += 6) {
-        run_step(step + 0, sx0, sx1, sx2, W0, W1, 0);
-        run_step(step + 1, sx1, sx2, sx0, W1, W0, 1);
-        run_step(step + 2, sx2, sx0, sx1, W0, W1, 0);
-        run_step(step + 3, sx0, sx1, sx2, W1, W0, 1);
-        run_step(step + 4, sx1, sx2, sx0, W0, W1, 0);
-        run_step(step + 5, sx2, sx0, sx1, W1, W0, 1);
+    for (int s0 = 0; s0 < n_steps; s0 += kPeriod) {
+        // the period unrolled; the final pass skips the steps from n_steps on (guards rather than
+        // an exit per step: a loop with 24 exits costs the register allocator thousands of spills)
+#define W4_STEP(p) \
+        if (s0 + (p) < n_steps) run_step(s0 + (p), std::integral_constant<int, (p)>{});
+        W4_STEP(0) W4_STEP(1) W4_STEP(2) W4_STEP(3) W4_STEP(4) W4_STEP(5)
+        W4_STEP(6) W4_STEP(7) W4_STEP(8) W4_STEP(9) W4_STEP(10) W4_STEP(11)
+        W4_STEP(12) W4_STEP(13) W4_STEP(14) W4_STEP(15) W4_STEP(16) W4_STEP(17)
+        W4_STEP(18) W4_STEP(19) W4_STEP(20) W4_STEP(21) W4_STEP(22) W4_STEP(23)
+#undef W4_STEP
     }
-    // the remaining 0..5 steps continue the same rotation
-    if (step < n_steps) run_step(step, sx0, sx1, sx2, W0, W1, 0);
-    if (step + 1 < n_steps) run_step(step + 1, sx1, sx2, sx0, W1, W0, 1);
-    if (step + 2 < n_steps) run_step(step + 2, sx2, sx0, sx1, W0, W1, 0);
-    if (step + 3 < n_steps) run_step(step + 3, sx0, sx1, sx2, W1, W0, 1);
-    if (step + 4 < n_steps) run_step(step + 4, sx1, sx2, sx0, W0, W1, 0);
-    // the last steps reloaded the final step: let those loads land before the block ends
+    // the loads that ran past the final step land before the block ends
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
     // epilogue: D[i][j] of a 16x16 tile sits in lane j + 16 * (i / 4), element i % 4
@@ -356,10 +414,10 @@ hipError_t launch_gemm(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t 
                        const uint16_t *scales, const uint16_t *zeros, const uint16_t *bias,
                        int64_t d_out, int64_t d_in, int64_t k_pad, int64_t span,
                        int64_t n_groups, void *y, int64_t ldy, bool out_f32, hipStream_t stream) {
-    // 256-token tiles when they still give every compute unit two blocks, else 128.
+    // 256-token tiles when they still give every compute unit a block, else 128.
     const int64_t tiles_n = (d_out + BN - 1) / BN;
     const int64_t blocks256 = ((M + 255) / 256) * tiles_n;
-    if (M > 128 && blocks256 >= 2 * static_cast<int64_t>(device_cu_count()))
+    if (M > 128 && blocks256 >= static_cast<int64_t>(device_cu_count()))
         return launch_bm<256>(x, M, ldx, qweight, scales, zeros, bias, d_out, d_in, k_pad, span,
                               n_groups, y, ldy, out_f32, stream);
     return launch_bm<128>(x, M, ldx, qweight, scales, zeros, bias, d_out, d_in, k_pad, span,
