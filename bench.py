@@ -55,10 +55,13 @@ def source_hash(*files):
     return h.hexdigest()[:16]
 
 
-# the sources of the C2 gate/up GEMV's kernel: the committed traffic figure is
-# reported only while their hash matches the one it was measured on
+# the sources of the C2 gate/up GEMV's kernel, of the routing that picks it and of the build
+# flags: the committed traffic figure is reported only while their hash matches the one it was
+# measured on
 TRAFFIC_SOURCES = ("int4_weight_only_amd/csrc/decode_i8.hip",
-                   "int4_weight_only_amd/csrc/w4_device.h")
+                   "int4_weight_only_amd/csrc/w4_device.h",
+                   "int4_weight_only_amd/csrc/decode.hip",
+                   "int4_weight_only_amd/build.py")
 
 
 def load_traffic(kernel_key, src_hash):

@@ -245,7 +245,9 @@ def summarize(workload, sq_csv, trace_csv, fetch_csv, write_csv):
         valu = mean(p["SQ_INSTS_VALU"])
         weights = d_out * d_in if d_out else 0
         lane_ops = valu * 64 / weights if weights else float("nan")
-        hbm = mean(p["FETCH_SIZE"]) * 1024 * fscale + mean(p["WRITE_SIZE"]) * 1024 * wscale
+        rd = mean(p["FETCH_SIZE"]) * 1024 * fscale
+        wr = mean(p["WRITE_SIZE"]) * 1024 * wscale
+        hbm = rd + wr
         if flops:
             rate = f"{flops / us / 1e6:.0f} TFLOP/s"
         else:
@@ -257,8 +259,11 @@ def summarize(workload, sq_csv, trace_csv, fetch_csv, write_csv):
               f"{mean(p['VALUBusy']):.1f} | {mean(p['MfmaUtil']):.1f} | "
               f"{mean(p['SQ_INSTS_MFMA']):.0f} | {mean(p['SQ_INSTS_LDS']):.0f} | "
               f"{mean(p['SQ_LDS_BANK_CONFLICT']):.0f} | {ratio:.4f} |")
-        table.append(dict(label=lab, kernel=kname, us=us, hbm_bytes=hbm, algorithmic_bytes=algo,
-                          flops=flops, valu_lane_ops_per_weight=lane_ops,
+        table.append(dict(label=lab, kernel=kname, us=us, hbm_bytes=hbm, read_bytes=rd,
+                          write_bytes=wr, fetch_kb_raw=mean(p["FETCH_SIZE"]),
+                          write_kb_raw=mean(p["WRITE_SIZE"]), fetch_scale=fscale,
+                          write_scale=wscale, dispatches=len(p["FETCH_SIZE"]),
+                          algorithmic_bytes=algo, flops=flops, valu_lane_ops_per_weight=lane_ops,
                           valu_busy=mean(p["VALUBusy"]), mfma_util=mean(p["MfmaUtil"])))
     print(f"\nFETCH_SIZE scale {fscale:.4f}, WRITE_SIZE scale {wscale:.4f} (256 MiB copy); "
           f"{REPS} dispatches per call")
@@ -276,8 +281,16 @@ def update_traffic(table):
         "kernel": row["kernel"] + " (C2 gate/up 37888x3584, M=1, bf16 out)",
         "source_hash": source_hash(*TRAFFIC_SOURCES),
         "bytes_per_launch": round(row["hbm_bytes"]),
+        "read_bytes_per_launch": round(row["read_bytes"]),
+        "write_bytes_per_launch": round(row["write_bytes"]),
         "algorithmic_bytes_per_launch": row["algorithmic_bytes"],
         "traffic_over_algorithmic": round(row["hbm_bytes"] / row["algorithmic_bytes"], 4),
+        "fetch_kb_raw": round(row["fetch_kb_raw"], 1),
+        "write_kb_raw": round(row["write_kb_raw"], 1),
+        "fetch_scale": round(row["fetch_scale"], 4),
+        "write_scale": round(row["write_scale"], 4),
+        "calibration": f"{COPY_BYTES >> 20} MiB device copy, mean of {CALIB_COPIES} dispatches",
+        "dispatches": row["dispatches"],
     }
     with open(out, "w") as fh:
         json.dump(data, fh, indent=2)
