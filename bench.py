@@ -394,6 +394,35 @@ def bench_gptq(torch, w4, workloads, iters):
                 quantize_ms=round(q_ms, 3), total_ms=round(h_ms + f_ms + q_ms, 3))
 
 
+def bench_c1(torch, w4, workloads, replays=20, calls=50):
+    """The tiny linear (128 x 256, g32 symmetric) at M = 1 and 4: the time of one call among
+    `calls` back-to-back calls in a HIP graph (kernel time plus the gap between graph nodes),
+    through w4_gemv and, at M = 4, also w4_gemm."""
+    cfg = workloads.C1
+    lin = cfg.linears[0]
+    dev = torch.device("cuda", 0)
+    w = torch.from_numpy(workloads.linear_weight(cfg, 0)).to(dev)
+    qw, sc, zr = w4.w4_pack(w, lin.group_size, lin.mode)
+    out = {}
+    for M in cfg.tokens:
+        x = torch.from_numpy(workloads.linear_x(cfg, 0, M).view(np.int16)).view(
+            torch.bfloat16).to(dev)
+        y = torch.empty((M, lin.d_out), dtype=torch.bfloat16, device=dev)
+        def gemv():
+            for _ in range(calls):
+                w4.w4_gemv(x, qw, sc, zr, None, lin.d_in, lin.group_size, out=y)
+
+        def gemm():
+            for _ in range(calls):
+                w4.w4_gemm(x, qw, sc, zr, None, lin.d_in, lin.group_size, out=y)
+
+        r = dict(gemv_us=round(graph_ms(torch, gemv, calls, replays) * 1e3, 2))
+        if M > 1:
+            r["gemm_us"] = round(graph_ms(torch, gemm, calls, replays) * 1e3, 2)
+        out[f"M={M}"] = r
+    return out
+
+
 def bench_c3(torch, w4, workloads, iters):
     """28 layers x {qkv, o, gate/up, down}, asymmetric g128, weights generated on the GPU with a
     seeded torch generator (timing only; parity of these shapes is in the GPU tests)."""
@@ -424,17 +453,61 @@ def bench_c3(torch, w4, workloads, iters):
         ms = graph_ms(torch, step, 1, iters)
         nbytes = cfg.repeat_layers * sum(linear_bytes(M, l.d_out, l.d_in, l.group_size, True)
                                          for l in cfg.linears)
+        # each linear alone (its 28 launches in one graph): per-call time and rate; their sum
+        # next to the whole step's time shows what the back-to-back launches cost or save
+        per_lin = {}
+        for k, lin in enumerate(cfg.linears):
+            def one(k=k, lin=lin):
+                for packs in layers:
+                    w4.w4_gemv(xs[k], *packs[k], None, lin.d_in, lin.group_size, out=ys[k])
+            lms = graph_ms(torch, one, cfg.repeat_layers, iters)
+            lb = linear_bytes(M, lin.d_out, lin.d_in, lin.group_size, True)
+            per_lin[lin.name] = dict(us=round(lms * 1e3, 2), gbs=round(lb / lms / 1e6, 1),
+                                     hbm_frac=round(lb / lms / 1e6 / HBM_PEAK_GBS, 4))
+        sum_us = cfg.repeat_layers * sum(v["us"] for v in per_lin.values())
         out[f"M={M}"] = dict(step_us=round(ms * 1e3, 1), gbs=round(nbytes / ms / 1e6, 1),
-                             hbm_frac=round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4))
+                             hbm_frac=round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
+                             sum_of_linears_us=round(sum_us, 1), linears=per_lin)
     del layers
     return out
 
 
+def host_cpu():
+    """The host's CPU model (from /proc/cpuinfo) and logical CPU count."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return dict(model=model, logical_cpus=os.cpu_count())
+
+
+def _oracle_rate(fn, budget_s, max_calls=100000):
+    """(calls, seconds) of repeated calls of fn within about budget_s (at least one call)."""
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        fn()
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= max_calls:
+            return n, el
+
+
 def cpu_baseline(workloads, budget_s):
-    """The oracle, as it stands, on the host's cores, over the same C2 step (M = 1)."""
+    """The oracle, as it stands, on the host's cores: the C2 step (M = 1) with all threads (the
+    headline baseline), then every other config on a bounded sample, with all threads and, for
+    C1, C2 and C5, with one thread."""
     import oracle
+    threads = oracle.max_threads()
+    per = {}
+
+    # C2: the headline (the whole decode step, all threads), then one thread
     cfg = workloads.C2
-    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     packs, xs = [], []
     for li, lin in enumerate(cfg.linears):
         w = workloads.linear_weight(cfg, li)
@@ -442,19 +515,104 @@ def cpu_baseline(workloads, budget_s):
         xs.append(workloads.linear_x(cfg, li, 1))
         del w
     nbytes = sum(linear_bytes(1, l.d_out, l.d_in, l.group_size, False) for l in cfg.linears)
-    n = 0
-    t0 = time.perf_counter()
-    while True:
+
+    def c2_step():
         for (qw, sc, zr), x, lin in zip(packs, xs, cfg.linears):
             oracle.w4a16(x, qw, sc, zr, None, lin.d_in, lin.group_size)
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or n >= 2000:
-            break
-    return dict(value=round(nbytes * n / el / 1e9, 3), unit="GB/s", cores=threads,
-                kind="oracle",
+
+    n, el = _oracle_rate(c2_step, 0.5 * budget_s, 2000)
+    head = dict(value=round(nbytes * n / el / 1e9, 3), unit="GB/s", cores=threads, kind="oracle",
                 sample=f"{n} full C2 decode steps (gate/up 37888x3584 + down 3584x18944, M=1) "
                        f"in {el:.1f} s, fp64 oracle with OpenMP over output rows")
+    oracle.set_num_threads(1)
+    n1, el1 = _oracle_rate(c2_step, 0.1 * budget_s, 100)
+    oracle.set_num_threads(threads)
+    per["C2"] = dict(step_ms=round(el / n * 1e3, 2), gbs=head["value"],
+                     step_ms_1thread=round(el1 / n1 * 1e3, 2),
+                     gbs_1thread=round(nbytes * n1 / el1 / 1e9, 3))
+    del packs, xs
+
+    # C1: the tiny linear at M = 1 and 4
+    cfg = workloads.C1
+    lin = cfg.linears[0]
+    qw, sc, zr = oracle.pack(workloads.linear_weight(cfg, 0), lin.group_size, lin.mode)
+    c1 = {}
+    for M in cfg.tokens:
+        x = workloads.linear_x(cfg, 0, M)
+        fn = lambda: oracle.w4a16(x, qw, sc, zr, None, lin.d_in, lin.group_size)
+        n, el = _oracle_rate(fn, 0.02 * budget_s)
+        oracle.set_num_threads(1)
+        n1, el1 = _oracle_rate(fn, 0.02 * budget_s)
+        oracle.set_num_threads(threads)
+        c1[f"M={M}"] = dict(us=round(el / n * 1e6, 2), us_1thread=round(el1 / n1 * 1e6, 2))
+    per["C1"] = c1
+
+    # C3: one layer's four linears (asymmetric g128) at M = 1 and 8, scaled to the 28 layers
+    cfg = workloads.C3
+    packs = [oracle.pack(workloads.linear_weight(cfg, li), l.group_size, l.mode)
+             for li, l in enumerate(cfg.linears)]
+    c3 = {}
+    for M in (1, 8):
+        xs = [workloads.linear_x(cfg, li, M) for li in range(len(cfg.linears))]
+
+        def layer():
+            for (qw, sc, zr), x, l in zip(packs, xs, cfg.linears):
+                oracle.w4a16(x, qw, sc, zr, None, l.d_in, l.group_size)
+
+        n, el = _oracle_rate(layer, 0.05 * budget_s, 50)
+        layer_bytes = sum(linear_bytes(M, l.d_out, l.d_in, l.group_size, True)
+                          for l in cfg.linears)
+        c3[f"M={M}"] = dict(layer_ms=round(el / n * 1e3, 2),
+                            step_ms_28_layers=round(el / n * 1e3 * cfg.repeat_layers, 1),
+                            gbs=round(layer_bytes * n / el / 1e9, 3))
+    c3["sample"] = "layer 0's four linears, timed whole; the 28-layer step is 28 x that"
+    per["C3"] = c3
+    del packs
+
+    # C4: 16 of the 2048 tokens through each full weight (all rows), as GFLOP/s; the full
+    # config's time at that rate
+    cfg = workloads.C4
+    c4, flop_all, t_all = {}, 0.0, 0.0
+    for li, l in enumerate(cfg.linears):
+        qw, sc, zr = oracle.pack(workloads.linear_weight(cfg, li), l.group_size, l.mode)
+        x = workloads.linear_x(cfg, li, 16)
+        n, el = _oracle_rate(lambda: oracle.w4a16(x, qw, sc, zr, None, l.d_in, l.group_size),
+                             0.04 * budget_s, 20)
+        rate = 2.0 * 16 * l.d_out * l.d_in * n / el
+        c4[l.name] = dict(gflops=round(rate / 1e9, 2))
+        flop = 2.0 * cfg.tokens[0] * l.d_out * l.d_in
+        flop_all += flop
+        t_all += flop / rate
+        del qw, sc, zr
+    c4["full_config_s_at_that_rate"] = round(t_all, 1)
+    c4["gflops"] = round(flop_all / t_all / 1e9, 2)
+    c4["sample"] = "16 of the 2048 tokens against all rows of each weight, fp64"
+    per["C4"] = c4
+
+    # C5: act_quant + W4A8 GEMV (per-row symmetric), M = 1, both shapes
+    cfg = workloads.C5
+    c5 = {}
+    for li, l in enumerate(cfg.linears):
+        qw, sw, _ = oracle.pack(workloads.linear_weight(cfg, li), 0, oracle.SYM)
+        x = workloads.linear_x(cfg, li, 1)
+        b = workloads.linear_bias(cfg, li)
+
+        def path():
+            q, s_x, _ = oracle.act_quant(x)
+            oracle.w4a8(q, s_x, qw, sw, b, l.d_in)
+
+        n, el = _oracle_rate(path, 0.04 * budget_s, 200)
+        oracle.set_num_threads(1)
+        n1, el1 = _oracle_rate(path, 0.02 * budget_s, 50)
+        oracle.set_num_threads(threads)
+        gb = linear_bytes(1, l.d_out, l.d_in, 0, False, bias=True, x_bytes=2)
+        c5[f"{l.d_out}x{l.d_in}"] = dict(us=round(el / n * 1e6, 1),
+                                         us_1thread=round(el1 / n1 * 1e6, 1),
+                                         gbs=round(gb * n / el / 1e9, 3))
+    per["C5"] = c5
+    head["per_config"] = per
+    head["host_cpu"] = host_cpu()
+    return head
 
 
 def main():
@@ -465,7 +623,8 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
-    ap.add_argument("--only", choices=["c2", "c3", "c4", "c5", "qat", "gptq"], default=None,
+    ap.add_argument("--only", choices=["c1", "c2", "c3", "c4", "c5", "qat", "gptq"],
+                    default=None,
                     help="time one workload only (for profiling runs)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -487,7 +646,9 @@ def main():
         log("C2 decode step")
         r = bench_c2(torch, w4, workloads, args.steps, args.warmup, rotate)
     if args.only is not None:
-        if args.only == "c3":
+        if args.only == "c1":
+            secondary["C1_tiny"] = bench_c1(torch, w4, workloads)
+        elif args.only == "c3":
             secondary["C3_decoder_step"] = bench_c3(torch, w4, workloads, 5)
         elif args.only == "c4":
             secondary["C4_prefill_gemm"] = bench_c4(torch, w4, workloads, 10)
@@ -501,6 +662,8 @@ def main():
             print(json.dumps(secondary), flush=True)
             return
     if not args.no_secondary and args.only is None:
+        log("C1 tiny linear")
+        secondary["C1_tiny"] = bench_c1(torch, w4, workloads)
         log("C4 prefill GEMM")
         secondary["C4_prefill_gemm"] = bench_c4(torch, w4, workloads, 10)
         log("C5 W4A8")

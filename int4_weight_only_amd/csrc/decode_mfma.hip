@@ -78,11 +78,14 @@ __host__ __device__ inline TokLds tok_lds(int T, int n_groups, int W, bool zp) {
 // Exact fp16 (c - zi) pairs of the 8 codes of one packed dword, in the order
 // (c0, c4), (c1, c5), (c2, c6), (c3, c7).  zlo = -(1024 + zi) and zhi = -(64 + zi) as fp16 pairs.
 __device__ __forceinline__ half8_t dequant8(uint32_t w, uint32_t zlo_neg, uint32_t zhi_neg) {
+    // (plain C, not the inline-asm and_or helper: the compiler's hazard checks do not look into
+    // inline asm, and an asm write scheduled right after an MFMA can land in that MFMA's source
+    // registers before it has read them)
     const uint32_t w8 = w >> 8;
-    const uint32_t p0 = and_or(w, 0x000F000Fu, 0x64006400u);
-    const uint32_t p1 = and_or(w, 0x00F000F0u, 0x64006400u);
-    const uint32_t p2 = and_or(w8, 0x000F000Fu, 0x64006400u);
-    const uint32_t p3 = and_or(w8, 0x00F000F0u, 0x64006400u);
+    const uint32_t p0 = (w & 0x000F000Fu) | 0x64006400u;
+    const uint32_t p1 = (w & 0x00F000F0u) | 0x64006400u;
+    const uint32_t p2 = (w8 & 0x000F000Fu) | 0x64006400u;
+    const uint32_t p3 = (w8 & 0x00F000F0u) | 0x64006400u;
     const half2_t zl = as_half2(zlo_neg);
     const half2_t zh = as_half2(zhi_neg);
     const half2_t sixteenth = {static_cast<_Float16>(0.0625f), static_cast<_Float16>(0.0625f)};

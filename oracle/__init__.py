@@ -257,6 +257,20 @@ def qat_repack(w_bits, d_in=None):
     return qw, sc, m
 
 
+def set_num_threads(n):
+    """Threads of the oracle's OpenMP loops from now on (the benchmark's timing leg sets 1 for its
+    single-thread figures).  No effect on results: every parallel loop is over independent
+    outputs."""
+    _load()
+    ctypes.CDLL("libgomp.so.1").omp_set_num_threads(int(n))
+
+
+def max_threads():
+    """Threads the next OpenMP loop of the oracle uses."""
+    _load()
+    return int(ctypes.CDLL("libgomp.so.1").omp_get_max_threads())
+
+
 def tolerance_ok(y, y_ref, rel=2e-3):
     """The floating-point parity bar: |y - y_ref| <= rel * (1 + |y_ref|), elementwise."""
     y = np.asarray(y, dtype=np.float64)
