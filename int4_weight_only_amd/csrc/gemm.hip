@@ -114,7 +114,7 @@ __device__ __forceinline__ void split4(uint32_t b, float s, float zs, uint32_t *
     lo2[1] = __builtin_amdgcn_perm(l[3], l[2], 0x07060302u);
 }
 
-template <int BM, bool ZP>
+template <int BM, bool ZP, bool SW>
 __global__ void __launch_bounds__(kThreads, 1) gemm_w4a16_kernel(
     const uint16_t *__restrict__ x, int M, int64_t ldx, const uint8_t *__restrict__ qweight,
     const uint16_t *__restrict__ scales, const uint16_t *__restrict__ zeros,
@@ -124,7 +124,9 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_w4a16_kernel(
     constexpr int WM = BM / 2;    // rows of a wave tile
     constexpr int TM = WM / 16;   // 16-row MFMA tiles per wave
     constexpr int XI = BM / 128;  // activation loads per wave per step (16 rows each)
-    constexpr int CI = ZP ? 6 : 4;  // chunk loads per wave per chunk (codes, scales, zeros: 2 each)
+    // chunk loads per wave per chunk (codes, scales, zeros: 2 each; with scale windows the codes
+    // only)
+    constexpr int CI = SW ? 2 : (ZP ? 6 : 4);
     // Shared memory, every stage an array of its own: the step loop is unrolled over the period
     // of all rings so that each access names its array, and the compiler then sees that a direct
     // load in flight does not touch the stage being read or written (it would otherwise wait for
@@ -141,8 +143,14 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_w4a16_kernel(
     __shared__ __attribute__((aligned(16))) uint8_t sq0[BN * KC * 16];
     __shared__ __attribute__((aligned(16))) uint8_t sq1[BN * KC * 16];
     // scale (zero point) bits of row 16 b + r for step k of the chunk in dword 64 b + 16 k + r
-    __shared__ __attribute__((aligned(16))) uint32_t ss0[BN * KC];
-    __shared__ __attribute__((aligned(16))) uint32_t ss1[BN * KC];
+    __shared__ __attribute__((aligned(16))) uint32_t ss0[SW ? 1 : BN * KC];
+    __shared__ __attribute__((aligned(16))) uint32_t ss1[SW ? 1 : BN * KC];
+    // scale windows (SW): the bf16 scales of 8 consecutive groups of every row, row r at element
+    // 8 r, a ring of three; waves 4..7 aim their (empty) window loads at a dummy
+    __shared__ __attribute__((aligned(16))) uint16_t sw0[SW ? BN * 8 : 1];
+    __shared__ __attribute__((aligned(16))) uint16_t sw1[SW ? BN * 8 : 1];
+    __shared__ __attribute__((aligned(16))) uint16_t sw2[SW ? BN * 8 : 1];
+    __shared__ __attribute__((aligned(16))) uint16_t swd[SW ? 64 * 8 : 1];
     __shared__ __attribute__((aligned(16))) uint32_t sz0[ZP ? BN * KC : 1];
     __shared__ __attribute__((aligned(16))) uint32_t sz1[ZP ? BN * KC : 1];
 
@@ -237,12 +245,34 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_w4a16_kernel(
         const uint32_t soff = 2u * (s_lane_row + static_cast<uint32_t>(g));
 #pragma unroll
         for (int h = 0; h < 2; ++h) load_lds16(q_rsrc[h], &sq[(2 * wid + h) * 1024], qoff);
+        if (!SW) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) load_lds2(s_rsrc[h], &ss[(2 * wid + h) * 64], soff);
+            for (int h = 0; h < 2; ++h) load_lds2(s_rsrc[h], &ss[(2 * wid + h) * 64], soff);
+        }
         if (ZP) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) load_lds2(z_rsrc[h], &sz[(2 * wid + h) * 64], soff);
         }
+    };
+
+    // Scale windows (32-column groups, no zero points, n_groups % 8 == 0, 16-byte aligned scales):
+    // one direct 16-byte load per lane brings the 8 scales of window w (groups 8 w .. 8 w + 7) of
+    // one row -- waves 0..3 load 64 rows each, the other waves an empty load into a dummy, so
+    // that every wave counts the same loads. A 256-row step then costs 32 lines instead of 64,
+    // and 0.5 loads per wave instead of 4.
+    rsrc_t w_rsrc = q_rsrc[0];
+    uint32_t w_lane_off = kOutOfRange;
+    if (SW) {
+        const int r0 = n0 + 64 * (wid & 3);
+        const int rows = r0 < d_out ? (d_out - r0 < 64 ? d_out - r0 : 64) : 0;
+        w_rsrc = make_rsrc(rows > 0 ? scales + static_cast<int64_t>(r0) * n_groups : scales,
+                           static_cast<uint32_t>(rows * n_groups * 2));
+        if (wid < 4) w_lane_off = static_cast<uint32_t>(lane * n_groups * 2);
+    }
+    auto dma_window = [&](int window, uint16_t *buf) {
+        const uint32_t off =
+            wid < 4 ? w_lane_off + 16u * static_cast<uint32_t>(window) : kOutOfRange;
+        load_lds16(w_rsrc, wid < 4 ? &buf[(wid & 3) * 64 * 8] : swd, off);
     };
 
     // Dequantizer roles: thread -> (row, 16-column half of the 32-column step); the 16 lanes of a
@@ -255,9 +285,9 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_w4a16_kernel(
 
     // Step k of a chunk -> exact hi/lo bf16 halves in a weight stage.
     auto dequant = [&](int k, const uint8_t *sq, const uint32_t *ss, const uint32_t *sz,
-                       uint16_t *shi, uint16_t *slo) {
+                       const uint16_t *swb, int k8, uint16_t *shi, uint16_t *slo) {
         const uint2 wq = *reinterpret_cast<const uint2 *>(&sq[q_read + 256 * k]);
-        const float sv = bf16_to_f32(ss[s_read + 16 * k]);
+        const float sv = SW ? bf16_to_f32(swb[ld_row * 8 + k8]) : bf16_to_f32(ss[s_read + 16 * k]);
         const float zv = ZP ? bf16_to_f32(sz[s_read + 16 * k]) : 8.0f;
         const float zs = -(zv * sv);
         // 16 codes = two 16-byte chunks of the stage (8 columns per packed dword); per dword the
@@ -314,6 +344,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_w4a16_kernel(
     uint8_t *const sq[2] = {sq0, sq1};
     uint32_t *const ss[2] = {ss0, ss1};
     uint32_t *const sz[2] = {sz0, sz1};
+    uint16_t *const swr[3] = {sw0, sw1, sw2};
 
     // Step s (P = s % kPeriod, known at compile time): start the activations of step s + 2 and,
     // at the first step of a chunk, the next chunk; multiply from the current stages; dequantize
@@ -331,21 +362,26 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_w4a16_kernel(
         constexpr int CN = ((P + 1) / KC) % 2;  // chunk buffer of step s + 1
         dma_x(step + 2, sx[(P + 2) % 3]);
         if constexpr (K == 0) dma_chunk(step / KC + 1, sq[CB ^ 1], ss[CB ^ 1], sz[CB ^ 1]);
+        // window w covers steps 8 w .. 8 w + 7; window w + 1 is loaded at step 8 w
+        if constexpr (SW && P % 8 == 0) dma_window(step / 8 + 1, swr[(P / 8 + 1) % 3]);
         __builtin_amdgcn_sched_barrier(0);
         compute(sx[P % 3], shi[P % 2], slo[P % 2]);
-        dequant((P + 1) % KC, sq[CN], ss[CN], sz[CN], shi[(P + 1) % 2], slo[(P + 1) % 2]);
+        dequant((P + 1) % KC, sq[CN], ss[CN], sz[CN], swr[((P + 1) / 8) % 3], (P + 1) % 8,
+                shi[(P + 1) % 2], slo[(P + 1) % 2]);
         trim_x(step + 1, sx[(P + 1) % 3]);
-        constexpr int N = XI + ((K == 0 || K == 1) ? CI : 0);
+        constexpr int N = XI + ((K == 0 || K == 1) ? CI : 0) +
+                          (SW ? ((P % 8 == 0 || P % 8 == 1) ? 1 : 0) : 0);
         stage_barrier<N>();
     };
 
-    // prologue: X(0), CH(0), X(1); step 0's weights into stage 0
+    // prologue: X(0), CH(0), [SW(0)], X(1); step 0's weights into stage 0
     dma_x(0, sx0);
     dma_chunk(0, sq0, ss0, sz0);
+    if (SW) dma_window(0, sw0);
     dma_x(1, sx1);
     wait_vm_lgkm0<XI>();
     __syncthreads();
-    dequant(0, sq0, ss0, sz0, shi0, slo0);
+    dequant(0, sq0, ss0, sz0, sw0, 0, shi0, slo0);
     trim_x(0, sx0);
     __syncthreads();
 
@@ -381,7 +417,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_w4a16_kernel(
     }
 }
 
-template <int BM>
+template <int BM, bool SW>
 hipError_t launch_bm(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
                      const uint16_t *scales, const uint16_t *zeros, const uint16_t *bias,
                      int64_t d_out, int64_t d_in, int64_t k_pad, int64_t span, int64_t n_groups,
@@ -393,14 +429,20 @@ hipError_t launch_bm(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *q
     if (static_cast<int64_t>(tiles_m) * tiles_n > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
     const dim3 grid(static_cast<unsigned>(tiles_m) * static_cast<unsigned>(tiles_n));
     const int64_t row_bytes = k_pad / 2;
-    if (zeros)
-        hipLaunchKernelGGL((gemm_w4a16_kernel<BM, true>), grid, dim3(kThreads), 0, stream, x,
+    if (SW)
+        hipLaunchKernelGGL((gemm_w4a16_kernel<BM, false, SW>), grid, dim3(kThreads), 0, stream, x,
+                           static_cast<int>(M), ldx, qweight, scales, zeros, bias,
+                           static_cast<int>(d_out), static_cast<int>(d_in), row_bytes,
+                           steps_per_group, static_cast<int>(n_groups), n_steps, tiles_m, tiles_n,
+                           y, ldy, out_f32 ? 1 : 0);
+    else if (zeros)
+        hipLaunchKernelGGL((gemm_w4a16_kernel<BM, true, false>), grid, dim3(kThreads), 0, stream, x,
                            static_cast<int>(M), ldx, qweight, scales, zeros, bias,
                            static_cast<int>(d_out), static_cast<int>(d_in), row_bytes,
                            steps_per_group, static_cast<int>(n_groups), n_steps, tiles_m, tiles_n,
                            y, ldy, out_f32 ? 1 : 0);
     else
-        hipLaunchKernelGGL((gemm_w4a16_kernel<BM, false>), grid, dim3(kThreads), 0, stream, x,
+        hipLaunchKernelGGL((gemm_w4a16_kernel<BM, false, false>), grid, dim3(kThreads), 0, stream, x,
                            static_cast<int>(M), ldx, qweight, scales, zeros, bias,
                            static_cast<int>(d_out), static_cast<int>(d_in), row_bytes,
                            steps_per_group, static_cast<int>(n_groups), n_steps, tiles_m, tiles_n,
@@ -417,11 +459,20 @@ hipError_t launch_gemm(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t 
     // 256-token tiles when they still give every compute unit a block, else 128.
     const int64_t tiles_n = (d_out + BN - 1) / BN;
     const int64_t blocks256 = ((M + 255) / 256) * tiles_n;
-    if (M > 128 && blocks256 >= static_cast<int64_t>(device_cu_count()))
-        return launch_bm<256>(x, M, ldx, qweight, scales, zeros, bias, d_out, d_in, k_pad, span,
-                              n_groups, y, ldy, out_f32, stream);
-    return launch_bm<128>(x, M, ldx, qweight, scales, zeros, bias, d_out, d_in, k_pad, span,
-                          n_groups, y, ldy, out_f32, stream);
+    const bool big = M > 128 && blocks256 >= static_cast<int64_t>(device_cu_count());
+    // scale windows: symmetric 32-column groups with 16-byte aligned rows of scales
+    const bool sw = zeros == nullptr && span == BK && n_groups % 8 == 0 &&
+                    reinterpret_cast<uintptr_t>(scales) % 16 == 0;
+#define W4_GEMM_LAUNCH(BMV, SWV)                                                                  \
+    return launch_bm<BMV, SWV>(x, M, ldx, qweight, scales, zeros, bias, d_out, d_in, k_pad, span, \
+                               n_groups, y, ldy, out_f32, stream);
+    if (big) {
+        if (sw) W4_GEMM_LAUNCH(256, true)
+        W4_GEMM_LAUNCH(256, false)
+    }
+    if (sw) W4_GEMM_LAUNCH(128, true)
+    W4_GEMM_LAUNCH(128, false)
+#undef W4_GEMM_LAUNCH
 }
 
 }  // namespace w4

@@ -612,6 +612,25 @@ def test_gemm_c4_sampled_full_size():
             assert_close(y32h[t, rows], ref, f"C4/{lin.name} token {t}")
 
 
+def test_gemm_scale_windows():
+    """The GEMM's scale-window path (symmetric 32-column groups, n_groups % 8 == 0, 16-byte
+    aligned scales): a row count that leaves the last wave's 64 rows mostly empty, a window count
+    that is not a multiple of the ring, two token tiles; and the same weights with the scales at
+    an address 2 bytes past alignment, which takes the general path."""
+    M, d_out, d_in, g = 300, 200, 1280, 32
+    w = workloads.weight(71, 0, d_out, d_in)
+    ph, pd = check_pack_bit_exact(w, g, SYM, "scale windows")
+    x = workloads.activations(71, 0, M, d_in)
+    check_linear("w4_gemm", x, ph, pd, None, d_in, g, "scale windows")
+    # scales 2 bytes past a 16-byte boundary
+    ng = ph[1].shape[1]
+    buf = torch.empty(d_out * ng + 8, dtype=torch.bfloat16, device="cuda")
+    sc_off = buf[1:1 + d_out * ng].view(d_out, ng)
+    sc_off.copy_(pd[1])
+    assert sc_off.data_ptr() % 16 == 2
+    check_linear("w4_gemm", x, ph, (pd[0], sc_off, None), None, d_in, g, "scale windows off16")
+
+
 def test_gemm_matches_gemv_small_m():
     d_out, d_in, g = 300, 1024, 32
     w = workloads.weight(27, 0, d_out, d_in)
