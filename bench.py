@@ -64,6 +64,27 @@ TRAFFIC_SOURCES = ("int4_weight_only_amd/csrc/decode_i8.hip",
                    "int4_weight_only_amd/build.py")
 
 
+# the sources of the C2 down GEMV's kernel (the streaming kernel) and of its routing
+DOWN_SOURCES = ("int4_weight_only_amd/csrc/decode_stream.hip",
+                "int4_weight_only_amd/csrc/w4_device.h",
+                "int4_weight_only_amd/csrc/w4_quant.h",
+                "int4_weight_only_amd/csrc/decode.hip",
+                "int4_weight_only_amd/build.py")
+
+
+def load_trace(kernel_key, src_hash):
+    """Kernel-trace average duration (us) of a C2 GEMV from the committed rocprofv3 summary, if it
+    was measured on the current kernel source; otherwise None."""
+    path = os.path.join(ROOT, "profiles", "kernel_trace.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        entry = json.load(f).get(kernel_key)
+    if not entry or entry.get("source_hash") != src_hash:
+        return None
+    return entry.get("avg_us")
+
+
 def load_traffic(kernel_key, src_hash):
     """HBM traffic per launch from the committed PMC summary, if it was measured on the current
     kernel source; otherwise None."""
@@ -682,6 +703,8 @@ def main():
     value = r["bytes_step"] / r["step_ms"] / 1e6
     gu_gbs = r["b_gu"] / r["gu_ms"] / 1e6
     src = source_hash(*TRAFFIC_SOURCES)
+    tr_gu = load_trace("gemv_c2_gate_up", src)
+    tr_dn = load_trace("gemv_c2_down", source_hash(*DOWN_SOURCES))
     roofline = {
         "bound": "hbm",
         "kernel": "gemv_i8_kernel (C2 gate/up 37888x3584, M=1)",
@@ -692,6 +715,13 @@ def main():
         "traffic": load_traffic("gemv_c2_gate_up", src),
         "algorithmic_bytes": r["b_gu"],
         "avg_launch_us": round(r["gu_ms"] * 1e3, 3),
+        # the same kernel's average duration in the committed kernel trace (profiles/
+        # kernel_trace.json, while its sources are unchanged) and the fraction it gives
+        "trace_avg_launch_us": tr_gu,
+        "frac_trace": round(r["b_gu"] / tr_gu / 1e3 / HBM_PEAK_GBS, 4) if tr_gu else None,
+        "down_trace_avg_launch_us": tr_dn,
+        "down_frac_trace": (round(r["b_dn"] / tr_dn / 1e3 / HBM_PEAK_GBS, 4)
+                            if tr_dn else None),
         "down_avg_launch_us": round(r["dn_ms"] * 1e3, 3),
         "down_gbs": round(r["b_dn"] / r["dn_ms"] / 1e6, 1),
         **{f"stream_{k}_gbs": v for k, v in stream_ceilings_gbs(torch).items()},

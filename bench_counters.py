@@ -26,6 +26,11 @@ label and derives:
   * the kernel-trace duration, and from it the algorithmic GB/s (or TFLOP/s);
   * calibrated HBM bytes per dispatch against the algorithmic bytes.
 The summary is printed as a markdown table (profiles/ keeps it with this command line).
+
+    python3 bench_counters.py trace <dir>/run_kernel_stats.csv
+
+records the kernel-trace averages of the C2 GEMVs from `rocprofv3 --kernel-trace --stats --
+python3 bench.py --only c2 ...` in profiles/kernel_trace.json (bench.py's trace-based fraction).
 """
 import csv
 import json
@@ -296,9 +301,32 @@ def update_traffic(table):
         json.dump(data, fh, indent=2)
 
 
+def update_trace(stats_csv):
+    """Record the kernel-trace average durations of the C2 GEMVs (rocprofv3 --kernel-trace --stats
+    of `bench.py --only c2`) for bench.py's trace-based roofline fraction."""
+    from bench import DOWN_SOURCES, TRAFFIC_SOURCES, source_hash
+
+    rows = _read(stats_csv)
+    want = {"gemv_c2_gate_up": ("gemv_i8_kernel<1, false, 1, false>", TRAFFIC_SOURCES),
+            "gemv_c2_down": ("gemv_w4a16_stream_kernel<1, 5, 1, 2, false, 2, 448>", DOWN_SOURCES)}
+    out = os.path.join(ROOT, "profiles", "kernel_trace.json")
+    data = json.load(open(out)) if os.path.exists(out) else {}
+    for key, (kname, srcs) in want.items():
+        for r in rows:
+            if kname in r["Name"]:
+                data[key] = {"kernel": kname, "source_hash": source_hash(*srcs),
+                             "calls": int(r["Calls"]),
+                             "avg_us": round(float(r["AverageNs"]) / 1e3, 3),
+                             "min_us": round(float(r["MinNs"]) / 1e3, 3)}
+    with open(out, "w") as fh:
+        json.dump(data, fh, indent=2)
+
+
 if __name__ == "__main__":
     if len(sys.argv) == 3 and sys.argv[1] == "run":
         run(sys.argv[2])
+    elif len(sys.argv) == 3 and sys.argv[1] == "trace":
+        update_trace(sys.argv[2])
     elif len(sys.argv) == 7 and sys.argv[1] == "summarize":
         t = summarize(*sys.argv[2:7])
         if sys.argv[2] == "c2":
