@@ -70,6 +70,23 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Waves that share a SIMD are issued oldest first. Left alone, the older wave runs through its
+// batches while the younger one waits, and the younger one's arithmetic piles up at the end,
+// after the weight traffic has stopped. So a wave lowers its priority by one level for each
+// quarter of its n batches it has done (k of them), and the wave that is behind goes first
+// (measured on the 3584 x 18944 down projection: 8.9 against 9.3 us).
+__device__ __forceinline__ void progress_priority(int k, int n) {
+    const int q = (4 * k >= n) + (4 * k >= 2 * n) + (4 * k >= 3 * n);  // wave-uniform
+    if (q == 0)
+        __builtin_amdgcn_s_setprio(3);
+    else if (q == 1)
+        __builtin_amdgcn_s_setprio(2);
+    else if (q == 2)
+        __builtin_amdgcn_s_setprio(1);
+    else
+        __builtin_amdgcn_s_setprio(0);
+}
+
 // Batch shape: RW rows per batch and NB batches in the ring. Measured on MI355X for the 7B
 // shapes (3584 and 18944 columns), one row per batch and two buffers with 2-4 workgroups per CU
 // (a few KiB in flight per wave) beat larger batches and deeper rings: more data in flight only
@@ -123,11 +140,11 @@ __global__ void __launch_bounds__(BT) gemv_w4a16_stream_kernel(
     const Rows<RW> R(wid, d_out, BT / kWave);
 
     // lane's chunk of step t: byte offsets of its codes in a row and of its group's scale (out of
-    // range past the row end), and its activation record (the token's zero record cpr past the
-    // row end, so a chunk of zero codes adds nothing)
+    // range past the row end), and of its activation record in LDS (the token's zero record cpr
+    // past the row end, so a chunk of zero codes adds nothing; a byte offset, so that reading it
+    // takes no multiply in the loop)
     static_assert(NB % SEG == 0, "ring slots hold fixed segments");
-    uint32_t wofs[SEG][T], gofs[SEG][T];
-    int xofs[SEG][T];
+    uint32_t wofs[SEG][T], gofs[SEG][T], xofs[SEG][T];
 #pragma unroll
     for (int sg = 0; sg < SEG; ++sg)
 #pragma unroll
@@ -136,7 +153,7 @@ __global__ void __launch_bounds__(BT) gemv_w4a16_stream_kernel(
             wofs[sg][t] = c < cpr ? static_cast<uint32_t>(c * 16) : kOutOfRange;
             gofs[sg][t] =
                 c < cpr ? static_cast<uint32_t>((c >> chunk_group_shift) * 2) : kOutOfRange;
-            xofs[sg][t] = static_cast<int>(c < cpr ? c : cpr);
+            xofs[sg][t] = static_cast<uint32_t>((c < cpr ? c : cpr) * sizeof(XChunk16));
         }
 
     // Everything a batch needs, including the per-row bias of the epilogue (16-bit values have
@@ -201,9 +218,14 @@ __global__ void __launch_bounds__(BT) gemv_w4a16_stream_kernel(
             xraw[si][p] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
         }
     }
+    // The ring's first batches. With segmented (long) rows only the first is issued before the
+    // activations are converted: the activation loads then wait behind less weight traffic, and
+    // the arithmetic starts earlier (measured on the 3584 x 18944 down projection: 9.9 against
+    // 10.3 us); the rest follow the barrier below.
+    constexpr int K0 = SEG > 1 ? 1 : NB;
     Batch buf[NB];
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
+    for (int i = 0; i < K0; ++i) {
         phase_fence();
         load_batch(i / SEG, i % SEG, buf[i]);
     }
@@ -278,6 +300,12 @@ __global__ void __launch_bounds__(BT) gemv_w4a16_stream_kernel(
         xsh[(int64_t)threadIdx.x * (cpr + 1) + cpr] = zero;
     }
     lds_barrier();  // (the weight loads of the ring stay in flight)
+#pragma unroll
+    for (int i = K0; i < NB; ++i) {
+        phase_fence();
+        load_batch(i / SEG, i % SEG, buf[i]);
+    }
+    phase_fence();
 
     // ---- dequantize inside the dot products ([Lab5 融合INT4反量化与矩阵乘]):
     //   (w & 0x000F000F) | 0x6400_6400 = fp16 (1024 + c0, 1024 + c4), (w & 0x00F000F0) | ... =
@@ -304,7 +332,10 @@ __global__ void __launch_bounds__(BT) gemv_w4a16_stream_kernel(
             float xs[MT];
 #pragma unroll
             for (int m = 0; m < MT; ++m) {
-                const XChunk16 &rec = xsh[(int64_t)m * (cpr + 1) + xofs[sg][t]];
+                const XChunk16 &rec = *reinterpret_cast<const XChunk16 *>(
+                    reinterpret_cast<const unsigned char *>(xsh) +
+                    static_cast<uint32_t>(m) * static_cast<uint32_t>((cpr + 1) * sizeof(XChunk16)) +
+                    xofs[sg][t]);
 #pragma unroll
                 for (int i = 0; i < 16; ++i) xf[m][i] = as_half2(rec.h[i]);
                 xe[m] = rec.e;
@@ -415,6 +446,7 @@ __global__ void __launch_bounds__(BT) gemv_w4a16_stream_kernel(
     do {
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
+            progress_priority(b + i, b_last + 1);
             if (b + i <= b_last) compute_batch(buf[i], out, i % SEG);
             phase_fence();
             load_batch((b + i + NB) / SEG, i % SEG, buf[i]);
@@ -518,9 +550,10 @@ __global__ void __launch_bounds__(BT) gemv_w4a8_stream_kernel(
                 __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
         }
     }
+    constexpr int K0 = SEG > 1 ? 1 : NB;  // (as in the W4A16 kernel)
     Batch buf[NB];
 #pragma unroll
-    for (int i = 0; i < NB; ++i) {
+    for (int i = 0; i < K0; ++i) {
         phase_fence();
         load_batch(i / SEG, i % SEG, buf[i]);
     }
@@ -645,6 +678,12 @@ __global__ void __launch_bounds__(BT) gemv_w4a8_stream_kernel(
         qsh[(int64_t)threadIdx.x * (cpr + 1) + cpr] = zero;
     }
     lds_barrier();  // (the weight loads of the ring stay in flight)
+#pragma unroll
+    for (int i = K0; i < NB; ++i) {
+        phase_fence();
+        load_batch(i / SEG, i % SEG, buf[i]);
+    }
+    phase_fence();
 
     // sum_k (c - 8) q = sum_k c q - 8 sum_k q, exactly in int32 ([Orin INT32 accumulator 是否安全])
     struct Out {  // see the W4A16 kernel
@@ -745,6 +784,7 @@ __global__ void __launch_bounds__(BT) gemv_w4a8_stream_kernel(
     do {
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
+            progress_priority(b + i, b_last + 1);
             if (b + i <= b_last) compute_batch(buf[i], out, i % SEG);
             phase_fence();
             load_batch((b + i + NB) / SEG, i % SEG, buf[i]);
