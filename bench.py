@@ -465,13 +465,23 @@ def bench_c3(torch, w4, workloads, iters):
               for lin in cfg.linears]
         ys = [torch.empty((M, lin.d_out), dtype=torch.bfloat16, device=dev)
               for lin in cfg.linears]
+        # one workspace for every call of the step (the calls are ordered on one stream): the
+        # library splits the reduction over column slices on the few-row matrices at M >= 2
+        need = max(w4.w4_gemv_work_bytes(M, l.d_out, l.d_in, l.group_size) for l in cfg.linears)
+        work = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
 
         def step():
+            for packs in layers:
+                for lin, p, x, y in zip(cfg.linears, packs, xs, ys):
+                    w4.w4_gemv_ws(x, *p, None, lin.d_in, lin.group_size, out=y, work=work)
+
+        def step_no_workspace():
             for packs in layers:
                 for lin, p, x, y in zip(cfg.linears, packs, xs, ys):
                     w4.w4_gemv(x, *p, None, lin.d_in, lin.group_size, out=y)
 
         ms = graph_ms(torch, step, 1, iters)
+        ms_nows = graph_ms(torch, step_no_workspace, 1, iters) if need > 0 else ms
         nbytes = cfg.repeat_layers * sum(linear_bytes(M, l.d_out, l.d_in, l.group_size, True)
                                          for l in cfg.linears)
         # each linear alone (its 28 launches in one graph): per-call time and rate; their sum
@@ -480,7 +490,8 @@ def bench_c3(torch, w4, workloads, iters):
         for k, lin in enumerate(cfg.linears):
             def one(k=k, lin=lin):
                 for packs in layers:
-                    w4.w4_gemv(xs[k], *packs[k], None, lin.d_in, lin.group_size, out=ys[k])
+                    w4.w4_gemv_ws(xs[k], *packs[k], None, lin.d_in, lin.group_size, out=ys[k],
+                                  work=work)
             lms = graph_ms(torch, one, cfg.repeat_layers, iters)
             lb = linear_bytes(M, lin.d_out, lin.d_in, lin.group_size, True)
             per_lin[lin.name] = dict(us=round(lms * 1e3, 2), gbs=round(lb / lms / 1e6, 1),
@@ -488,7 +499,9 @@ def bench_c3(torch, w4, workloads, iters):
         sum_us = cfg.repeat_layers * sum(v["us"] for v in per_lin.values())
         out[f"M={M}"] = dict(step_us=round(ms * 1e3, 1), gbs=round(nbytes / ms / 1e6, 1),
                              hbm_frac=round(nbytes / ms / 1e6 / HBM_PEAK_GBS, 4),
-                             sum_of_linears_us=round(sum_us, 1), linears=per_lin)
+                             sum_of_linears_us=round(sum_us, 1), linears=per_lin,
+                             step_us_without_workspace=round(ms_nows * 1e3, 1),
+                             workspace_bytes=int(need))
     del layers
     return out
 

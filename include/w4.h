@@ -188,6 +188,38 @@ int w4_gemv(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
             int64_t d_in, int group_size, void *y, int64_t ldy, int out_dtype, void *stream);
 
 /*
+ * w4_gemv_ws -- w4_gemv with a caller-provided workspace, for 2 <= M <= 64 token rows.
+ * [Lab5 Prefill和Decode分流] (the small-M path reads every weight once per step),
+ * [Lab5 Linear形状采样] (the projections of a decoder layer: q/k/v and o have few rows, down has
+ * few rows and long ones).
+ * On matrices with fewer than four 16-row tiles per compute unit (d_out < 64 * CUs) and long
+ * rows (at least 64 KiB of codes per compute unit; groups of 128 or 256 columns or one per row),
+ * the reduction over d_in is split over column slices that run on different compute units: each
+ * slice converts only its own columns of the activations and stores fp32 partial sums in `work`,
+ * and a second kernel adds the slices in slice order (so the result is deterministic).  Other
+ * shapes run the w4_gemv path.
+ *   work        device memory of at least w4_gemv_work_bytes(M, d_out, d_in, group_size) bytes,
+ *               16-byte aligned, owned by the caller; its contents on entry do not matter and
+ *               are left undefined.  Calls that share a workspace must be ordered (one stream,
+ *               or events).  May be NULL when that size is 0.
+ *   work_bytes  its size in bytes
+ *   the other arguments as for w4_gemv, with the same result within the tolerance.
+ * Returns W4_ERR_NULL for a missing workspace, W4_ERR_RANGE for one that is too small,
+ * W4_ERR_ALIGN for a misaligned one, and otherwise the codes of w4_gemv.
+ */
+int w4_gemv_ws(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
+               const uint16_t *scales, const uint16_t *zeros, const uint16_t *bias, int64_t d_out,
+               int64_t d_in, int group_size, void *y, int64_t ldy, int out_dtype, void *work,
+               size_t work_bytes, void *stream);
+
+/*
+ * w4_gemv_work_bytes -- the workspace w4_gemv_ws needs for these sizes (0: none; also 0 for
+ * arguments w4_gemv_ws rejects): S * M * d_out * 4 bytes of partial sums for S column slices
+ * (S <= d_in / 128 + 1).  It depends only on its arguments and the device's compute-unit count.
+ */
+size_t w4_gemv_work_bytes(int64_t M, int64_t d_out, int64_t d_in, int group_size);
+
+/*
  * w4_gemv_glu -- the gate/up half of the MLP with its gate fused into the epilogue:
  *   h[m][j] = SiLU(g[m][j]) * u[m][j],  SiLU(v) = v / (1 + exp(-v)),
  *   g = x W_gate^T (+ b_gate),  u = x W_up^T (+ b_up),

@@ -16,7 +16,7 @@ import torch
 
 __all__ = [
     "W4_SYM", "W4_ASYM", "W4_OUT_BF16", "W4_OUT_F32", "W4Error", "packed_layout", "w4_pack",
-    "w4_gemv", "w4_gemv_glu", "w4_gemm", "act_quant_int8", "w4a8_gemv", "w4a8_gemm", "w4a8_linear",
+    "w4_gemv", "w4_gemv_ws", "w4_gemv_work_bytes", "w4_gemv_glu", "w4_gemm", "act_quant_int8", "w4a8_gemv", "w4a8_gemm", "w4a8_linear",
     "w4_qat_repack", "gptq_hessian", "gptq_factor", "gptq_quantize", "gptq_quantize_noalloc",
     "gptq",
     "w4_linear",
@@ -54,6 +54,9 @@ def _load(path):
     lib.w4_gptq_quantize_noalloc.argtypes = [p, i64, i64, i64, p, p, i32, i32, p, p, p, p, p]
     lin = [p, i64, i64, p, p, p, p, i64, i64, i32, p, i64, i32]
     lib.w4_gemv.argtypes = lin + [p]
+    lib.w4_gemv_ws.argtypes = lin + [p, ctypes.c_size_t, p]
+    lib.w4_gemv_work_bytes.argtypes = [i64, i64, i64, i32]
+    lib.w4_gemv_work_bytes.restype = ctypes.c_size_t
     lib.w4_gemv_glu.argtypes = lin + [p]
     lib.w4_gemm.argtypes = lin + [p]
     lib.act_quant_int8.argtypes = [p, i64, i64, i64, p, i64, p, p, p]
@@ -61,7 +64,8 @@ def _load(path):
     lib.w4a8_gemm.argtypes = lib.w4a8_gemv.argtypes
     lib.w4a8_linear.argtypes = [p, i64, i64, p, p, p, i64, i64, p, i64, i32, p, p, p]
     for f in ("w4_packed_layout", "w4_pack", "w4_qat_repack", "w4_gptq_hessian", "w4_gptq_factor",
-              "w4_gptq_quantize", "w4_gptq_quantize_noalloc", "w4_gemv", "w4_gemv_glu", "w4_gemm",
+              "w4_gptq_quantize", "w4_gptq_quantize_noalloc", "w4_gemv", "w4_gemv_ws",
+              "w4_gemv_glu", "w4_gemm",
               "act_quant_int8", "w4a8_gemv", "w4a8_gemm", "w4a8_linear"):
         getattr(lib, f).restype = i32
     lib.w4_status_string.argtypes = [i32]
@@ -274,7 +278,8 @@ def gptq(w, x, group_size, mode, alpha=0.01, d_in=None):
     return gptq_quantize(w.clone(), u, dead, group_size, mode, d_in)
 
 
-def _linear(fn_name, x, qweight, scales, zeros, bias, d_in, group_size, out_dtype, out):
+def _linear(fn_name, x, qweight, scales, zeros, bias, d_in, group_size, out_dtype, out,
+            extra=()):
     _need(x, "x", torch.bfloat16, dim=2)
     dev = x.device
     _need(qweight, "qweight", torch.uint8, dev, 2)
@@ -300,8 +305,26 @@ def _linear(fn_name, x, qweight, scales, zeros, bias, d_in, group_size, out_dtyp
     fn = getattr(_lib, fn_name)
     args = [_ptr(x), M, x.stride(0), _ptr(qweight), _ptr(scales), _ptr(zeros), _ptr(bias),
             d_out, d_in, group_size, _ptr(out), out.stride(0), out_dtype]
-    _check(fn_name, fn(*args, _stream(dev)))
+    _check(fn_name, fn(*args, *extra, _stream(dev)))
     return out
+
+
+def w4_gemv_work_bytes(M, d_out, d_in, group_size):
+    """Bytes of workspace w4_gemv_ws needs for these sizes (0: none)."""
+    return int(_lib.w4_gemv_work_bytes(M, d_out, d_in, group_size))
+
+
+def w4_gemv_ws(x, qweight, scales, zeros, bias, d_in, group_size, out_dtype=W4_OUT_BF16,
+               out=None, work=None):
+    """w4_gemv with a workspace (a device uint8 tensor of at least w4_gemv_work_bytes bytes; one
+    is allocated with torch when work is None): the reduction over d_in split over column slices
+    on matrices with few, long rows per compute unit."""
+    need = w4_gemv_work_bytes(x.shape[0], qweight.shape[0], d_in, group_size)
+    if work is None:
+        work = torch.zeros(max(need, 16), dtype=torch.uint8, device=x.device)
+    _need(work, "work", torch.uint8, x.device, 1)
+    return _linear("w4_gemv_ws", x, qweight, scales, zeros, bias, d_in, group_size, out_dtype,
+                   out, extra=(_ptr(work), work.numel()))
 
 
 def w4_gemv(x, qweight, scales, zeros, bias, d_in, group_size, out_dtype=W4_OUT_BF16, out=None):

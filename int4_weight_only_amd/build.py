@@ -12,7 +12,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libw4.so")
-SOURCES = ["abi.hip", "codec.hip", "decode.hip", "decode_i8.hip", "decode_mfma.hip",
+SOURCES = ["abi.hip", "codec.hip", "decode.hip", "decode_i8.hip", "decode_mfma.hip", "decode_split.hip",
            "decode_stream.hip", "gemm.hip", "gemm_w4a8.hip", "qat_repack.hip",
            "gptq.hip"]
 

@@ -213,6 +213,44 @@ int w4_gemv(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
     return err == hipSuccess ? W4_OK : hip_fail(err);
 }
 
+size_t w4_gemv_work_bytes(int64_t M, int64_t d_out, int64_t d_in, int group_size) {
+    if (M < 2 || M > W4_GEMV_MAX_M || check_dims(d_out, d_in) != W4_OK || d_in > kDecodeMaxDin ||
+        !valid_group(group_size))
+        return 0;
+    const Layout L = layout_of(d_in, group_size);
+    return w4::split_work_bytes(w4::plan_split(M, d_out, L.k_pad, L.span, L.n_groups), M, d_out);
+}
+
+int w4_gemv_ws(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
+               const uint16_t *scales, const uint16_t *zeros, const uint16_t *bias, int64_t d_out,
+               int64_t d_in, int group_size, void *y, int64_t ldy, int out_dtype, void *work,
+               size_t work_bytes, void *stream) {
+    if (int st = check_linear(x, M, ldx, qweight, scales, zeros, bias, d_out, d_in, group_size,
+                              y, ldy, out_dtype))
+        return st;
+    if (zeros && !aligned(zeros, 2)) return W4_ERR_ALIGN;
+    if (M > W4_GEMV_MAX_M) return W4_ERR_UNSUPPORTED;
+    if (d_in > kDecodeMaxDin) return W4_ERR_RANGE;
+    const Layout L = layout_of(d_in, group_size);
+    const w4::SplitPlan p = w4::plan_split(M, d_out, L.k_pad, L.span, L.n_groups);
+    const size_t need = w4::split_work_bytes(p, M, d_out);
+    if (need > 0) {
+        if (!work) return W4_ERR_NULL;
+        if (work_bytes < need) return W4_ERR_RANGE;
+        if (!aligned(work, 16)) return W4_ERR_ALIGN;
+    }
+    hipError_t err;
+    if (w4::gemv_split_supported(p, M, d_in, L.k_pad, ldx))
+        err = w4::launch_gemv_split(p, x, M, ldx, qweight, scales, zeros, bias, d_out, d_in,
+                                    L.k_pad, L.n_groups, work, y, ldy,
+                                    out_dtype == W4_OUT_F32, static_cast<hipStream_t>(stream));
+    else
+        err = w4::launch_gemv(x, M, ldx, qweight, scales, zeros, bias, d_out, d_in, L.k_pad,
+                              L.span, L.n_groups, y, ldy, out_dtype == W4_OUT_F32,
+                              static_cast<hipStream_t>(stream));
+    return err == hipSuccess ? W4_OK : hip_fail(err);
+}
+
 int w4_gemm(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,
             const uint16_t *scales, const uint16_t *zeros, const uint16_t *bias, int64_t d_out,
             int64_t d_in, int group_size, void *y, int64_t ldy, int out_dtype, void *stream) {

@@ -489,14 +489,16 @@ hipError_t launch_i8_t(const uint16_t *x, int64_t ldx, const uint8_t *qweight,
 // most 32 groups of 128 columns. A build with W4_TEST_HOOKS defined (the test library, never the
 // product one) also exports w4_test_force_decode_path, so that the tests can run each kernel on
 // shapes the choice gives to another: 1 = the int8 kernel wherever it applies, 2 = never it,
-// 0 = the library's choice.
+// 3 = the column-split kernel of w4_gemv_ws wherever it applies, 0 = the library's choice.
 #ifdef W4_TEST_HOOKS
 namespace {
 int g_forced_path = 0;
 }  // namespace
 int gemv_path_override() { return g_forced_path == 1 ? 1 : (g_forced_path == 2 ? -1 : 0); }
+bool split_forced() { return g_forced_path == 3; }
 #else
 int gemv_path_override() { return 0; }
+bool split_forced() { return false; }
 #endif
 
 bool gemv_i8_preferred(int64_t M, int64_t d_out, int64_t k_pad) {
@@ -568,7 +570,7 @@ hipError_t launch_gemv_i8(const uint16_t *x, int64_t M, int64_t ldx, const uint8
 
 #ifdef W4_TEST_HOOKS
 extern "C" int w4_test_force_decode_path(int path) {
-    if (path < 0 || path > 2) return 5;  // W4_ERR_RANGE
+    if (path < 0 || path > 3) return 5;  // W4_ERR_RANGE
     w4::g_forced_path = path;
     return 0;
 }

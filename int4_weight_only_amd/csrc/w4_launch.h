@@ -25,6 +25,25 @@ hipError_t launch_w4a8(const int8_t *q, const float *s_x, int64_t M, int64_t ldq
                        int64_t d_out, int64_t d_in, int64_t k_pad, void *y, int64_t ldy,
                        bool out_f32, int32_t *acc, hipStream_t stream);
 
+// Decode W4A16 for 2 <= M <= 64 on matrices with few rows per compute unit (groups of 128 or 256
+// columns or one per row), the reduction dimension split over S column slices
+// (decode_split.hip). With S > 1 the slices' fp32 partial sums go through a caller-provided
+// workspace of split_work_bytes() bytes and a second kernel adds them.
+bool split_forced();  // the test build's hook (always false in the product library)
+struct SplitPlan {
+    int tw, S, slices, xk, gshift;
+    bool ok;
+};
+SplitPlan plan_split(int64_t M, int64_t d_out, int64_t k_pad, int64_t span, int64_t n_groups);
+size_t split_work_bytes(const SplitPlan &p, int64_t M, int64_t d_out);
+bool gemv_split_supported(const SplitPlan &p, int64_t M, int64_t d_in, int64_t k_pad,
+                          int64_t ldx);
+hipError_t launch_gemv_split(const SplitPlan &p, const uint16_t *x, int64_t M, int64_t ldx,
+                             const uint8_t *qweight, const uint16_t *scales,
+                             const uint16_t *zeros, const uint16_t *bias, int64_t d_out,
+                             int64_t d_in, int64_t k_pad, int64_t n_groups, void *work, void *y,
+                             int64_t ldy, bool out_f32, hipStream_t stream);
+
 // W4A8 with the activation quantization folded into the GEMV (bf16 x in; s_x out, nullable).
 bool w4a8_linear_supported(int64_t M, int64_t k_pad);
 hipError_t launch_w4a8_linear(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,

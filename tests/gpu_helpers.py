@@ -60,8 +60,9 @@ def assert_bf16_is_rne_of_f32(y_bf16, y_f32, what=""):
 def forced_decode_path(path):
     """Run the library's test build (libw4_hooks.so: the same kernels, plus a hook on the decode
     kernel choice) with the choice forced: "i8" = the int8 matrix-core kernel wherever it applies,
-    "stream" = never it, None = the library's own choice."""
-    code = {None: 0, "i8": 1, "stream": 2}[path]
+    "stream" = never it, "split" = the column-split kernel of w4_gemv_ws wherever it applies,
+    None = the library's own choice."""
+    code = {None: 0, "i8": 1, "stream": 2, "split": 3}[path]
     prev = w4._select_library(HOOKS_LIB)
     try:
         assert w4._lib.w4_test_force_decode_path(code) == 0

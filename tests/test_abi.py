@@ -37,6 +37,9 @@ def lib():
     L.w4_gptq_quantize.argtypes = [p, i64, i64, i64, p, p, i32, i32, p, p, p, p, p, p]
     lin = [p, i64, i64, p, p, p, p, i64, i64, i32, p, i64, i32]
     L.w4_gemv.argtypes = lin + [p]
+    L.w4_gemv_ws.argtypes = lin + [p, ctypes.c_size_t, p]
+    L.w4_gemv_work_bytes.argtypes = [i64, i64, i64, i32]
+    L.w4_gemv_work_bytes.restype = ctypes.c_size_t
     L.w4_gemv_glu.argtypes = lin + [p]
     L.w4_gemm.argtypes = lin + [p]
     L.act_quant_int8.argtypes = [p, i64, i64, i64, p, i64, p, p, p]
@@ -50,7 +53,7 @@ def lib():
 
 def test_header_declares_the_five_entry_points():
     names = declared_functions()
-    for n in ("w4_pack", "w4_gemv", "w4_gemv_glu", "w4_gemm", "act_quant_int8", "w4a8_gemv",
+    for n in ("w4_pack", "w4_gemv", "w4_gemv_ws", "w4_gemv_work_bytes", "w4_gemv_glu", "w4_gemm", "act_quant_int8", "w4a8_gemv",
               "w4a8_gemm", "w4a8_linear", "w4_qat_repack", "w4_gptq_hessian", "w4_gptq_factor",
               "w4_gptq_quantize",
               "w4_packed_layout", "w4_status_string",
@@ -73,7 +76,8 @@ def test_test_hook_only_in_the_test_build(lib):
     for name in declared_functions():
         assert hasattr(h, name), name
     h.w4_test_force_decode_path.argtypes = [ctypes.c_int]
-    assert h.w4_test_force_decode_path(3) == W4_ERR_RANGE
+    assert h.w4_test_force_decode_path(4) == W4_ERR_RANGE
+    assert h.w4_test_force_decode_path(-1) == W4_ERR_RANGE
     assert h.w4_test_force_decode_path(0) == W4_OK
 
 
@@ -147,6 +151,42 @@ def test_linear_rejects_bad_arguments(lib, entry):
     assert _lin(fn, y=D + 2, out=1) == W4_ERR_ALIGN
     assert _lin(fn, zr=E + 1) == W4_ERR_ALIGN
     assert _lin(fn, d_in=(1 << 24) + 8, ldx=(1 << 24) + 8) == W4_ERR_RANGE
+
+
+def _lin_ws(lib, work, work_bytes, **kw):
+    a = dict(x=A, M=16, ldx=18944, qw=B, sc=C, zr=None, bias=None, d_out=3584, d_in=18944, g=128,
+             y=D, ldy=3584, out=0)
+    a.update(kw)
+    args = [a["x"], a["M"], a["ldx"], a["qw"], a["sc"], a["zr"], a["bias"], a["d_out"],
+            a["d_in"], a["g"], a["y"], a["ldy"], a["out"]]
+    return lib.w4_gemv_ws(*args, work, work_bytes, None)
+
+
+def test_gemv_work_bytes(lib):
+    # few rows per compute unit and 2..64 tokens: S column slices of fp32 partial sums
+    # S column slices of fp32 partial sums
+    need = lib.w4_gemv_work_bytes(16, 3584, 18944, 128)
+    assert need > 0 and need % (16 * 3584 * 4) == 0
+    assert 2 <= need // (16 * 3584 * 4) <= 18944 // 128 + 1
+    # short rows (q/k/v, o: under 64 KiB of codes per compute unit) take the w4_gemv path
+    assert lib.w4_gemv_work_bytes(16, 4608, 3584, 128) == 0
+    # one token, more than 64 tokens, many rows, invalid arguments: no workspace
+    assert lib.w4_gemv_work_bytes(1, 3584, 18944, 128) == 0
+    assert lib.w4_gemv_work_bytes(65, 3584, 18944, 128) == 0
+    assert lib.w4_gemv_work_bytes(16, 37888, 3584, 128) == 0
+    assert lib.w4_gemv_work_bytes(16, 3584, 18944, 48) == 0
+    assert lib.w4_gemv_work_bytes(16, 0, 18944, 128) == 0
+
+
+def test_gemv_ws_rejects_bad_workspaces(lib):
+    need = lib.w4_gemv_work_bytes(16, 3584, 18944, 128)
+    assert _lin_ws(lib, None, need) == W4_ERR_NULL
+    assert _lin_ws(lib, E, need - 4) == W4_ERR_RANGE
+    assert _lin_ws(lib, E + 4, need) == W4_ERR_ALIGN
+    # the checks of w4_gemv come first
+    assert _lin_ws(lib, E, need, x=None) == W4_ERR_NULL
+    assert _lin_ws(lib, E, need, M=65) == W4_ERR_UNSUPPORTED
+    assert _lin_ws(lib, E, need, g=96) == W4_ERR_GROUP
 
 
 def test_gemv_token_limit(lib):
