@@ -47,10 +47,21 @@ typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 constexpr int kTokThreads = 512;  // at most 8 waves per block
 constexpr int kTokMaxWaves = kTokThreads / kWave;
 constexpr int kTokTile = 16;      // tokens per MFMA tile
+constexpr int kTokTableBatch = 8; // table entries a thread loads before it uses them
 constexpr uint32_t kTokLdsLimit = 160 * 1024;
 // Activation offset of a lane without a token: past the input (below 2^30, host-checked), and
 // still below 2^32 with bit 31 added.
 constexpr uint32_t kTokNoToken = 0x40000000u;
+
+// Workgroup barrier for LDS-only dependencies, without a memory fence: the caller's LDS accesses
+// are completed first (lgkmcnt(0)), but the weight loads of the ring stay in flight across it
+// (a fenced barrier waits for every outstanding load).
+__device__ __forceinline__ void tok_lds_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited for
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
 
 // LDS layout (bytes): table [16 T rows][n_groups | 1] entries -- symmetric: the fp32 scale; with zero
 // points: {fp32 scale, fp16 pair -(1024 + zi), fp16 pair -(64 + zi), fp32 residual z - zi}
@@ -212,18 +223,33 @@ __global__ void __launch_bounds__(kTokThreads) gemv_tok_kernel(
     };
     zero_mine();
 
-    // ---- scale / zero-point table of the slice ----
+    // ---- scale / zero-point table of the slice: kTokTableBatch entries per thread are loaded
+    // before any is used (one round trip per batch: a loop of dependent loads took 11 us for the
+    // 148 x 28 entries of a gate/up slice) ----
     {
         const int nent = R * n_groups;
-        const uint16_t *sp = scales + (int64_t)r0 * n_groups;
-        const uint16_t *zp = ZP ? zeros + (int64_t)r0 * n_groups : nullptr;
+        const rsrc_t rs = make_rsrc(scales + (int64_t)r0 * n_groups, static_cast<uint32_t>(nent) * 2u);
+        const rsrc_t rz = make_rsrc(ZP ? zeros + (int64_t)r0 * n_groups : scales,
+                                    ZP ? static_cast<uint32_t>(nent) * 2u : 0u);
         int frac = 0;
         const int ts = tok_table_stride(n_groups);
-        for (int e = tid; e < nent; e += blockDim.x) {
+        const int stride = static_cast<int>(blockDim.x);
+        for (int e0 = tid; e0 < nent; e0 += kTokTableBatch * stride) {
+            uint32_t sv[kTokTableBatch], zv[ZP ? kTokTableBatch : 1];
+#pragma unroll
+            for (int b = 0; b < kTokTableBatch; ++b) {  // past nent: out of range, zeros
+                const uint32_t off = static_cast<uint32_t>(e0 + b * stride) * 2u;
+                sv[b] = __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0);
+                if (ZP) zv[ZP ? b : 0] = __builtin_amdgcn_raw_buffer_load_b16(rz, off, 0, 0);
+            }
+#pragma unroll
+            for (int b = 0; b < kTokTableBatch; ++b) {
+            const int e = e0 + b * stride;
+            if (e >= nent) break;
             const int te = (e / n_groups) * ts + e % n_groups;  // its slot in the table
-            const float s = bf16_to_f32(sp[e]);
+            const float s = bf16_to_f32(sv[b]);
             if (ZP) {
-                const float z = bf16_to_f32(zp[e]);
+                const float z = bf16_to_f32(zv[ZP ? b : 0]);
                 const float zi = fminf(fmaxf(__builtin_rintf(z), -1024.0f), 1024.0f);
                 const float zr = z - zi;
                 frac |= zr != 0.0f;
@@ -237,13 +263,14 @@ __global__ void __launch_bounds__(kTokThreads) gemv_tok_kernel(
             } else {
                 *reinterpret_cast<float *>(lds + L.table + 4u * te) = s;
             }
+            }
         }
         if (ZP) {
             const bool any = __builtin_amdgcn_ballot_w64(frac != 0) != 0;
             if (lane == 0) reinterpret_cast<int *>(lds + L.flags)[w] = any ? 1 : 0;
         }
     }
-    __syncthreads();
+    tok_lds_barrier();  // (the weight loads of the ring stay in flight)
     bool frac_any = false;
     if (ZP) {
         const int *fl = reinterpret_cast<const int *>(lds + L.flags);
