@@ -32,6 +32,8 @@
 // the row end reads zeros without touching memory. Every load is unconditional; a unit or pair
 // past the wave's share gets bit 31 of its offset set arithmetically (a select on a wave-uniform
 // condition becomes a branch, and the waits after it would drain the ring).
+#include <type_traits>
+
 #include "w4_device.h"
 #include "w4_launch.h"
 
@@ -47,7 +49,8 @@ typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 constexpr int kTokThreads = 512;  // at most 8 waves per block
 constexpr int kTokMaxWaves = kTokThreads / kWave;
 constexpr int kTokTile = 16;      // tokens per MFMA tile
-constexpr int kTokTableBatch = 8; // table entries a thread loads before it uses them
+constexpr int kTokTableBatch = 12;  // table entries a thread loads before it uses them
+constexpr int kTokEarlySlots = 1;   // ring slots loaded before the table is built
 constexpr uint32_t kTokLdsLimit = 160 * 1024;
 // Activation offset of a lane without a token: past the input (below 2^30, host-checked), and
 // still below 2^32 with bit 31 added.
@@ -66,9 +69,9 @@ __device__ __forceinline__ void tok_lds_barrier() {
 // LDS layout (bytes): table [16 T rows][n_groups | 1] entries -- symmetric: the fp32 scale; with zero
 // points: {fp32 scale, fp16 pair -(1024 + zi), fp16 pair -(64 + zi), fp32 residual z - zi}
 // (rows past the slice are never written: only lanes whose results are dropped read them); red
-// [W][T][64] fp32 x 4 partial sums; flags [W] (a wave's rows hold a non-integer zero point).
+// [W][T][64] fp32 x 4 partial sums.
 struct TokLds {
-    uint32_t table, red, flags, total;
+    uint32_t table, red, total;
 };
 
 __host__ __device__ inline uint32_t tok_align16(uint32_t v) { return (v + 15u) & ~15u; }
@@ -81,22 +84,35 @@ __host__ __device__ inline TokLds tok_lds(int T, int n_groups, int W, bool zp) {
     TokLds L;
     L.table = 0;
     L.red = tok_align16(16u * T * tok_table_stride(n_groups) * (zp ? 16u : 4u));
-    L.flags = L.red + static_cast<uint32_t>(W) * T * kWave * 16u;
-    L.total = L.flags + 16u * 4u;
+    L.total = L.red + static_cast<uint32_t>(W) * T * kWave * 16u;
     return L;
+}
+
+// The masks and the fp16 exponent pattern of the unpack, held in VGPRs the compiler cannot see
+// into: with them as literals it emits a separate AND and OR per dword (gfx950 has no literal
+// operands in three-operand VALU encodings), with them in registers one v_and_or_b32.
+struct DqMasks {
+    uint32_t lo, hi, magic;
+};
+
+__device__ __forceinline__ DqMasks dq_masks() {
+    DqMasks k{0x000F000Fu, 0x00F000F0u, 0x64006400u};
+    asm volatile("" : "+v"(k.lo), "+v"(k.hi), "+v"(k.magic));  // (no instruction is emitted)
+    return k;
 }
 
 // Exact fp16 (c - zi) pairs of the 8 codes of one packed dword, in the order
 // (c0, c4), (c1, c5), (c2, c6), (c3, c7).  zlo = -(1024 + zi) and zhi = -(64 + zi) as fp16 pairs.
-__device__ __forceinline__ half8_t dequant8(uint32_t w, uint32_t zlo_neg, uint32_t zhi_neg) {
-    // (plain C, not the inline-asm and_or helper: the compiler's hazard checks do not look into
-    // inline asm, and an asm write scheduled right after an MFMA can land in that MFMA's source
+__device__ __forceinline__ half8_t dequant8(uint32_t w, uint32_t zlo_neg, uint32_t zhi_neg,
+                                            const DqMasks &k) {
+    // (plain C, not an inline-asm and_or: the compiler's hazard checks do not look into inline
+    // asm, and an asm write scheduled right after an MFMA can land in that MFMA's source
     // registers before it has read them)
     const uint32_t w8 = w >> 8;
-    const uint32_t p0 = (w & 0x000F000Fu) | 0x64006400u;
-    const uint32_t p1 = (w & 0x00F000F0u) | 0x64006400u;
-    const uint32_t p2 = (w8 & 0x000F000Fu) | 0x64006400u;
-    const uint32_t p3 = (w8 & 0x00F000F0u) | 0x64006400u;
+    const uint32_t p0 = (w & k.lo) | k.magic;
+    const uint32_t p1 = (w & k.hi) | k.magic;
+    const uint32_t p2 = (w8 & k.lo) | k.magic;
+    const uint32_t p3 = (w8 & k.hi) | k.magic;
     const half2_t zl = as_half2(zlo_neg);
     const half2_t zh = as_half2(zhi_neg);
     const half2_t sixteenth = {static_cast<_Float16>(0.0625f), static_cast<_Float16>(0.0625f)};
@@ -121,12 +137,13 @@ struct XOp {
     floatx4_t sx[2];
 };
 
-// P: weight units in flight per wave, one pair's worth (at least 8 KiB): a unit's ring slot is a
-// constant in a loop body of two pairs (rings that do not match the tiles of a pair made the
-// register allocator spill); XR: pairs of activations in flight.
+// P: weight units in flight per wave; a unit's ring slot is a constant in a loop body of two
+// pairs. Two units (4 KiB a wave) beyond two tiles: the waves are bound by the dequantization
+// there, and a deeper ring only delays their first compute (C = 28, T = 10, 16 tokens: 21.0 us
+// with 2, 22.6 with 4 or 5, 22.5-23.5 with 10). XR: pairs of activations in flight.
 template <int T>
 struct TokShape {
-    static constexpr int P = T == 1 ? 2 : T == 2 ? 4 : T;
+    static constexpr int P = T == 2 ? 4 : 2;
     static constexpr int XR = T == 1 ? 2 : 1;
     static_assert((2 * T) % P == 0, "ring slots must repeat within two pairs");
 };
@@ -199,20 +216,22 @@ __global__ void __launch_bounds__(kTokThreads) gemv_tok_kernel(
 
     XRaw xr[XR];
     u32x4_t rlo[P], rhi[P];
-    auto prime = [&](int tt) {
+    auto prime_x = [&](int tt) {
 #pragma unroll
         for (int s = 0; s < XR; ++s) {
             phase_fence();
             xload(tt, s, xr[s]);
         }
+        phase_fence();
+    };
+    auto prime_w = [&](int a, int b) {  // ring slots [a, b)
 #pragma unroll
-        for (int s = 0; s < P; ++s) {
+        for (int s = a; s < b; ++s) {
             phase_fence();
             wload(s / T, s % T, rlo[s], rhi[s]);
         }
         phase_fence();
     };
-    prime(0);  // the first loads are in flight while the table is built
 
     // this wave's partial sums, [T][64] fp32 x 4 in LDS (read and written once per unit)
     float4 *red = reinterpret_cast<float4 *>(lds + L.red);
@@ -221,30 +240,29 @@ __global__ void __launch_bounds__(kTokThreads) gemv_tok_kernel(
 #pragma unroll
         for (int i = 0; i < T; ++i) mine[i * kWave] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     };
-    zero_mine();
 
-    // ---- scale / zero-point table of the slice: kTokTableBatch entries per thread are loaded
-    // before any is used (one round trip per batch: a loop of dependent loads took 11 us for the
-    // 148 x 28 entries of a gate/up slice) ----
-    {
-        const int nent = R * n_groups;
-        const rsrc_t rs = make_rsrc(scales + (int64_t)r0 * n_groups, static_cast<uint32_t>(nent) * 2u);
-        const rsrc_t rz = make_rsrc(ZP ? zeros + (int64_t)r0 * n_groups : scales,
-                                    ZP ? static_cast<uint32_t>(nent) * 2u : 0u);
-        int frac = 0;
+    // ---- scale / zero-point table of the slice, kTokTableBatch entries per thread at a time:
+    // every load of a batch is issued before any is used ----
+    const int nent = R * n_groups;
+    const rsrc_t rs = make_rsrc(scales + (int64_t)r0 * n_groups, static_cast<uint32_t>(nent) * 2u);
+    const rsrc_t rz = make_rsrc(ZP ? zeros + (int64_t)r0 * n_groups : scales,
+                                ZP ? static_cast<uint32_t>(nent) * 2u : 0u);
+    const int tstride = static_cast<int>(blockDim.x);
+    uint32_t sv[kTokTableBatch], zv[ZP ? kTokTableBatch : 1];
+    // entries e0, e0 + stride, ..., NB of them; past nent: out of range, zeros
+    auto tload = [&](auto nb, int e0) {
+#pragma unroll
+        for (int b = 0; b < decltype(nb)::value; ++b) {
+            const uint32_t off = static_cast<uint32_t>(e0 + b * tstride) * 2u;
+            sv[b] = __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0);
+            if (ZP) zv[ZP ? b : 0] = __builtin_amdgcn_raw_buffer_load_b16(rz, off, 0, 0);
+        }
+    };
+    auto tstore = [&](auto nb, int e0) {
         const int ts = tok_table_stride(n_groups);
-        const int stride = static_cast<int>(blockDim.x);
-        for (int e0 = tid; e0 < nent; e0 += kTokTableBatch * stride) {
-            uint32_t sv[kTokTableBatch], zv[ZP ? kTokTableBatch : 1];
 #pragma unroll
-            for (int b = 0; b < kTokTableBatch; ++b) {  // past nent: out of range, zeros
-                const uint32_t off = static_cast<uint32_t>(e0 + b * stride) * 2u;
-                sv[b] = __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0);
-                if (ZP) zv[ZP ? b : 0] = __builtin_amdgcn_raw_buffer_load_b16(rz, off, 0, 0);
-            }
-#pragma unroll
-            for (int b = 0; b < kTokTableBatch; ++b) {
-            const int e = e0 + b * stride;
+        for (int b = 0; b < decltype(nb)::value; ++b) {
+            const int e = e0 + b * tstride;
             if (e >= nent) break;
             const int te = (e / n_groups) * ts + e % n_groups;  // its slot in the table
             const float s = bf16_to_f32(sv[b]);
@@ -252,7 +270,6 @@ __global__ void __launch_bounds__(kTokThreads) gemv_tok_kernel(
                 const float z = bf16_to_f32(zv[ZP ? b : 0]);
                 const float zi = fminf(fmaxf(__builtin_rintf(z), -1024.0f), 1024.0f);
                 const float zr = z - zi;
-                frac |= zr != 0.0f;
                 const uint32_t hl =
                     __builtin_bit_cast(uint16_t, static_cast<_Float16>(-(1024.0f + zi)));
                 const uint32_t hh =
@@ -263,21 +280,8 @@ __global__ void __launch_bounds__(kTokThreads) gemv_tok_kernel(
             } else {
                 *reinterpret_cast<float *>(lds + L.table + 4u * te) = s;
             }
-            }
         }
-        if (ZP) {
-            const bool any = __builtin_amdgcn_ballot_w64(frac != 0) != 0;
-            if (lane == 0) reinterpret_cast<int *>(lds + L.flags)[w] = any ? 1 : 0;
-        }
-    }
-    tok_lds_barrier();  // (the weight loads of the ring stay in flight)
-    bool frac_any = false;
-    if (ZP) {
-        const int *fl = reinterpret_cast<const int *>(lds + L.flags);
-        int f = 0;
-        for (int i = 0; i < W; ++i) f |= fl[i];
-        frac_any = f != 0;
-    }
+    };
 
     auto convert = [&](int j, const XRaw &X, XOp &O) {
         const int colq = 256 * (p0 + j) + 32 * q;
@@ -341,7 +345,8 @@ __global__ void __launch_bounds__(kTokThreads) gemv_tok_kernel(
         const float pm = ldexpf(1.0f, ex);
 #pragma unroll
         for (int r = 0; r < 4; ++r) O.p[r] = __shfl(pm, 4 * q + r, kWave);
-        if (ZP && frac_any) {  // sums of the scaled activations, through a ones operand
+        if (ZP) {  // sums of the scaled activations, through a ones operand, for the residual
+                   // zero points (with none, every residual is 0 and they subtract exactly nothing)
             const half8_t ones = {1, 1, 1, 1, 1, 1, 1, 1};
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -354,8 +359,30 @@ __global__ void __launch_bounds__(kTokThreads) gemv_tok_kernel(
         }
     };
 
+    // Load order: the first activations, the first table batch and the first K0 ring slots;
+    // the first pair's activations are converted while the table is in flight, and the rest of
+    // the ring is loaded once the table is back. (Behind the whole ring the table took 10 us at
+    // C = 28, T = 10 on 256 slices: the streaming weight reads starve the scattered table reads.)
+    constexpr int K0 = kTokEarlySlots < P ? kTokEarlySlots : P;
+    using Batch = std::integral_constant<int, kTokTableBatch>;
+    prime_x(0);
+    tload(Batch{}, tid);
+    phase_fence();
+    prime_w(0, K0);
+    zero_mine();
+    XOp O;  // the converted activations of the pair in work
+    convert(0, xr[0], O);  // the first pair's, while the table is in flight
+    tstore(Batch{}, tid);
+    for (int e0 = tid + kTokTableBatch * tstride; e0 < nent; e0 += kTokTableBatch * tstride) {
+        tload(Batch{}, e0);
+        tstore(Batch{}, e0);
+    }
+    prime_w(K0, P);
+    tok_lds_barrier();  // (the weight loads of the ring stay in flight)
+
     const int ts = tok_table_stride(n_groups);
     const uint32_t t_lane = static_cast<uint32_t>(n) * ts;  // table row of lane's row n
+    const DqMasks dqk = dq_masks();
     auto compute = [&](int i, int j, const u32x4_t &wlo, const u32x4_t &whi, const XOp &O) {
         // every LDS read first (sums, both table entries), then the two chunks' MFMA chains
         // interleaved: they are independent, so neither waits for the other's results
@@ -386,7 +413,7 @@ __global__ void __launch_bounds__(kTokThreads) gemv_tok_kernel(
             for (int h = 0; h < 2; ++h) {
                 const uint32_t wd = (h ? whi : wlo)[t];
                 d[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(O.a[h][t],
-                                                              dequant8(wd, zlo[h], zhi[h]), d[h],
+                                                              dequant8(wd, zlo[h], zhi[h], dqk), d[h],
                                                               0, 0, 0);
             }
         // sum = s0 d0 + s1 d1 per token, then acc += 2^e sum
@@ -394,7 +421,7 @@ __global__ void __launch_bounds__(kTokThreads) gemv_tok_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             float v0 = d[0][r], v1 = d[1][r];
-            if (ZP && frac_any) {
+            if (ZP) {  // (zr = 0 and sx = 0 unless the block has a non-integer zero point)
                 v0 = fmaf(-zr[0], O.sx[0][r], v0);
                 v1 = fmaf(-zr[1], O.sx[1][r], v1);
             }
@@ -407,15 +434,16 @@ __global__ void __launch_bounds__(kTokThreads) gemv_tok_kernel(
     for (int tt = 0; tt < TT; ++tt) {
         if (tt > 0) {  // the previous tile's sums have been read (barrier below)
             zero_mine();
-            prime(tt);
+            prime_x(tt);
+            prime_w(0, P);
+            convert(0, xr[0], O);
         }
         // bodies of two pairs: every unit and activation slot index is a constant
         int j = 0;
         for (; j + 2 <= np; j += 2) {
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
-                XOp O;
-                convert(j + jj, xr[jj % XR], O);
+                if (jj != 0 || j > 0) convert(j + jj, xr[jj % XR], O);  // (pair 0's is done)
                 phase_fence();
                 xload(tt, j + jj + XR, xr[jj % XR]);
                 phase_fence();
@@ -434,8 +462,7 @@ __global__ void __launch_bounds__(kTokThreads) gemv_tok_kernel(
         // an odd last pair: its activations sit in slot 0 and its units in slots 0 .. T - 1
         // (j T is a multiple of P); nothing is loaded after them
         if (j < np) {
-            XOp O;
-            convert(j, xr[0], O);
+            if (j > 0) convert(j, xr[0], O);
 #pragma unroll
             for (int i = 0; i < T; ++i) compute(i, j, rlo[i % P], rhi[i % P], O);
         }

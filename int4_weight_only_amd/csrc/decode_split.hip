@@ -89,16 +89,30 @@ __host__ __device__ inline int sp_groups(int ncb, int gshift) {
     return gshift >= 30 ? 1 : ((ncb + (1 << gshift) - 1) >> gshift) + 1;
 }
 
+// The unpack's masks and fp16 exponent pattern in VGPRs the compiler cannot see into: as
+// literals they cost a separate AND and OR per dword (no literal operands in gfx950's
+// three-operand VALU encodings), in registers one v_and_or_b32.
+struct SpMasks {
+    uint32_t lo, hi, magic;
+};
+
+__device__ __forceinline__ SpMasks sp_masks() {
+    SpMasks k{0x000F000Fu, 0x00F000F0u, 0x64006400u};
+    asm volatile("" : "+v"(k.lo), "+v"(k.hi), "+v"(k.magic));  // (no instruction is emitted)
+    return k;
+}
+
 // Exact fp16 (c - zi) pairs of the 8 codes of one packed dword, in the order
 // (c0, c4), (c1, c5), (c2, c6), (c3, c7).  zlo = -(1024 + zi) and zhi = -(64 + zi) as fp16 pairs.
 // (plain C: the compiler's hazard checks do not look into inline asm, and an asm write placed
 // right after an MFMA could land in that MFMA's source registers before it has read them)
-__device__ __forceinline__ half8_t sp_dequant8(uint32_t w, uint32_t zlo_neg, uint32_t zhi_neg) {
+__device__ __forceinline__ half8_t sp_dequant8(uint32_t w, uint32_t zlo_neg, uint32_t zhi_neg,
+                                               const SpMasks &k) {
     const uint32_t w8 = w >> 8;
-    const uint32_t p0 = (w & 0x000F000Fu) | 0x64006400u;
-    const uint32_t p1 = (w & 0x00F000F0u) | 0x64006400u;
-    const uint32_t p2 = (w8 & 0x000F000Fu) | 0x64006400u;
-    const uint32_t p3 = (w8 & 0x00F000F0u) | 0x64006400u;
+    const uint32_t p0 = (w & k.lo) | k.magic;
+    const uint32_t p1 = (w & k.hi) | k.magic;
+    const uint32_t p2 = (w8 & k.lo) | k.magic;
+    const uint32_t p3 = (w8 & k.hi) | k.magic;
     const half2_t zl = as_half2(zlo_neg);
     const half2_t zh = as_half2(zhi_neg);
     const half2_t sixteenth = {static_cast<_Float16>(0.0625f), static_cast<_Float16>(0.0625f)};
@@ -347,6 +361,7 @@ __global__ void __launch_bounds__(kSpThreads) gemv_split_kernel(
     // table entry with a zero scale: its loads read zeros, and it adds exactly nothing; computing
     // it keeps the ring's loop free of branches, whose joins made the compiler wait for every
     // outstanding load)
+    const SpMasks spk = sp_masks();
     auto compute = [&](int ci, int i, const u32x4_t &wv, bool valid) {
         // the chunk's quantization group is (cb0 + ci) >> gshift
         const uint32_t te = static_cast<uint32_t>(16 * (w * TW + i) + n) * static_cast<uint32_t>(ts) +
@@ -366,7 +381,7 @@ __global__ void __launch_bounds__(kSpThreads) gemv_split_kernel(
         floatx4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[j], sp_dequant8(wv[j], zlo, zhi), d, 0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[j], sp_dequant8(wv[j], zlo, zhi, spk), d, 0, 0, 0);
         if (ZP && frac_any) {  // residual zero points, through the activations' sums
             const float *sxp = reinterpret_cast<const float *>(lds + L.sx) + ci * kSpTile + 4 * q;
 #pragma unroll
