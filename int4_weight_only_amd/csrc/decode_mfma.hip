@@ -305,15 +305,19 @@ __global__ void __launch_bounds__(kTokThreads) gemv_tok_kernel(
                     u[h][k] &= col + 1 < d_in ? 0xFFFFFFFFu : (col < d_in ? 0x0000FFFFu : 0u);
                 }
         }
-        // largest magnitude of the pair for token m: bf16 magnitude bits are monotone in |x|
-        u16x2_t m2 = {0, 0};
+        // largest magnitude of the pair for token m: bf16 and fp16 are both sign-magnitude with
+        // magnitude bits monotone in |x|, so an fp16 maximum of the raw bf16 patterns and their
+        // negations finds the largest |x| (one v_pk_maximum3_f16 per dword)
+        half2_t m2 = {0, 0};
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-            for (int k = 0; k < 16; ++k)
-                m2 = __builtin_elementwise_max(m2,
-                                               __builtin_bit_cast(u16x2_t, u[h][k] & 0x7FFF7FFFu));
-        uint32_t am = m2[0] > m2[1] ? m2[0] : m2[1];
+            for (int k = 0; k < 16; ++k) {
+                const half2_t v = as_half2(u[h][k]);
+                m2 = __builtin_elementwise_maximum(__builtin_elementwise_maximum(m2, v), -v);
+            }
+        const uint32_t mb = as_u32(m2) & 0x7FFF7FFFu;
+        uint32_t am = (mb & 0xFFFFu) > (mb >> 16) ? (mb & 0xFFFFu) : (mb >> 16);
         am = max(am, static_cast<uint32_t>(__shfl_xor(static_cast<int>(am), 16, kWave)));
         am = max(am, static_cast<uint32_t>(__shfl_xor(static_cast<int>(am), 32, kWave)));
         const float amax = __uint_as_float(am << 16);
