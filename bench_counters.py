@@ -11,7 +11,8 @@ Each counter pass is a run of its own (rocprofv3 does not split counters over pa
         <dir_sq>/pmc_kernel_trace.csv <dir_f>/pmc_counter_collection.csv <dir_w>/pmc_counter_collection.csv
 
 Workloads: c2 (the decode step's gate/up and down GEMVs at M = 1, and the gate/up GEMV with the
-SiLU * up epilogue), c3 (one decoder layer's four linears at M = 1, 8, 16), c4 (the prefill GEMMs,
+SiLU * up epilogue), c3 (one decoder layer's four linears at M = 1, 8, 16, through w4_gemv_ws as
+the bench calls them), c4 (the prefill GEMMs,
 W4A16 and W4A8, M = 2048), c5 (the W4A8 GEMVs, act_quant_int8, the fused W4A8 linear).
 
 `run` first copies a 256 MiB device buffer (known bytes: the calibration of FETCH_SIZE and
@@ -145,9 +146,13 @@ def run(workload):
                  for li, lin in enumerate(cfg.linears)]
         separator()
         for M in (1, 8, 16):
+            # the bench's calls: w4_gemv_ws with one workspace (the column split where it applies)
+            need = max(w4.w4_gemv_work_bytes(M, l.d_out, l.d_in, l.group_size) for l in cfg.linears)
+            work = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
             for li, lin in enumerate(cfg.linears):
                 x = bf16(workloads.linear_x(cfg, li, M))
-                repeat(lambda c: w4.w4_gemv(x, *c, None, lin.d_in, lin.group_size), packs[li])
+                repeat(lambda c: w4.w4_gemv_ws(x, *c, None, lin.d_in, lin.group_size, work=work),
+                       packs[li])
     elif workload == "c4":
         cfg = workloads.C4
         M = cfg.tokens[0]
@@ -188,14 +193,18 @@ def _read(path, value_field="Counter_Value"):
 
 def _runs(rows, name_field):
     """Consecutive runs of the library's dispatches (kernel names in namespace w4, the set-up
-    packs left out), split by any other dispatch; returns [(kernel name, [dispatch ids])]."""
+    packs left out), split by any other dispatch; returns [([kernel names in order of first
+    dispatch], [dispatch ids])]. A call that launches two kernels (the column-split GEMV and its
+    reduction) puts both in its label's run."""
     order = sorted({(int(r["Dispatch_Id"]), r[name_field]) for r in rows})
     runs, cur = [], None
     for did, name in order:
         if "w4::" in name and "pack_kernel" not in name:  # (the set-up packs are not timed)
             if cur is None:
-                cur = (name, [did])
+                cur = ([name], [did])
             else:
+                if name not in cur[0]:
+                    cur[0].append(name)
                 cur[1].append(did)
         elif cur is not None:
             runs.append(cur)
@@ -223,8 +232,8 @@ def summarize(workload, sq_csv, trace_csv, fetch_csv, write_csv):
         by_id = defaultdict(dict)
         for r in rows:
             by_id[int(r["Dispatch_Id"])][r["Counter_Name"]] = float(r["Counter_Value"])
-        for (lab, *_), (kname, ids) in zip(labels, runs):
-            per[lab]["kernel"] = [kname]
+        for (lab, *_), (knames, ids) in zip(labels, runs):
+            per[lab]["kernel"] = knames
             for did in ids:
                 for c, v in by_id[did].items():
                     per[lab][c].append(v)
@@ -233,12 +242,18 @@ def summarize(workload, sq_csv, trace_csv, fetch_csv, write_csv):
     dur = {}
     by_tid = {int(r["Dispatch_Id"]): (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
               for r in trace}
-    for (lab, *_), (kname, ids) in zip(labels, truns):
-        ds = sorted(by_tid[i] for i in ids)
-        dur[lab] = sum(ds) / len(ds)
+    wsum = {}  # duration-weighted means of the derived % metrics (VALUBusy, MfmaUtil)
+    sq_by_id = defaultdict(dict)
+    for r in _read(sq_csv):
+        sq_by_id[int(r["Dispatch_Id"])][r["Counter_Name"]] = float(r["Counter_Value"])
+    for (lab, *_), (knames, ids) in zip(labels, truns):
+        dur[lab] = sum(by_tid[i] for i in ids) / REPS  # per call: every kernel the call launches
+        tot = sum(by_tid[i] for i in ids)
+        wsum[lab] = {c: sum(sq_by_id[i].get(c, 0.0) * by_tid[i] for i in ids) / tot
+                     for c in ("VALUBusy", "MfmaUtil")}
     fscale = COPY_BYTES / (_copy_mean(_read(fetch_csv), "FETCH_SIZE") * 1024)
     wscale = COPY_BYTES / (_copy_mean(_read(write_csv), "WRITE_SIZE") * 1024)
-    mean = lambda v: sum(v) / len(v) if v else float("nan")
+    mean = lambda v: sum(v) / REPS if v else float("nan")  # per call (sum over its kernels)
     print(f"| call | kernel | us (trace) | rate | VALU lane-ops / weight | VALUBusy % | "
           f"MfmaUtil % | MFMA insts | LDS insts | LDS bank-conflict cycles | HBM bytes / "
           f"algorithmic |")
@@ -258,20 +273,21 @@ def summarize(workload, sq_csv, trace_csv, fetch_csv, write_csv):
         else:
             rate = f"{algo / us / 1e3:.0f} GB/s"
         ratio = hbm / algo if algo else float("nan")
-        kname = p["kernel"][0].replace("(anonymous namespace)::", "").split("(")[0]
-        kname = kname.replace("void ", "")
+        kname = " + ".join(k.replace("(anonymous namespace)::", "").split("(")[0].replace(
+            "void ", "") for k in p["kernel"])
         print(f"| {lab} | `{kname}` | {us:.2f} | {rate} | {lane_ops:.2f} | "
-              f"{mean(p['VALUBusy']):.1f} | {mean(p['MfmaUtil']):.1f} | "
+              f"{wsum[lab]['VALUBusy']:.1f} | {wsum[lab]['MfmaUtil']:.1f} | "
               f"{mean(p['SQ_INSTS_MFMA']):.0f} | {mean(p['SQ_INSTS_LDS']):.0f} | "
               f"{mean(p['SQ_LDS_BANK_CONFLICT']):.0f} | {ratio:.4f} |")
         table.append(dict(label=lab, kernel=kname, us=us, hbm_bytes=hbm, read_bytes=rd,
                           write_bytes=wr, fetch_kb_raw=mean(p["FETCH_SIZE"]),
                           write_kb_raw=mean(p["WRITE_SIZE"]), fetch_scale=fscale,
                           write_scale=wscale, dispatches=len(p["FETCH_SIZE"]),
+                          calls=REPS,
                           algorithmic_bytes=algo, flops=flops, valu_lane_ops_per_weight=lane_ops,
-                          valu_busy=mean(p["VALUBusy"]), mfma_util=mean(p["MfmaUtil"])))
+                          valu_busy=wsum[lab]["VALUBusy"], mfma_util=wsum[lab]["MfmaUtil"]))
     print(f"\nFETCH_SIZE scale {fscale:.4f}, WRITE_SIZE scale {wscale:.4f} (256 MiB copy); "
-          f"{REPS} dispatches per call")
+          f"{REPS} calls per label, counters and durations summed over the kernels of a call")
     return table
 
 

@@ -51,6 +51,7 @@ constexpr int kSpWaves = kSpThreads / kWave;
 constexpr int kSpRing = 8;                       // weight units (1 KiB each) in flight per wave
 constexpr int kSpTableLoads = 8;                 // table entries per thread
 constexpr int kSpTile = 16;                      // tokens per MFMA tile
+constexpr int kSpReduceBatch = 16;               // partial-sum loads in flight per output
 constexpr uint32_t kSpLdsLimit = 160 * 1024;
 constexpr uint32_t kSpNoToken = 0x40000000u;     // activation offset of a lane past M
 
@@ -452,22 +453,25 @@ __global__ void __launch_bounds__(kSpThreads) gemv_split_kernel(
 __global__ void __launch_bounds__(256) gemv_split_reduce_kernel(
     const float *__restrict__ part, int S, int M, int d_out, const uint16_t *__restrict__ bias,
     void *__restrict__ y, int64_t ldy, int out_f32) {
-    const int64_t total = static_cast<int64_t>(M) * d_out;
-    const int64_t idx = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    // (M d_out S 4 bytes < 2^31: the host's plan keeps the partial sums of a split that small)
+    const uint32_t total = static_cast<uint32_t>(M) * static_cast<uint32_t>(d_out);
+    const uint32_t idx = blockIdx.x * blockDim.x + threadIdx.x;
     if (idx >= total) return;
-    const int m = static_cast<int>(idx / d_out);
-    const int row = static_cast<int>(idx - static_cast<int64_t>(m) * d_out);
-    const float *p = part + idx;  // part[s][m][row] = p[s * total]
+    const int m = static_cast<int>(idx / static_cast<uint32_t>(d_out));
+    const int row = static_cast<int>(idx - static_cast<uint32_t>(m) * static_cast<uint32_t>(d_out));
+    // part[s][m][row]: the slices' partial sums of one output, kSpReduceBatch loads in flight at
+    // once (past S they read out of range, zeros), added in slice order
+    const rsrc_t rp = make_rsrc(part, static_cast<uint32_t>(S) * total * 4u);
     float v = 0.0f;
-    int s = 0;
-    for (; s + 8 <= S; s += 8) {
-        float t[8];
+    for (int s0 = 0; s0 < S; s0 += kSpReduceBatch) {
+        float t[kSpReduceBatch];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) t[k] = p[(s + k) * total];
+        for (int k = 0; k < kSpReduceBatch; ++k)
+            t[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(
+                rp, (static_cast<uint32_t>(s0 + k) * total + idx) * 4u, 0, 0));
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v += t[k];
+        for (int k = 0; k < kSpReduceBatch; ++k) v += t[k];
     }
-    for (; s < S; ++s) v += p[s * total];
     if (bias) v += bf16_to_f32(bias[row]);
     store_out(y, static_cast<int64_t>(m) * ldy + row, v, out_f32 != 0);
 }
@@ -572,6 +576,8 @@ bool gemv_split_supported(const SplitPlan &p, int64_t M, int64_t d_in, int64_t k
     // and units past a share step one chunk further) and the activations
     if (int64_t(16) * p.tw * kSpWaves * (k_pad / 2) + 2 * (k_pad / 2) + 1024 >= (int64_t)kOutOfRange)
         return false;
+    // the reduction's descriptor spans every partial sum
+    if (int64_t(p.S) * M * p.slices * 16 * p.tw * kSpWaves * 4 >= (int64_t)kOutOfRange) return false;
     return d_in <= k_pad && (M * ldx + 1024) * 2 < (int64_t)kSpNoToken;
 }
 
