@@ -12,8 +12,8 @@ Each counter pass is a run of its own (rocprofv3 does not split counters over pa
 
 Workloads: c2 (the decode step's gate/up and down GEMVs at M = 1, and the gate/up GEMV with the
 SiLU * up epilogue), c3 (one decoder layer's four linears at M = 1, 8, 16, through w4_gemv_ws as
-the bench calls them), c4 (the prefill GEMMs,
-W4A16 and W4A8, M = 2048), c5 (the W4A8 GEMVs, act_quant_int8, the fused W4A8 linear).
+the bench calls them), c4 (the prefill GEMMs, W4A16 and W4A8, M = 2048), c5 (the W4A8 GEMVs,
+act_quant_int8, the fused W4A8 linear).
 
 `run` first copies a 256 MiB device buffer (known bytes: the calibration of FETCH_SIZE and
 WRITE_SIZE, whose units this part counts differently), then launches each labelled call of the
