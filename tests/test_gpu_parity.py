@@ -559,6 +559,21 @@ def test_gemv_c3_layers():
                              f"C3/L{layer}/{lin.name} M={M}")
 
 
+def test_gemv_c3_gate_up_two_and_three_tokens():
+    """The C3 gate/up shape at M = 2 and 3, which the library gives to the int8 digit kernel
+    (tall matrix of short rows), through w4_gemv and w4_gemv_ws."""
+    cfg = workloads.C3
+    li = [lin.name for lin in cfg.linears].index("gate_up")
+    lin = cfg.linears[li]
+    w = workloads.linear_weight(cfg, li)
+    ph, pd = check_pack_bit_exact(w, lin.group_size, lin.mode, "C3/gate_up")
+    for M in (2, 3):
+        x = workloads.linear_x(cfg, li, M)
+        check_linear("w4_gemv", x, ph, pd, None, lin.d_in, lin.group_size, f"C3/gate_up M={M}")
+        check_linear("w4_gemv_ws", x, ph, pd, None, lin.d_in, lin.group_size,
+                     f"C3/gate_up ws M={M}")
+
+
 def test_gemv_all_token_counts():
     d_out, d_in, g = 200, 520, 64
     w = workloads.weight(26, 0, d_out, d_in)
