@@ -131,10 +131,11 @@ struct XRaw {
 
 // The converted pair: MFMA operands, the factors 2^e of the tokens whose D rows this lane holds,
 // and (for non-integer zero points) the sums of the scaled activations.
+template <int GPC>
 struct XOp {
     half8_t a[2][4];
     float p[4];
-    floatx4_t sx[2];
+    floatx4_t sx[2];  // (one group per chunk only; with more, the units take the sums themselves)
 };
 
 // P: weight units in flight per wave; a unit's ring slot is a constant in a loop body of two
@@ -148,7 +149,23 @@ struct TokShape {
     static_assert((2 * T) % P == 0, "ring slots must repeat within two pairs");
 };
 
-template <int T, bool ZP>
+// A 4 x 4 transpose of dwords across the four 16-lane rows of a wave: on return, v[t] of row r
+// holds what v[r] of row t held (two v_permlane32_swap, then two v_permlane16_swap).
+__device__ __forceinline__ void row_transpose4(u32x4_t &v) {
+    const auto a = __builtin_amdgcn_permlane32_swap(v[0], v[2], false, false);
+    const auto b = __builtin_amdgcn_permlane32_swap(v[1], v[3], false, false);
+    const auto c = __builtin_amdgcn_permlane16_swap(a[0], b[0], false, false);
+    const auto d = __builtin_amdgcn_permlane16_swap(a[1], b[1], false, false);
+    v[0] = c[0];
+    v[1] = c[1];
+    v[2] = d[0];
+    v[3] = d[1];
+}
+
+// GPC: quantization groups per 128-column chunk (1 for groups of 128, 256 or a whole row; 2 for
+// 64; 4 for 32). With GPC > 1 a lane's loads are transposed across the four 16-lane rows so that
+// each MFMA's 32 columns lie in one group: lane (n, q) of MFMA t holds columns 32 t + 8 q .. + 7.
+template <int T, bool ZP, int GPC>
 __global__ void __launch_bounds__(kTokThreads) gemv_tok_kernel(
     const uint16_t *__restrict__ x, int64_t ldx, int M, int d_in,
     const uint8_t *__restrict__ qweight, const uint16_t *__restrict__ scales,
@@ -202,8 +219,10 @@ __global__ void __launch_bounds__(kTokThreads) gemv_tok_kernel(
     auto xload = [&](int tt, int j, XRaw &X) {
         const uint32_t past = static_cast<uint32_t>((np - 1 - j) >> 31) << 31;
         const int token = tt * kTokTile + n;
+        // (GPC > 1: piece t of a lane is columns 32 t + 8 q .. + 7 of the chunk, else 32 q + 8 t)
+        constexpr uint32_t kLaneStep = GPC > 1 ? 16u : 64u, kPieceStep = GPC > 1 ? 64u : 16u;
         const uint32_t x_lane =
-            token < M ? static_cast<uint32_t>(token) * static_cast<uint32_t>(ldx) * 2u + 64u * q
+            token < M ? static_cast<uint32_t>(token) * static_cast<uint32_t>(ldx) * 2u + kLaneStep * q
                       : kTokNoToken;
         const uint32_t u = uni((512u * static_cast<uint32_t>(p0 + j)) | past);
 #pragma unroll
@@ -211,7 +230,7 @@ __global__ void __launch_bounds__(kTokThreads) gemv_tok_kernel(
 #pragma unroll
             for (int t = 0; t < 4; ++t)
                 X.v[h][t] = __builtin_amdgcn_raw_buffer_load_b128(
-                    rx, x_lane + u + static_cast<uint32_t>(256 * h + 16 * t), 0, 0);
+                    rx, x_lane + u + static_cast<uint32_t>(256 * h) + kPieceStep * t, 0, 0);
     };
 
     XRaw xr[XR];
@@ -283,8 +302,8 @@ __global__ void __launch_bounds__(kTokThreads) gemv_tok_kernel(
         }
     };
 
-    auto convert = [&](int j, const XRaw &X, XOp &O) {
-        const int colq = 256 * (p0 + j) + 32 * q;
+    auto convert = [&](int j, const XRaw &X, XOp<GPC> &O) {
+        const int colq = 256 * (p0 + j) + (GPC > 1 ? 8 : 32) * q;
         uint32_t u[2][16];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -301,7 +320,7 @@ __global__ void __launch_bounds__(kTokThreads) gemv_tok_kernel(
             for (int h = 0; h < 2; ++h)
 #pragma unroll
                 for (int k = 0; k < 16; ++k) {
-                    const int col = colq + 128 * h + 8 * (k >> 2) + 2 * (k & 3);
+                    const int col = colq + 128 * h + (GPC > 1 ? 32 : 8) * (k >> 2) + 2 * (k & 3);
                     u[h][k] &= col + 1 < d_in ? 0xFFFFFFFFu : (col < d_in ? 0x0000FFFFu : 0u);
                 }
         }
@@ -355,9 +374,11 @@ __global__ void __launch_bounds__(kTokThreads) gemv_tok_kernel(
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 floatx4_t s = {0.0f, 0.0f, 0.0f, 0.0f};
+                if constexpr (GPC == 1) {
 #pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    s = __builtin_amdgcn_mfma_f32_16x16x32_f16(O.a[h][t], ones, s, 0, 0, 0);
+                    for (int t = 0; t < 4; ++t)
+                        s = __builtin_amdgcn_mfma_f32_16x16x32_f16(O.a[h][t], ones, s, 0, 0, 0);
+                }
                 O.sx[h] = s;
             }
         }
@@ -374,7 +395,7 @@ __global__ void __launch_bounds__(kTokThreads) gemv_tok_kernel(
     phase_fence();
     prime_w(0, K0);
     zero_mine();
-    XOp O;  // the converted activations of the pair in work
+    XOp<GPC> O;  // the converted activations of the pair in work
     convert(0, xr[0], O);  // the first pair's, while the table is in flight
     tstore(Batch{}, tid);
     for (int e0 = tid + kTokTableBatch * tstride; e0 < nent; e0 += kTokTableBatch * tstride) {
@@ -387,49 +408,112 @@ __global__ void __launch_bounds__(kTokThreads) gemv_tok_kernel(
     const int ts = tok_table_stride(n_groups);
     const uint32_t t_lane = static_cast<uint32_t>(n) * ts;  // table row of lane's row n
     const DqMasks dqk = dq_masks();
-    auto compute = [&](int i, int j, const u32x4_t &wlo, const u32x4_t &whi, const XOp &O) {
-        // every LDS read first (sums, both table entries), then the two chunks' MFMA chains
+    auto compute = [&](int i, int j, const u32x4_t &wlo_in, const u32x4_t &whi_in,
+                       const XOp<GPC> &O) {
+        // every LDS read first (sums, the table entries), then the two chunks' MFMA chains
         // interleaved: they are independent, so neither waits for the other's results
         const float4 a4 = mine[i * kWave];
-        float sc[2];
-        uint32_t zlo[2] = {0xE408E408u, 0xE408E408u};  // -(1024 + 8) as an fp16 pair
-        uint32_t zhi[2] = {0xD480D480u, 0xD480D480u};  // -(64 + 8)
-        float zr[2] = {0.0f, 0.0f};
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            int G = (2 * (p0 + j) + h) >> gshift;
-            G = G < n_groups ? G : n_groups - 1;  // past the last chunk: x is zero there
-            const uint32_t e = t_lane + uni(static_cast<uint32_t>(16 * i * ts + G));
-            if (ZP) {
-                const u32x4_t ent = *reinterpret_cast<const u32x4_t *>(lds + L.table + 16u * e);
-                sc[h] = __uint_as_float(ent.x);
-                zlo[h] = ent.y;
-                zhi[h] = ent.z;
-                zr[h] = __uint_as_float(ent.w);
-            } else {
-                sc[h] = *reinterpret_cast<const float *>(lds + L.table + 4u * e);
-            }
+        u32x4_t wlo = wlo_in, whi = whi_in;
+        if constexpr (GPC > 1) {  // piece t of lane (n, q): columns 32 t + 8 q .. + 7
+            row_transpose4(wlo);
+            row_transpose4(whi);
         }
-        floatx4_t d[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
+        float acc[4] = {a4.x, a4.y, a4.z, a4.w};
+        if constexpr (GPC == 1) {
+            float sc[2];
+            uint32_t zlo[2] = {0xE408E408u, 0xE408E408u};  // -(1024 + 8) as an fp16 pair
+            uint32_t zhi[2] = {0xD480D480u, 0xD480D480u};  // -(64 + 8)
+            float zr[2] = {0.0f, 0.0f};
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                const uint32_t wd = (h ? whi : wlo)[t];
-                d[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(O.a[h][t],
-                                                              dequant8(wd, zlo[h], zhi[h], dqk), d[h],
-                                                              0, 0, 0);
+                int G = (2 * (p0 + j) + h) >> gshift;
+                G = G < n_groups ? G : n_groups - 1;  // past the last chunk: x is zero there
+                const uint32_t e = t_lane + uni(static_cast<uint32_t>(16 * i * ts + G));
+                if (ZP) {
+                    const u32x4_t ent =
+                        *reinterpret_cast<const u32x4_t *>(lds + L.table + 16u * e);
+                    sc[h] = __uint_as_float(ent.x);
+                    zlo[h] = ent.y;
+                    zhi[h] = ent.z;
+                    zr[h] = __uint_as_float(ent.w);
+                } else {
+                    sc[h] = *reinterpret_cast<const float *>(lds + L.table + 4u * e);
+                }
             }
-        // sum = s0 d0 + s1 d1 per token, then acc += 2^e sum
-        float acc[4] = {a4.x, a4.y, a4.z, a4.w};
+            floatx4_t d[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            float v0 = d[0][r], v1 = d[1][r];
-            if (ZP) {  // (zr = 0 and sx = 0 unless the block has a non-integer zero point)
-                v0 = fmaf(-zr[0], O.sx[0][r], v0);
-                v1 = fmaf(-zr[1], O.sx[1][r], v1);
+            for (int t = 0; t < 4; ++t)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t wd = (h ? whi : wlo)[t];
+                    d[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        O.a[h][t], dequant8(wd, zlo[h], zhi[h], dqk), d[h], 0, 0, 0);
+                }
+            // sum = s0 d0 + s1 d1 per token, then acc += 2^e sum
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                float v0 = d[0][r], v1 = d[1][r];
+                if (ZP) {  // (zr = 0 unless the zero point is not an integer)
+                    v0 = fmaf(-zr[0], O.sx[0][r], v0);
+                    v1 = fmaf(-zr[1], O.sx[1][r], v1);
+                }
+                acc[r] = fmaf(O.p[r], fmaf(sc[1], v1, sc[0] * v0), acc[r]);
             }
-            acc[r] = fmaf(O.p[r], fmaf(sc[1], v1, sc[0] * v0), acc[r]);
+        } else {
+            // one chunk at a time: its GPC groups are GPC independent MFMA chains already
+            constexpr int kPer = 4 / GPC;  // MFMA pieces per group
+            float sum[4];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                float sc[GPC], zr[GPC];
+                uint32_t zlo[GPC], zhi[GPC];
+#pragma unroll
+                for (int g = 0; g < GPC; ++g) {
+                    zlo[g] = 0xE408E408u;
+                    zhi[g] = 0xD480D480u;
+                    zr[g] = 0.0f;
+                    int G = (2 * (p0 + j) + h) * GPC + g;
+                    G = G < n_groups ? G : n_groups - 1;  // past the last group: x is zero there
+                    const uint32_t e = t_lane + uni(static_cast<uint32_t>(16 * i * ts + G));
+                    if (ZP) {
+                        const u32x4_t ent =
+                            *reinterpret_cast<const u32x4_t *>(lds + L.table + 16u * e);
+                        sc[g] = __uint_as_float(ent.x);
+                        zlo[g] = ent.y;
+                        zhi[g] = ent.z;
+                        zr[g] = __uint_as_float(ent.w);
+                    } else {
+                        sc[g] = *reinterpret_cast<const float *>(lds + L.table + 4u * e);
+                    }
+                }
+                floatx4_t d[GPC], sx[GPC];
+                const half8_t ones = {1, 1, 1, 1, 1, 1, 1, 1};
+#pragma unroll
+                for (int g = 0; g < GPC; ++g) {
+                    d[g] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                    sx[g] = floatx4_t{0.0f, 0.0f, 0.0f, 0.0f};
+                }
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int g = t / kPer;
+                    const uint32_t wd = (h ? whi : wlo)[t];
+                    d[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                        O.a[h][t], dequant8(wd, zlo[g], zhi[g], dqk), d[g], 0, 0, 0);
+                    if (ZP)  // the group's sums of the scaled activations, for a residual zr
+                        sx[g] = __builtin_amdgcn_mfma_f32_16x16x32_f16(O.a[h][t], ones, sx[g], 0,
+                                                                       0, 0);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+#pragma unroll
+                    for (int g = 0; g < GPC; ++g) {
+                        float v = d[g][r];
+                        if (ZP) v = fmaf(-zr[g], sx[g][r], v);  // (zr = 0 for integer z)
+                        sum[r] = (h == 0 && g == 0) ? sc[g] * v : fmaf(sc[g], v, sum[r]);
+                    }
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[r] = fmaf(O.p[r], sum[r], acc[r]);
         }
         mine[i * kWave] = make_float4(acc[0], acc[1], acc[2], acc[3]);
     };
@@ -558,14 +642,14 @@ TokPlan plan_tok(int64_t d_out, int64_t k_pad, int64_t n_groups, bool zp) {
     return p;
 }
 
-template <int T, bool ZP>
+template <int T, bool ZP, int GPC>
 hipError_t launch_tok_t(const TokPlan &p, const uint16_t *x, int64_t ldx, int64_t M, int64_t d_in,
                         const uint8_t *qweight, const uint16_t *scales, const uint16_t *zeros,
                         const uint16_t *bias, int64_t d_out, int64_t k_pad, int64_t n_groups,
                         int gshift, void *y, int64_t ldy, bool out_f32, hipStream_t stream) {
     const size_t lds = tok_lds(T, static_cast<int>(n_groups), p.W, ZP).total;
     const int C = static_cast<int>((k_pad + 127) / 128);
-    hipLaunchKernelGGL((gemv_tok_kernel<T, ZP>), dim3(p.blocks), dim3(p.W * kWave), lds, stream, x,
+    hipLaunchKernelGGL((gemv_tok_kernel<T, ZP, GPC>), dim3(p.blocks), dim3(p.W * kWave), lds, stream, x,
                        ldx, static_cast<int>(M), static_cast<int>(d_in), qweight, scales, zeros,
                        bias, static_cast<int>(d_out), static_cast<int>(k_pad / 2),
                        static_cast<int>(n_groups), gshift, C, p.rows_per_block, y, ldy,
@@ -573,15 +657,16 @@ hipError_t launch_tok_t(const TokPlan &p, const uint16_t *x, int64_t ldx, int64_
     return hipGetLastError();
 }
 
-template <bool ZP>
+template <bool ZP, int GPC>
 hipError_t launch_tok_zp(const TokPlan &p, const uint16_t *x, int64_t ldx, int64_t M, int64_t d_in,
                          const uint8_t *qweight, const uint16_t *scales, const uint16_t *zeros,
                          const uint16_t *bias, int64_t d_out, int64_t k_pad, int64_t n_groups,
                          int gshift, void *y, int64_t ldy, bool out_f32, hipStream_t stream) {
 #define W4_TOK_CASE(TV)                                                                          \
     case TV:                                                                                     \
-        return launch_tok_t<TV, ZP>(p, x, ldx, M, d_in, qweight, scales, zeros, bias, d_out,    \
-                                    k_pad, n_groups, gshift, y, ldy, out_f32, stream);
+        return launch_tok_t<TV, ZP, GPC>(p, x, ldx, M, d_in, qweight, scales, zeros, bias,      \
+                                         d_out,                                                  \
+                                         k_pad, n_groups, gshift, y, ldy, out_f32, stream);
     switch (p.T) {
         W4_TOK_CASE(1)
         W4_TOK_CASE(2)
@@ -603,8 +688,9 @@ hipError_t launch_tok_zp(const TokPlan &p, const uint16_t *x, int64_t ldx, int64
 bool gemv_mfma_supported(int64_t M, int64_t d_out, int64_t d_in, int64_t k_pad, int64_t span,
                          int64_t n_groups, int64_t ldx, bool zp) {
     if (M < 2 || M > 64 || d_out < 1 || d_in < 1) return false;
-    // a group must cover whole 128-column chunks (128 or 256), or be the whole row
-    if (n_groups != 1 && span != 128 && span != 256) return false;
+    // a group covers whole 128-column chunks (128 or 256), is the whole row, or divides a chunk
+    // (32 or 64: the lanes' pieces are then transposed so that an MFMA stays in one group)
+    if (n_groups != 1 && span != 32 && span != 64 && span != 128 && span != 256) return false;
     if (d_in > k_pad || k_pad % 32 != 0) return false;
     const TokPlan p = plan_tok(d_out, k_pad, n_groups, zp);
     if (!p.ok) return false;
@@ -624,11 +710,19 @@ hipError_t launch_gemv_mfma(const uint16_t *x, int64_t M, int64_t ldx, const uin
     const TokPlan p = plan_tok(d_out, k_pad, n_groups, zp);
     if (!p.ok) return hipErrorInvalidValue;
     const int gshift = n_groups == 1 ? 30 : (span == 256 ? 1 : 0);
-    if (zp)
-        return launch_tok_zp<true>(p, x, ldx, M, d_in, qweight, scales, zeros, bias, d_out, k_pad,
-                                   n_groups, gshift, y, ldy, out_f32, stream);
-    return launch_tok_zp<false>(p, x, ldx, M, d_in, qweight, scales, zeros, bias, d_out, k_pad,
-                                n_groups, gshift, y, ldy, out_f32, stream);
+    const int gpc = n_groups == 1 || span >= 128 ? 1 : static_cast<int>(128 / span);
+#define W4_TOK_GPC(ZPV, GV)                                                                       \
+    return launch_tok_zp<ZPV, GV>(p, x, ldx, M, d_in, qweight, scales, zeros, bias, d_out, k_pad, \
+                                  n_groups, gshift, y, ldy, out_f32, stream);
+    if (zp) {
+        if (gpc == 4) W4_TOK_GPC(true, 4)
+        if (gpc == 2) W4_TOK_GPC(true, 2)
+        W4_TOK_GPC(true, 1)
+    }
+    if (gpc == 4) W4_TOK_GPC(false, 4)
+    if (gpc == 2) W4_TOK_GPC(false, 2)
+    W4_TOK_GPC(false, 1)
+#undef W4_TOK_GPC
 }
 
 }  // namespace w4

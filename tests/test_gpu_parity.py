@@ -657,11 +657,13 @@ def test_gemm_matches_gemv_small_m():
 
 
 @pytest.mark.parametrize("entry", ["w4_gemv", "w4_gemm"])
-def test_linear_zero_points_beyond_pack(entry):
+@pytest.mark.parametrize("g", [128, 64, 32])
+def test_linear_zero_points_beyond_pack(entry, g):
     """Zero points that w4_pack never writes (non-integers, beyond the code range, negative,
     large) still follow w = s (c - z): every decode kernel (forced where one token would pick
-    another) and the GEMM against the oracle, which takes z as given."""
-    d_out, d_in, g = 300, 1000, 128
+    another) and the GEMM against the oracle, which takes z as given. Groups of 128, and of 64
+    and 32 (several groups per 128-column chunk in the few-token kernel)."""
+    d_out, d_in = 300, 1000
     w = workloads.weight(29, 0, d_out, d_in)
     ph, pd = check_pack_bit_exact(w, g, ASYM, "zero points beyond pack")
     rng = np.random.default_rng(29)
@@ -671,7 +673,7 @@ def test_linear_zero_points_beyond_pack(entry):
     ph2 = (ph[0], ph[1], zb)
     pd2 = (pd[0], pd[1], dev_bf16(zb))
     b = workloads.bias(29, 1, d_out)
-    paths = (None, "i8", "stream") if entry == "w4_gemv" else (None,)
+    paths = (None, "i8", "stream") if entry == "w4_gemv" and g == 128 else (None,)
     for path in paths:
         with forced_decode_path(path):
             for M in (1, 2, 5, 16):
@@ -1086,8 +1088,8 @@ def test_w4a8_worst_case_accumulator(H):
 def test_w4a16_activation_outlier_channels(scale, mode):
     """1% of the input channels scaled (x20, as in C5, and x3000), the same channels for every
     token, against O4: the int8 decode kernel forced onto 1-4 tokens (groups 128 and per row),
-    the streaming kernel at one token (forced), the few-token matrix-core kernel (8 and 16
-    tokens), the per-row kernel (32-column groups, 2-5 tokens) and the GEMM."""
+    the streaming kernel at one token (forced), the few-token matrix-core kernel (2-16 tokens;
+    with 32-column groups in its transposed layout) and the GEMM."""
     d_out, d_in = 640, 3584
     w = workloads.weight(51, mode, d_out, d_in)
     workloads.add_weight_outliers(w, 51, mode, 1e-3, 0.5)
