@@ -506,6 +506,42 @@ def bench_c3(torch, w4, workloads, iters):
     return out
 
 
+def bench_decode_g32(torch, w4, workloads, iters):
+    """Decode at 1, 8 and 16 tokens on the C4 shapes with 32-column symmetric groups (the format
+    the QAT page's repack produces), each linear over rotated weight copies in one HIP graph:
+    per-call time and rate (timing only; parity of g32 decode is in the GPU tests)."""
+    cfg = workloads.C4
+    dev = torch.device("cuda", 0)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(cfg.seed + 32)
+    copies = 6
+    out = {}
+    for lin in cfg.linears:
+        packs = []
+        for _ in range(copies):
+            w = torch.randn((lin.d_out, lin.d_in), generator=gen, device=dev) * workloads.W_SIGMA
+            packs.append(w4.w4_pack(w, lin.group_size, lin.mode))
+            del w
+        r = {}
+        for M in (1, 8, 16):
+            x = torch.randn((M, lin.d_in), generator=gen, device=dev).to(torch.bfloat16)
+            y = torch.empty((M, lin.d_out), dtype=torch.bfloat16, device=dev)
+            need = w4.w4_gemv_work_bytes(M, lin.d_out, lin.d_in, lin.group_size)
+            work = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+
+            def body(x=x, y=y, work=work):
+                for p in packs:
+                    w4.w4_gemv_ws(x, *p, None, lin.d_in, lin.group_size, out=y, work=work)
+
+            ms = graph_ms(torch, body, copies, iters)
+            b = linear_bytes(M, lin.d_out, lin.d_in, lin.group_size, False)
+            r[f"M={M}"] = dict(us=round(ms * 1e3, 2), gbs=round(b / ms / 1e6, 1),
+                               hbm_frac=round(b / ms / 1e6 / HBM_PEAK_GBS, 4))
+        out[f"{lin.name} {lin.d_out}x{lin.d_in}"] = r
+        del packs
+    return out
+
+
 def host_cpu():
     """The host's CPU model (from /proc/cpuinfo) and logical CPU count."""
     model = "unknown"
@@ -657,7 +693,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=12.0)
-    ap.add_argument("--only", choices=["c1", "c2", "c3", "c4", "c5", "qat", "gptq"],
+    ap.add_argument("--only", choices=["c1", "c2", "c3", "c4", "c5", "qat", "gptq", "g32"],
                     default=None,
                     help="time one workload only (for profiling runs)")
     args = ap.parse_args()
@@ -692,6 +728,8 @@ def main():
             secondary["qat_repack"] = bench_qat(torch, w4, workloads, 10)
         elif args.only == "gptq":
             secondary["gptq"] = bench_gptq(torch, w4, workloads, 3)
+        elif args.only == "g32":
+            secondary["decode_g32"] = bench_decode_g32(torch, w4, workloads, 10)
         if args.only != "c2":
             print(json.dumps(secondary), flush=True)
             return
@@ -704,6 +742,8 @@ def main():
         secondary["C5_w4a8"] = bench_c5(torch, w4, workloads, 100)
         log("C3 decoder step")
         secondary["C3_decoder_step"] = bench_c3(torch, w4, workloads, 5)
+        log("decode with 32-column groups")
+        secondary["decode_g32"] = bench_decode_g32(torch, w4, workloads, 10)
         log("QAT repack")
         secondary["qat_repack"] = bench_qat(torch, w4, workloads, 10)
         log("GPTQ")
