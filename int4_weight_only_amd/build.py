@@ -13,7 +13,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libw4.so")
 SOURCES = ["abi.hip", "codec.hip", "decode.hip", "decode_i8.hip", "decode_mfma.hip", "decode_split.hip",
-           "decode_stream.hip", "gemm.hip", "gemm_w4a8.hip", "qat_repack.hip",
+           "decode_stream.hip", "decode_w4a8_mfma.hip", "gemm.hip", "gemm_w4a8.hip", "qat_repack.hip",
            "gptq.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

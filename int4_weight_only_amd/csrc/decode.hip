@@ -584,6 +584,10 @@ hipError_t launch_w4a8(const int8_t *q, const float *s_x, int64_t M, int64_t ldq
                        const uint8_t *qweight, const uint16_t *s_w, const uint16_t *bias,
                        int64_t d_out, int64_t d_in, int64_t k_pad, void *y, int64_t ldy,
                        bool out_f32, int32_t *acc, hipStream_t stream) {
+    // two or more tokens: the matrix-core kernel reads the weights once per 16 of them
+    if (w4a8_tok_supported(M, d_out, d_in, k_pad, ldq))
+        return launch_w4a8_tok(q, s_x, M, ldq, qweight, s_w, bias, d_out, d_in, k_pad, y, ldy,
+                               out_f32, acc, stream);
     if (w4a8_stream_supported(M, k_pad, false))  // see launch_gemv
         return launch_w4a8_stream(q, false, const_cast<float *>(s_x), M, ldq, qweight, s_w, bias,
                                   d_out, d_in, k_pad, y, ldy, out_f32, acc, stream);

@@ -102,6 +102,13 @@ hipError_t launch_w4a8_stream(const void *act, bool fused_quant, float *s_x, int
 
 // Few-token decode on the fp16 matrix cores (decode_mfma.hip): activations converted inside
 // each block, one pass over the weights for all tokens of a 16-token tile; no workspace.
+// W4A8 decode for 2..64 tokens on the int8 matrix cores (decode_w4a8_mfma.hip): the weights are
+// read once per 16 tokens; same y and acc as the streaming kernel
+bool w4a8_tok_supported(int64_t M, int64_t d_out, int64_t d_in, int64_t k_pad, int64_t ldq);
+hipError_t launch_w4a8_tok(const int8_t *q, const float *s_x, int64_t M, int64_t ldq,
+                           const uint8_t *qweight, const uint16_t *s_w, const uint16_t *bias,
+                           int64_t d_out, int64_t d_in, int64_t k_pad, void *y, int64_t ldy,
+                           bool out_f32, int32_t *acc, hipStream_t stream);
 bool gemv_mfma_supported(int64_t M, int64_t d_out, int64_t d_in, int64_t k_pad, int64_t span,
                          int64_t n_groups, int64_t ldx, bool zp);
 hipError_t launch_gemv_mfma(const uint16_t *x, int64_t M, int64_t ldx, const uint8_t *qweight,

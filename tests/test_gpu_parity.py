@@ -987,6 +987,18 @@ def test_w4a8_c5_full_size():
         check_w4a8(w, x, b, f"C5/{lin.name}")
 
 
+def test_w4a8_c5_full_size_few_tokens():
+    """Both C5 shapes at 16 and 33 tokens (one and three 16-token tiles, the last partial), which
+    the library gives to the int8 matrix-core kernel: int32 accumulators bit for bit."""
+    cfg = workloads.C5
+    for li, lin in enumerate(cfg.linears):
+        w = workloads.linear_weight(cfg, li)
+        b = workloads.linear_bias(cfg, li)
+        for M in (16, 33):
+            x = workloads.linear_x(cfg, li, M)
+            check_w4a8(w, x, b, f"C5/{lin.name} M={M}")
+
+
 def test_w4a8_ragged_and_token_counts():
     for M, d_out, d_in in ((1, 1, 1), (3, 70, 90), (5, 257, 1000), (64, 130, 3600),
                            (16, 64, 18944)):
