@@ -331,13 +331,29 @@ def bench_c5(torch, w4, workloads, iters):
         gb = linear_bytes(1, lin.d_out, lin.d_in, 0, False, bias=True, x_bytes=1) + 4
         aq_bytes = 2 * lin.d_in + lin.d_in + 4
         fb = linear_bytes(1, lin.d_out, lin.d_in, 0, False, bias=True, x_bytes=2)
+        # a few tokens (the int8 matrix-core kernel: the weights read once per 16 tokens)
+        few = {}
+        for M in (4, 16):
+            xm = torch.from_numpy(workloads.linear_x(cfg, li, M).view(np.int16)).view(
+                torch.bfloat16).to(dev)
+            qm, sm, _ = w4.act_quant_int8(xm, lin.d_in, with_sum=False)
+            ym = torch.empty((M, lin.d_out), dtype=torch.bfloat16, device=dev)
+
+            def gemvs_m(qm=qm, sm=sm, ym=ym):
+                for c in copies:
+                    w4.w4a8_gemv(qm, sm, c[0], c[1], b, lin.d_in, out=ym)
+
+            ms = graph_ms(torch, gemvs_m, n_copies, max(1, iters // n_copies))
+            mb = linear_bytes(M, lin.d_out, lin.d_in, 0, False, bias=True, x_bytes=1) + 4 * M
+            few[f"M={M}"] = dict(gemv_us=round(ms * 1e3, 2), gemv_gbs=round(mb / ms / 1e6, 1),
+                                 gemv_hbm_frac=round(mb / ms / 1e6 / HBM_PEAK_GBS, 4))
         out[f"{lin.d_out}x{lin.d_in}"] = dict(
             gemv_us=round(gemv_ms * 1e3, 2), gemv_gbs=round(gb / gemv_ms / 1e6, 1),
             gemv_hbm_frac=round(gb / gemv_ms / 1e6 / HBM_PEAK_GBS, 4),
             act_quant_us=round(aq_ms * 1e3, 2),
             path_gbs=round((gb + aq_bytes) / (gemv_ms + aq_ms) / 1e6, 1),
             fused_us=round(fused_ms * 1e3, 2), fused_gbs=round(fb / fused_ms / 1e6, 1),
-            fused_hbm_frac=round(fb / fused_ms / 1e6 / HBM_PEAK_GBS, 4))
+            fused_hbm_frac=round(fb / fused_ms / 1e6 / HBM_PEAK_GBS, 4), few_tokens=few)
         del copies, base
     return out
 
