@@ -285,7 +285,30 @@ def bench_c4(torch, w4, workloads, iters):
             gemm_ms=round(g_ms, 4), tops=round(flop / g_ms / 1e9, 1),
             int8_mfma_frac=round(flop / g_ms / 1e9 / INT8_MFMA_PEAK_TOPS, 4),
             act_quant_ms=round(aq_ms, 4), path_ms=round(g_ms + aq_ms, 4))
-        del qw8, sw8, q, s_x, x, y
+        # context, not a ceiling of this library's kernels: the vendor GEMMs (hipBLASLt through
+        # torch) on dense operands of the same shape, bf16 x bf16 and int8 x int8 (random values,
+        # weights column-major), the forms a dequantize-then-GEMM path would call
+        wd = torch.randn((lin.d_out, lin.d_in), device=dev, dtype=torch.bfloat16)
+        xd = torch.randn((M, lin.d_in), device=dev, dtype=torch.bfloat16)
+        qd = torch.randint(-127, 128, (M, lin.d_in), device=dev, dtype=torch.int8)
+        wq = torch.randint(-8, 8, (lin.d_out, lin.d_in), device=dev, dtype=torch.int8)
+        lib = {}
+        for key, fn in (("bf16_tflops", lambda: torch.matmul(xd, wd.t())),
+                        ("int8_tops", lambda: torch._int_mm(qd, wq.t()))):
+            try:
+                for _ in range(2):
+                    fn()
+                torch.cuda.synchronize()
+                for _ in range(iters):
+                    timer.start(key)
+                    fn()
+                    timer.stop(key)
+                torch.cuda.synchronize()
+                lib[key] = round(flop / timer.mean_ms(key) / 1e9, 1)
+            except RuntimeError:
+                lib[key] = None
+        out[lin.name]["vendor_gemm_same_shape"] = lib
+        del qw8, sw8, q, s_x, x, y, wd, xd, qd, wq
     out["total"] = dict(gflop=round(total_flop / 1e9, 2), ms=round(total_ms, 4),
                         tflops=round(total_flop / total_ms / 1e9, 1),
                         mfma_frac=round(total_flop / total_ms / 1e9 / BF16_MFMA_PEAK_TFLOPS, 4),
