@@ -1008,6 +1008,38 @@ def test_w4a8_ragged_and_token_counts():
         check_w4a8(w, x, b if M % 2 else None, f"M={M} {d_out}x{d_in}")
 
 
+def test_w4a8_gemv_few_tokens_junk_pads():
+    """w4a8_gemv at 2-64 tokens (the int8 matrix-core kernel's 16-token tiles, full and partial)
+    on ragged shapes, with random bytes in q past d_in (act_quant_int8 leaves them unset), a q
+    row stride past the padded width and a strided y: the int32 accumulators equal the oracle's
+    O6 bit for bit, y is within the bar and bf16 y is the RNE image of fp32 y."""
+    for M, d_out, d_in, extra in ((2, 1, 1, 0), (3, 70, 90, 16), (7, 257, 1000, 32),
+                                  (16, 130, 3600, 0), (17, 64, 129, 48), (40, 300, 4100, 16),
+                                  (64, 33, 777, 0)):
+        what = f"M={M} {d_out}x{d_in}"
+        _announce("w4a8_gemv few tokens, junk pads", what)
+        w = workloads.weight(37, M + d_in, d_out, d_in)
+        ph, pd = check_pack_bit_exact(w, 0, SYM, what)
+        x = workloads.activations(37, M, M, d_in, 0.01, 20.0)
+        bias_bits = workloads.bias(37, 3, d_out) if M % 2 else None
+        q_o, s_o, _ = oracle.act_quant(x, d_in)
+        acc_o, y_ref, nov = oracle.w4a8(q_o, s_o, ph[0], ph[1][:, 0], bias_bits, d_in)
+        assert nov == 0
+        ldq = (d_in + 15) // 16 * 16 + extra
+        q = _q_with_junk_pads(q_o, d_in, ldq, 7 * M + d_in)
+        s = torch.from_numpy(np.ascontiguousarray(s_o, dtype=np.float32)).cuda()
+        b = dev_bf16(bias_bits) if bias_bits is not None else None
+        out = torch.full((M, d_out + 5), float("nan"), dtype=torch.float32, device="cuda")
+        y32, acc = w4.w4a8_gemv(q, s, pd[0], pd[1], b, d_in, F32, want_acc=True, out=out)
+        y16 = w4.w4a8_gemv(q, s, pd[0], pd[1], b, d_in, BF16)
+        torch.cuda.synchronize()
+        assert np.array_equal(host(acc), acc_o), f"{what}: int32 accumulators differ"
+        y32h = host(y32)[:, :d_out]
+        assert_close(y32h, y_ref, what)
+        assert np.isnan(host(out)[:, d_out:]).all(), f"{what}: write past d_out"
+        assert_bf16_is_rne_of_f32(y16, y32h, what)
+
+
 def _near_tie_activations():
     """Tokens whose values sit on and next to the rounding ties s (k + 1/2) of their own scale
     s = max|x| / 127, for every k in [-127, 126]; one token's maximum is so small that 1/s is
