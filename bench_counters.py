@@ -12,8 +12,8 @@ Each counter pass is a run of its own (rocprofv3 does not split counters over pa
 
 Workloads: c2 (the decode step's gate/up and down GEMVs at M = 1, and the gate/up GEMV with the
 SiLU * up epilogue), c3 (one decoder layer's four linears at M = 1, 8, 16, through w4_gemv_ws as
-the bench calls them), c4 (the prefill GEMMs, W4A16 and W4A8, M = 2048), c5 (the W4A8 GEMVs,
-act_quant_int8, the fused W4A8 linear).
+the bench calls them), c4 (the prefill GEMMs, W4A16 and W4A8, M = 2048), c5 (act_quant_int8 and
+the W4A8 GEMV at one token, the fused W4A8 linear, act_quant_int8 and the W4A8 GEMV at 16 tokens).
 
 `run` first copies a 256 MiB device buffer (known bytes: the calibration of FETCH_SIZE and
 WRITE_SIZE, whose units this part counts differently), then launches each labelled call of the
@@ -84,6 +84,10 @@ def _labels(workload):
             out.append((f"act_quant {lin.name}", 0, lin.d_in, 1, 3 * lin.d_in, 0))
             out.append((f"w4a8_gemv {lin.name}", lin.d_out, lin.d_in, 1, b, 0))
             out.append((f"w4a8_linear {lin.name}", lin.d_out, lin.d_in, 1, b + lin.d_in, 0))
+            b16 = (lin.d_out * k32 // 2 + 2 * lin.d_out + 16 * (lin.d_in + 4) + 2 * lin.d_out
+                   + 16 * 2 * lin.d_out)
+            out.append((f"act_quant M=16 {lin.name}", 0, lin.d_in, 16, 16 * 3 * lin.d_in, 0))
+            out.append((f"w4a8_gemv M=16 {lin.name}", lin.d_out, lin.d_in, 16, b16, 0))
     else:
         raise SystemExit(f"unknown workload {workload}")
     return out
@@ -174,12 +178,19 @@ def run(workload):
             pk = copies_of(w4.w4_pack(torch.from_numpy(workloads.linear_weight(cfg, li)).to(dev),
                                       lin.group_size, lin.mode))
             x = bf16(workloads.linear_x(cfg, li, 1))
+            x16 = bf16(workloads.linear_x(cfg, li, 16))  # 16 tokens: the int8 matrix-core kernel
             bias = bf16(workloads.linear_bias(cfg, li))
+            ldq = (lin.d_in + 15) // 16 * 16
+            q = torch.empty((1, ldq), dtype=torch.int8, device=dev)
+            s = torch.empty((1,), dtype=torch.float32, device=dev)
+            q16 = torch.empty((16, ldq), dtype=torch.int8, device=dev)
+            s16 = torch.empty((16,), dtype=torch.float32, device=dev)
             separator()
-            q, s, _ = w4.act_quant_int8(x, with_sum=False)  # (one run with the repeats below)
             repeat(lambda c: w4.act_quant_int8(x, with_sum=False, out=(q, s)), [None])
             repeat(lambda c: w4.w4a8_gemv(q, s, c[0], c[1], bias, lin.d_in), pk)
             repeat(lambda c: w4.w4a8_linear(x, c[0], c[1], bias, lin.d_in), pk)
+            repeat(lambda c: w4.act_quant_int8(x16, with_sum=False, out=(q16, s16)), [None])
+            repeat(lambda c: w4.w4a8_gemv(q16, s16, c[0], c[1], bias, lin.d_in), pk)
     else:
         raise SystemExit(f"unknown workload {workload}")
     torch.cuda.synchronize()
