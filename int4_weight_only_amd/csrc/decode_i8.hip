@@ -269,9 +269,12 @@ __global__ void __launch_bounds__(kI8Threads) gemv_i8_kernel(
                 const uint32_t a = u[k] & 0x7FFF7FFFu;
                 am = max(am, max(a & 0xFFFFu, a >> 16));
             }
-#pragma unroll
-            for (int o = 1; o < 16; o <<= 1)
-                am = max(am, static_cast<uint32_t>(__shfl_xor(static_cast<int>(am), o, kWave)));
+            // over the group's 16 lanes, one DPP row: quad swaps, then the half-row and row
+            // mirrors (cross-lane moves inside the VALU; LDS-routed shuffles held the prologue up)
+            am = max(am, static_cast<uint32_t>(dpp_i<0xB1, 0xF, false>(static_cast<int>(am))));
+            am = max(am, static_cast<uint32_t>(dpp_i<0x4E, 0xF, false>(static_cast<int>(am))));
+            am = max(am, static_cast<uint32_t>(dpp_i<0x141, 0xF, false>(static_cast<int>(am))));
+            am = max(am, static_cast<uint32_t>(dpp_i<0x140, 0xF, false>(static_cast<int>(am))));
             const float amax = __uint_as_float(am << 16);
             const bool finite = am < 0x7F80u;
             const int S = finite && amax > 0.0f ? 29 - ilogbf(amax) : 0;  // max|x| 2^S < 2^30
@@ -297,9 +300,12 @@ __global__ void __launch_bounds__(kI8Threads) gemv_i8_kernel(
                     static_cast<int>(dlo[pl]), ones,
                     __builtin_amdgcn_sdot4(static_cast<int>(dhi[pl]), ones, 0, false), false);
 #pragma unroll
-            for (int o = 1; o < 16; o <<= 1)
-#pragma unroll
-                for (int pl = 0; pl < 4; ++pl) ds[pl] += __shfl_xor(ds[pl], o, kWave);
+            for (int pl = 0; pl < 4; ++pl) {  // (the same DPP row reduction)
+                ds[pl] += dpp_i<0xB1, 0xF, false>(ds[pl]);
+                ds[pl] += dpp_i<0x4E, 0xF, false>(ds[pl]);
+                ds[pl] += dpp_i<0x141, 0xF, false>(ds[pl]);
+                ds[pl] += dpp_i<0x140, 0xF, false>(ds[pl]);
+            }
             // lane (n, q) of B holds columns 32q .. 32q+31 of the group, bytes 4i .. 4i+3 of an
             // operand being columns 32q + 8i + 2b (+1): here q = j / 4, i = j % 4
             const int kq = j >> 2, ki = j & 3;
